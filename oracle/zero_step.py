@@ -1,0 +1,369 @@
+"""CPU oracle: one data-parallel rank's share of the ZeRO mixed-precision
+AdamW step, written out plainly in NumPy.
+
+TEST INFRASTRUCTURE ONLY. This module is the slow, obviously-correct
+definition the HIP library is checked against. Only the test suite, the
+smoke check and the bench's CPU-baseline leg may import it. It shares no
+code with the library and imports nothing from it.
+
+Pages the definitions follow (cited by title and section below):
+  [algomooc]  algomooc.com interview answer on the DeepSpeed framework
+  [aidhplus]  aidhplus.com, "DeepSpeed" overview
+  [csdn]      devpress.csdn.net DeepSpeed distributed-training tutorial
+  [aiqz]      aiqz.cc, "DeepSpeed ZeRO引擎深入"
+  [ch01]      jwzheng96.github.io llm-train-tutorials, DeepSpeed chapter 1
+
+Arrays: 16-bit values (fp16, bf16) travel as their raw bit patterns
+(np.uint16); fp32 arrays are np.float32. NumPy's float32 array arithmetic is
+IEEE round-to-nearest-even, one rounding per operation and never fused, and
+its float32 sqrt and divide are correctly rounded; the step below relies on
+exactly that.
+
+Pin status: every function here is pinned by a CPU test against closed
+forms, exact rational arithmetic, brute force or the pages' printed numbers.
+Two constants have no page behind them and are readings, not pins: the 1e-6
+added to the norm in the clip coefficient, and the hysteresis rule for H > 1.
+"""
+
+from dataclasses import dataclass, replace
+from fractions import Fraction
+import math
+
+import numpy as np
+
+FP16, BF16, FP32 = "fp16", "bf16", "fp32"
+
+
+# ---------------------------------------------------------------------------
+# Byte accounting of mixed-precision Adam state.
+# [csdn] §2.1 ZeRO: per parameter, 2 B fp16 param + 2 B fp16 grad + 12 B of
+# fp32 master/momentum/variance, i.e. 16 B; [aiqz] 显存四巨头 gives the same
+# split. Per-stage per-GPU formulas: [ch01] §1.2 and [aiqz] ZeRO三阶段.
+# ---------------------------------------------------------------------------
+
+def state_bytes_ddp(psi):
+    """Every data-parallel replica holds all 16 bytes per parameter."""
+    return 2 * psi + 2 * psi + 12 * psi
+
+
+def state_bytes_stage1(psi, n):
+    """Optimizer state (12 B/param) split over n ranks; params and grads whole."""
+    return Fraction(4 * psi) + Fraction(12 * psi, n)
+
+
+def state_bytes_stage2(psi, n):
+    """Optimizer state and grads (14 B/param) split; params whole."""
+    return Fraction(2 * psi) + Fraction(14 * psi, n)
+
+
+def state_bytes_stage3(psi, n):
+    """All 16 B/param split over n ranks."""
+    return Fraction(16 * psi, n)
+
+
+# ---------------------------------------------------------------------------
+# Flat buffer layout and the Stage-1 contiguous shard.
+# [csdn] §3.2: contiguous_gradients keeps the grads in one contiguous buffer;
+# [aiqz] 通信优化: many small grad tensors are packed into buckets.
+# [csdn] §2.1 and §2.4: under Stage 1 each rank holds and updates only its own
+# part of the optimizer state. The part is a contiguous 1/N slice of the flat
+# buffer (reading: equal slices, the buffer padded with zeros to a multiple of
+# N * align).
+# ---------------------------------------------------------------------------
+
+def align_up(x, a):
+    return ((x + a - 1) // a) * a
+
+
+def flat_layout(numels, align):
+    """Each tensor starts at the next multiple of `align` elements after the
+    previous one ends. Returns (offsets, padded_total)."""
+    offsets = []
+    pos = 0
+    for n in numels:
+        offsets.append(pos)
+        pos = align_up(pos + n, align)
+    return offsets, pos
+
+
+def shard_range(flat_total, world, rank, align):
+    """[lo, hi) of rank `rank` out of `world` equal contiguous slices of the
+    flat buffer padded to a multiple of world * align."""
+    padded = align_up(flat_total, world * align)
+    per = padded // world
+    return rank * per, (rank + 1) * per
+
+
+def shard_entries(numels, align, lo, hi):
+    """Pieces of tensors that fall inside flat range [lo, hi).
+
+    Returns a list of (tensor_index, start_in_tensor, length, dst_offset) where
+    dst_offset is relative to lo."""
+    offsets, _ = flat_layout(numels, align)
+    out = []
+    for t, (o, n) in enumerate(zip(offsets, numels)):
+        a = max(o, lo)
+        b = min(o + n, hi)
+        if a < b:
+            out.append((t, a - o, b - a, a - lo))
+    return out
+
+
+def round_robin_owners(names, world):
+    """The partition of the [aiqz] Python 演示: whole tensors dealt to ranks in
+    turn, rank r owning names[r], names[r + world], ..."""
+    return [list(names[r::world]) for r in range(world)]
+
+
+# ---------------------------------------------------------------------------
+# 16-bit <-> fp32 element conversions.
+# ---------------------------------------------------------------------------
+
+def widen(x, dtype):
+    """Exact conversion of fp16/bf16 bit patterns (or fp32 values) to fp32."""
+    if dtype == FP16:
+        return x.view(np.float16).astype(np.float32)
+    if dtype == BF16:
+        return (x.astype(np.uint32) << np.uint32(16)).view(np.float32)
+    if dtype == FP32:
+        return np.asarray(x, dtype=np.float32)
+    raise ValueError(dtype)
+
+
+def narrow(p, dtype):
+    """fp32 -> 16-bit bit patterns, round to nearest, ties to even.
+
+    fp16: NumPy's IEEE conversion (overflow to inf, subnormals kept).
+    bf16: keep the upper 16 bits of the fp32 pattern after adding half of the
+    dropped range plus the tie-to-even bit; NaN stays a quiet NaN."""
+    p = np.asarray(p, dtype=np.float32)
+    if dtype == FP16:
+        return p.astype(np.float16).view(np.uint16)
+    if dtype == BF16:
+        u = p.view(np.uint32).astype(np.uint64)
+        lsb = (u >> np.uint64(16)) & np.uint64(1)
+        r = (u + np.uint64(0x7FFF) + lsb) >> np.uint64(16)
+        nan = (u & np.uint64(0x7FFFFFFF)) > np.uint64(0x7F800000)
+        r = np.where(nan, (u >> np.uint64(16)) | np.uint64(0x40), r)
+        return r.astype(np.uint16)
+    raise ValueError(dtype)
+
+
+# ---------------------------------------------------------------------------
+# Row a1: flatten / accumulate gradients into the flat bucket.
+# [csdn] §2.3: micro-batch grads are summed in memory and one update is made
+# at the end; [csdn] §3.2 contiguous_gradients; [aiqz] 通信优化 buckets.
+# ---------------------------------------------------------------------------
+
+COPY, OVERWRITE, ACCUMULATE = 0, 1, 2
+
+
+def flatten_copy(srcs, entries, bucket):
+    """COPY: bucket[d + j] = src_t[s + j] (16-bit to 16-bit)."""
+    for t, s, n, d in entries:
+        bucket[d:d + n] = srcs[t][s:s + n]
+    return bucket
+
+
+def flatten_accumulate(srcs, src_dtype, entries, acc, overwrite):
+    """OVERWRITE: acc[d + j] = fp32(src); ACCUMULATE: acc[d + j] += fp32(src)
+    with one fp32 round-to-nearest add per element."""
+    for t, s, n, d in entries:
+        x = widen(srcs[t][s:s + n], src_dtype)
+        if overwrite:
+            acc[d:d + n] = x
+        else:
+            acc[d:d + n] = acc[d:d + n] + x
+    return acc
+
+
+# ---------------------------------------------------------------------------
+# Row a2: overflow check, L2 norm, clip coefficient.
+# [csdn] §2.2: grads overflowing to inf under the loss scale are detected and
+# the scale is lowered; §4.4 a NaN loss points at the fp16 setup. Clipping by
+# the global norm is not on the pages: it is the conventional
+# coef = max_norm / (norm + 1e-6), applied only when norm > max_norm (reading;
+# the 1e-6 is unpinned). Accumulated grads are averaged over the K
+# micro-batches ([csdn] §2.3: the accumulated grad stands for the big batch).
+# ---------------------------------------------------------------------------
+
+_EXP_MASK = {FP16: 0x7C00, BF16: 0x7F80, FP32: 0x7F800000}
+
+
+def nonfinite_mask(x, dtype):
+    """Element is inf or NaN: its exponent field is all ones."""
+    if dtype == FP32:
+        bits = np.asarray(x, dtype=np.float32).view(np.uint32)
+    else:
+        bits = x
+    m = bits.dtype.type(_EXP_MASK[dtype])
+    return (bits & m) == m
+
+
+def overflow_flag(x, dtype):
+    return int(bool(np.any(nonfinite_mask(x, dtype))))
+
+
+def sum_of_squares(x, dtype, chunk=1 << 22):
+    """Sum over elements of float64(x)^2, chunk partials added in order."""
+    total = 0.0
+    for a in range(0, x.shape[0], chunk):
+        xc = widen(x[a:a + chunk], dtype).astype(np.float64)
+        total += float(np.sum(xc * xc))
+    return total
+
+
+def clip_scalars(sumsq, scale, accum_steps, max_norm):
+    """From the raw (loss-scaled, summed over K micro-batches) sum of squares:
+    the true norm, the clip coefficient and the single fp32 factor the Adam
+    pass multiplies every raw grad element by. All in float64, rounded once."""
+    sk = float(scale) * float(accum_steps)
+    norm = math.sqrt(sumsq) / sk
+    coef = 1.0
+    if max_norm > 0.0 and norm > max_norm:
+        coef = float(max_norm) / (norm + 1e-6)
+    grad_scale = np.float32(coef / sk)
+    return norm, coef, grad_scale
+
+
+def overflow_and_norm(x, dtype, scale, accum_steps, max_norm):
+    ovf = overflow_flag(x, dtype)
+    sumsq = sum_of_squares(x, dtype)
+    if ovf:
+        return dict(overflow=1, sumsq=sumsq, norm=np.float32(np.inf),
+                    coef=1.0, grad_scale=np.float32(0.0))
+    norm, coef, gs = clip_scalars(sumsq, scale, accum_steps, max_norm)
+    return dict(overflow=0, sumsq=sumsq, norm=np.float32(norm), coef=coef, grad_scale=gs)
+
+
+# ---------------------------------------------------------------------------
+# Row a3: dynamic loss-scale state machine.
+# [csdn] §2.2: multiply the loss so fp16 grads do not underflow, unscale
+# before the update, lower the scale when an overflow is detected and try to
+# raise it again once training is stable. [csdn] §3.2 fp16 block: loss_scale 0
+# selects the dynamic mode; loss_scale_window, initial_scale_power, hysteresis
+# and min_loss_scale. [aidhplus] feature list: dynamic loss scaling.
+# Readings: factor 2 both ways; grow after `window` consecutive clean steps;
+# halve when `hysteresis` overflows have come in a row (clean steps reset the
+# count); never below min_scale; an overflow always skips the step, which
+# leaves the Adam step counter and beta powers untouched.
+# ---------------------------------------------------------------------------
+
+@dataclass(frozen=True)
+class ScalerState:
+    scale: float
+    good_steps: int
+    hyst_left: int
+    window: int
+    hysteresis: int
+    min_scale: float
+    dynamic: bool
+    t: int            # Adam steps applied so far
+    beta1_pow: float  # beta1^t in float64
+    beta2_pow: float  # beta2^t in float64
+    last_skip: int
+
+
+def scaler_init(dynamic=True, initial_scale_power=16, window=1000, hysteresis=1,
+                min_scale=1.0, static_scale=1.0, t=0, beta1_pow=1.0, beta2_pow=1.0):
+    scale = float(2.0 ** initial_scale_power) if dynamic else float(static_scale)
+    return ScalerState(scale=scale, good_steps=0, hyst_left=hysteresis, window=window,
+                       hysteresis=hysteresis, min_scale=float(min_scale), dynamic=bool(dynamic),
+                       t=t, beta1_pow=beta1_pow, beta2_pow=beta2_pow, last_skip=0)
+
+
+def scaler_update(st, overflow, beta1, beta2):
+    """State after a step whose grads had the given overflow flag. beta1 and
+    beta2 are the fp32 hyperparameters; the powers advance in float64."""
+    if overflow:
+        if not st.dynamic:
+            return replace(st, last_skip=1)
+        if st.hyst_left <= 1:
+            return replace(st, scale=max(st.scale / 2.0, st.min_scale),
+                           hyst_left=st.hysteresis, good_steps=0, last_skip=1)
+        return replace(st, hyst_left=st.hyst_left - 1, good_steps=0, last_skip=1)
+    b1 = float(np.float32(beta1))
+    b2 = float(np.float32(beta2))
+    st = replace(st, t=st.t + 1, beta1_pow=st.beta1_pow * b1, beta2_pow=st.beta2_pow * b2,
+                 last_skip=0)
+    if not st.dynamic:
+        return st
+    good = st.good_steps + 1
+    if good == st.window:
+        return replace(st, scale=st.scale * 2.0, good_steps=0, hyst_left=st.hysteresis)
+    return replace(st, good_steps=good, hyst_left=st.hysteresis)
+
+
+# ---------------------------------------------------------------------------
+# Row a4: AdamW on the fp32 master shard, then the cast back to 16 bits.
+# [csdn] §2.2 and [aiqz] 混合精度: forward/backward in 16 bits, the update on
+# the fp32 master copy. [csdn] §3.2 optimizer block: AdamW, betas, eps,
+# weight_decay. [csdn] §2.4: each rank updates only its slice. [aiqz] Python
+# 演示: the two moment recurrences and p -= lr * m / (sqrt(v) + eps).
+# Readings: bias correction on (off reproduces the demo); eps added after
+# dividing sqrt(v) by sqrt(1 - beta2^t); decoupled decay p *= 1 - lr * wd
+# applied before the Adam term; hyperparameters rounded to fp32 first; the
+# per-step scalars derived in float64 and rounded once to fp32; every
+# element operation in fp32 in the order written below.
+# ---------------------------------------------------------------------------
+
+@dataclass(frozen=True)
+class AdamW:
+    lr: float = 1e-3
+    beta1: float = 0.9
+    beta2: float = 0.999
+    eps: float = 1e-8
+    weight_decay: float = 0.01
+
+
+def adamw_constants(hp, beta1_pow, beta2_pow, bias_correction=True):
+    """fp32 scalars for the step that raises t by one. beta?_pow are the
+    float64 powers before the step."""
+    lr = np.float32(hp.lr)
+    b1 = np.float32(hp.beta1)
+    b2 = np.float32(hp.beta2)
+    eps = np.float32(hp.eps)
+    wd = np.float32(hp.weight_decay)
+    c = dict(b1=b1, b2=b2, eps=eps,
+             omb1=np.float32(np.float32(1.0) - b1),
+             omb2=np.float32(np.float32(1.0) - b2))
+    if bias_correction:
+        p1 = beta1_pow * float(b1)
+        p2 = beta2_pow * float(b2)
+        c["step_size"] = np.float32(float(lr) / (1.0 - p1))
+        c["bc2_sqrt"] = np.float32(math.sqrt(1.0 - p2))
+    else:
+        c["step_size"] = lr
+        c["bc2_sqrt"] = np.float32(1.0)
+    c["decay"] = np.float32(1.0 - float(lr) * float(wd))
+    return c
+
+
+def adamw_update(x, dtype, grad_scale, master, m, v, c):
+    """New (master, m, v) for raw grads x, with grad_scale folding the loss
+    unscale, the 1/K mean and the clip coefficient into one fp32 factor."""
+    g = widen(x, dtype) * np.float32(grad_scale)
+    m = c["b1"] * m + c["omb1"] * g
+    v = c["b2"] * v + c["omb2"] * (g * g)
+    denom = np.sqrt(v) / c["bc2_sqrt"] + c["eps"]
+    p = master * c["decay"]
+    p = p - c["step_size"] * (m / denom)
+    return p, m, v
+
+
+# ---------------------------------------------------------------------------
+# One whole optimizer step on the rank's shard, in the engine's order
+# ([csdn] §3.3: backward per micro-batch, then one step that handles
+# accumulation, mixed precision and the optimizer).
+# ---------------------------------------------------------------------------
+
+def optimizer_step(x, gdtype, master, m, v, state, hp, max_norm, accum_steps, pdtype):
+    """Returns (master, m, v, p16 or None, new_state, scalars). On overflow the
+    state arrays are returned unchanged and p16 is None (not written)."""
+    sc = overflow_and_norm(x, gdtype, state.scale, accum_steps, max_norm)
+    if sc["overflow"]:
+        return master, m, v, None, scaler_update(state, 1, hp.beta1, hp.beta2), sc
+    c = adamw_constants(hp, state.beta1_pow, state.beta2_pow)
+    master, m, v = adamw_update(x, gdtype, sc["grad_scale"], master, m, v, c)
+    p16 = narrow(master, pdtype)
+    return master, m, v, p16, scaler_update(state, 0, hp.beta1, hp.beta2), sc

@@ -1,0 +1,53 @@
+"""Pin strength: plant plausible mistakes in a copy of the oracle (on the CPU)
+and check that the oracle pins reject every one of them."""
+
+import os
+import shutil
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+MUTANTS = {
+ "no_decay": ("p = master * c[\"decay\"]", "p = master * np.float32(1.0)"),
+ "sign": ("p = p - c[\"step_size\"] * (m / denom)", "p = p + c[\"step_size\"] * (m / denom)"),
+ "swap_b1": ("m = c[\"b1\"] * m + c[\"omb1\"] * g", "m = c[\"omb1\"] * m + c[\"b1\"] * g"),
+ "eps_in": ("denom = np.sqrt(v) / c[\"bc2_sqrt\"] + c[\"eps\"]", "denom = np.sqrt(v / c[\"bc2_sqrt\"] + c[\"eps\"])"),
+ "no_bc2": ("denom = np.sqrt(v) / c[\"bc2_sqrt\"] + c[\"eps\"]", "denom = np.sqrt(v) + c[\"eps\"]"),
+ "no_bc1": ("c[\"step_size\"] = np.float32(float(lr) / (1.0 - p1))", "c[\"step_size\"] = lr"),
+ "no_sq": ("v = c[\"b2\"] * v + c[\"omb2\"] * (g * g)", "v = c[\"b2\"] * v + c[\"omb2\"] * g"),
+ "bf16_trunc": ("r = (u + np.uint64(0x7FFF) + lsb) >> np.uint64(16)", "r = u >> np.uint64(16)"),
+ "grow_off1": ("if good == st.window:", "if good == st.window - 1:"),
+ "hyst_noreset": ("return replace(st, good_steps=good, hyst_left=st.hysteresis)", "return replace(st, good_steps=good)"),
+ "clip_always": ("if max_norm > 0.0 and norm > max_norm:", "if max_norm > 0.0:"),
+ "sumsq_abs": ("total += float(np.sum(xc * xc))", "total += float(np.sum(np.abs(xc)))"),
+ "shard_off1": ("out.append((t, a - o, b - a, a - lo))", "out.append((t, a - o, b - a - (1 if b - a > 1 else 0), a - lo))"),
+ "layout_noalign": ("pos = align_up(pos + n, align)", "pos = pos + n"),
+ "acc_overwrite": ("acc[d:d + n] = acc[d:d + n] + x", "acc[d:d + n] = x"),
+ "no_K": ("sk = float(scale) * float(accum_steps)", "sk = float(scale)"),
+ "scale_not_halved": ("return replace(st, scale=max(st.scale / 2.0, st.min_scale),", "return replace(st, scale=max(st.scale, st.min_scale),"),
+ "t_on_skip": ("return replace(st, hyst_left=st.hyst_left - 1, good_steps=0, last_skip=1)", "return replace(st, hyst_left=st.hyst_left - 1, good_steps=0, last_skip=1, t=st.t+1)"),
+ "ovf_mask": ("return (bits & m) == m", "return (bits & m) == m - 1"),
+ "widen_bf16": ("return (x.astype(np.uint32) << np.uint32(16)).view(np.float32)", "return (x.astype(np.uint32) << np.uint32(15)).view(np.float32)"),
+ "decay_sign": ("c[\"decay\"] = np.float32(1.0 - float(lr) * float(wd))", "c[\"decay\"] = np.float32(1.0 + float(lr) * float(wd))"),
+ "beta_pow_skip": ("st = replace(st, t=st.t + 1, beta1_pow=st.beta1_pow * b1, beta2_pow=st.beta2_pow * b2,", "st = replace(st, t=st.t + 1, beta1_pow=st.beta1_pow * b2, beta2_pow=st.beta2_pow * b1,"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_pins_reject_mutant(name, tmp_path):
+    old, new = MUTANTS[name]
+    src = open(os.path.join(ROOT, "oracle", "zero_step.py")).read()
+    assert src.count(old) >= 1, name
+    shutil.copytree(os.path.join(ROOT, "oracle"), tmp_path / "oracle")
+    shutil.copytree(os.path.join(ROOT, "workloads"), tmp_path / "workloads")
+    shutil.copytree(os.path.join(ROOT, "tests", "golden"), tmp_path / "tests" / "golden")
+    shutil.copy(os.path.join(ROOT, "tests", "conftest.py"), tmp_path / "tests" / "conftest.py")
+    shutil.copy(os.path.join(ROOT, "tests", "test_oracle_pins.py"), tmp_path / "tests" / "test_oracle_pins.py")
+    (tmp_path / "oracle" / "zero_step.py").write_text(src.replace(old, new, 1))
+    r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
+                        "tests/test_oracle_pins.py"], cwd=tmp_path, capture_output=True, text=True,
+                       timeout=300)
+    assert r.returncode != 0, "mutant %s passed every pin:\n%s" % (name, r.stdout[-2000:])

@@ -1,0 +1,621 @@
+"""Pins for the CPU oracle: each test checks the oracle against something other
+than itself (the pages' printed numbers, closed forms, exact rational or
+high-precision decimal arithmetic, brute-force enumeration, format
+definitions), chosen so that a dropped term, a wrong sign or index or a
+swapped operand in the oracle fails at least one of them."""
+
+import decimal
+import json
+import math
+import os
+import struct
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle as O
+from workloads import llama_7b_tensors, llama_65b_tensors, llama_7b_split_1024, tiny_shard_sizes
+
+GOLDEN = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "pages_numbers.json")))
+
+PSI_7B = 6_738_411_520
+PSI_65B = 65_285_652_480
+
+
+# ---------------------------------------------------------------- accounting
+
+def test_accounting_pages_numbers():
+    g = GOLDEN["bytes_per_param_mixed_adam"]
+    assert O.state_bytes_ddp(1) == g["total"] == g["fp16_param"] + g["fp16_grad"] + 12
+    s = GOLDEN["seven_b_static_bytes"]
+    assert O.state_bytes_ddp(s["psi"]) == s["bytes"]
+
+
+def test_accounting_brute_force_bytes():
+    """Materialise each stage's per-rank buffers as real arrays and count."""
+    for psi in (96, 840):
+        for n in (1, 2, 3, 4, 8):
+            if psi % n:
+                continue
+            sh = psi // n
+            full16 = np.zeros(psi, np.float16).nbytes
+            shard16 = np.zeros(sh, np.float16).nbytes
+            shard32x3 = 3 * np.zeros(sh, np.float32).nbytes
+            full32x3 = 3 * np.zeros(psi, np.float32).nbytes
+            assert O.state_bytes_ddp(psi) == 2 * full16 + full32x3
+            assert O.state_bytes_stage1(psi, n) == 2 * full16 + shard32x3
+            assert O.state_bytes_stage2(psi, n) == full16 + shard16 + shard32x3
+            assert O.state_bytes_stage3(psi, n) == 2 * shard16 + shard32x3
+
+
+def test_accounting_limits_and_n1():
+    r = GOLDEN["memory_reduction_approx"]
+    big = 10 ** 12
+    psi = 7 * 10 ** 9
+    assert abs(float(O.state_bytes_ddp(psi) / O.state_bytes_stage1(psi, big)) - r["stage1"]) < 1e-6
+    assert abs(float(O.state_bytes_ddp(psi) / O.state_bytes_stage2(psi, big)) - r["stage2"]) < 1e-6
+    for f in (O.state_bytes_stage1, O.state_bytes_stage2, O.state_bytes_stage3):
+        assert f(psi, 1) == 16 * psi
+    # at N = 8 the reduction is well short of the limits
+    assert round(float(Fraction(16) / Fraction(O.state_bytes_stage1(1, 8))), 2) == 2.91
+    assert round(float(Fraction(16) / Fraction(O.state_bytes_stage2(1, 8))), 2) == 4.27
+
+
+def test_accounting_workload_footprints():
+    assert sum(n for _, n in llama_7b_tensors()) == PSI_7B
+    assert sum(n for _, n in llama_65b_tensors()) == PSI_65B
+    assert O.state_bytes_ddp(PSI_7B) == 107_814_584_320          # whole 7B, ~108 GB
+    assert O.state_bytes_stage3(PSI_65B, 8) == 130_571_304_960    # 65B 1/8 shard, ~130 GB
+
+
+def test_accumulation_example():
+    g = GOLDEN["grad_accumulation_example"]
+    assert g["global_batch"] // (g["gpus"] * g["micro_batch"]) == g["accumulation_steps"]
+
+
+# ---------------------------------------------------------------- layout
+
+def _brute_flat(numels, align):
+    """Flat buffer of (tensor id, index) labels, -1 for padding, built
+    element by element."""
+    lab_t, lab_i = [], []
+    for t, n in enumerate(numels):
+        while len(lab_t) % align:
+            lab_t.append(-1)
+            lab_i.append(-1)
+        lab_t.extend([t] * n)
+        lab_i.extend(range(n))
+    while len(lab_t) % align:
+        lab_t.append(-1)
+        lab_i.append(-1)
+    return np.array(lab_t), np.array(lab_i)
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_shard_entries_brute_force(seed):
+    rng = np.random.default_rng(seed)
+    T = int(rng.integers(1, 9))
+    numels = [int(x) for x in rng.integers(1, 300, T)]
+    align = int(rng.choice([1, 4, 8, 64]))
+    world = int(rng.integers(1, 9))
+    lab_t, lab_i = _brute_flat(numels, align)
+    _, total = O.flat_layout(numels, align)
+    assert total == len(lab_t)
+    padded = total
+    while padded % (world * align):
+        padded += 1
+    lab_t = np.concatenate([lab_t, -np.ones(padded - total, int)])
+    lab_i = np.concatenate([lab_i, -np.ones(padded - total, int)])
+    per = padded // world
+    seen = np.zeros(padded, bool)
+    for r in range(world):
+        lo, hi = O.shard_range(total, world, r, align)
+        assert (lo, hi) == (r * per, (r + 1) * per)
+        for t, s, n, d in O.shard_entries(numels, align, lo, hi):
+            seg_t = lab_t[lo + d: lo + d + n]
+            seg_i = lab_i[lo + d: lo + d + n]
+            assert (seg_t == t).all()
+            assert (seg_i == np.arange(s, s + n)).all()
+            assert not seen[lo + d: lo + d + n].any()
+            seen[lo + d: lo + d + n] = True
+    assert (seen == (lab_t >= 0)).all()
+
+
+def test_shard_entries_llama():
+    t7 = llama_7b_tensors()
+    n7 = [n for _, n in t7]
+    lo, hi = O.shard_range(PSI_7B, 8, 0, 64)
+    assert hi - lo == 842_301_440
+    e0 = O.shard_entries(n7, 64, lo, hi)
+    assert len(e0) == 33
+    assert t7[e0[-1][0]][0] == "gate3" and e0[-1][1] == 0 and e0[-1][2] == 36_970_496
+    lo, hi = O.shard_range(PSI_7B, 8, 7, 64)
+    e7 = O.shard_entries(n7, 64, lo, hi)
+    assert len(e7) == 33
+    assert t7[e7[0][0]][0] == "gate28" and e7[0][1] == 31_195_136 and e7[0][2] == 13_893_632
+    t65 = llama_65b_tensors()
+    lo, hi = O.shard_range(PSI_65B, 8, 0, 64)
+    e = O.shard_entries([n for _, n in t65], 64, lo, hi)
+    assert hi - lo == 8_160_706_560 and len(e) == 88
+    assert t65[e[-1][0]][0] == "up9" and e[-1][1] == 0 and e[-1][2] == 164_118_528
+    s1024 = llama_7b_split_1024()
+    assert len(s1024) == 1024 and sum(n for _, n in s1024) == PSI_7B
+    tiny = tiny_shard_sizes()
+    assert sum(n for _, n in tiny) == 733_953
+
+
+def test_round_robin_demo_partition():
+    d = GOLDEN["zero1_demo"]
+    names = ["w%d" % i for i in range(len(d["sizes"]))]
+    assert O.round_robin_owners(names, d["world_size"]) == [["w0"], ["w1"], ["w2"], []]
+
+
+# ---------------------------------------------------------------- formats
+
+def _fp16_by_definition(h):
+    s = -1.0 if h >> 15 else 1.0
+    e = (h >> 10) & 0x1F
+    f = h & 0x3FF
+    if e == 0x1F:
+        return s * math.inf if f == 0 else math.nan
+    if e == 0:
+        return s * math.ldexp(f, -24)
+    return s * math.ldexp(1024 + f, e - 25)
+
+
+def test_widen_fp16_all_patterns():
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    with np.errstate(invalid="ignore"):
+        w = O.widen(bits, O.FP16).astype(np.float64)
+    ref = np.array([_fp16_by_definition(int(h)) for h in range(65536)])
+    same = (w == ref) | (np.isnan(w) & np.isnan(ref))
+    assert same.all()
+
+
+def test_widen_bf16_all_patterns():
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    w = O.widen(bits, O.BF16)
+    ref = [struct.unpack(">f", struct.pack(">HH", h, 0))[0] for h in range(65536)]
+    for a, b in zip(w.tolist(), ref):
+        assert (a == b and math.copysign(1, a) == math.copysign(1, b)) or (math.isnan(a) and math.isnan(b))
+
+
+def _bf16_value(pat):
+    return Fraction(struct.unpack("<f", struct.pack("<I", pat << 16))[0])
+
+
+def _bf16_rne_exact(u32):
+    """Nearest-even bf16 pattern of the fp32 pattern u32, chosen by exact
+    rational distances to the two neighbouring bf16 values; None for NaN."""
+    x = struct.unpack("<f", struct.pack("<I", u32))[0]
+    if math.isnan(x):
+        return None
+    lo_pat = u32 >> 16           # same sign, magnitude truncated
+    if math.isinf(x):
+        return lo_pat
+    up_pat = lo_pat + 1          # next magnitude away from zero
+    ax = abs(Fraction(x))
+    if (up_pat & 0x7F80) == 0x7F80:
+        # above the largest finite bf16 (2^128 - 2^120): overflow to inf at
+        # half an ulp past it, the tie going to the even (infinite) side
+        return up_pat if ax >= Fraction(2) ** 128 - Fraction(2) ** 119 else lo_pat
+    dlo = ax - abs(_bf16_value(lo_pat))
+    dup = abs(_bf16_value(up_pat)) - ax
+    if dlo != dup:
+        return lo_pat if dlo < dup else up_pat
+    return lo_pat if (lo_pat & 1) == 0 else up_pat
+
+
+def test_narrow_bf16_exact_rounding():
+    rng = np.random.default_rng(5)
+    his = rng.integers(0, 65536, 3000)
+    los = np.array([0, 1, 0x7FFF, 0x8000, 0x8001, 0xFFFF])
+    pats = [(int(h) << 16) | int(l) for h in his for l in los]
+    pats += [int(x) for x in rng.integers(0, 2 ** 32, 4000, dtype=np.uint64)]
+    pats += [0x7F7F7FFF, 0x7F7F8000, 0x7F7F8001, 0xFF7F8000, 0x00008000, 0x00018000]
+    arr = np.array(pats, dtype=np.uint32)
+    got = O.narrow(arr.view(np.float32), O.BF16)
+    for p, g in zip(pats, got):
+        want = _bf16_rne_exact(p)
+        if want is None:
+            assert (int(g) & 0x7F80) == 0x7F80 and (int(g) & 0x7F) != 0
+        else:
+            assert int(g) == want, hex(p)
+
+
+def _fp16_rne_exact(x32):
+    """Nearest-even fp16 pattern of an fp32 value from the binary16 grid: the
+    quantum is 2^-24 below 2^-14 and 2^(e-10) in binade [2^e, 2^(e+1));
+    magnitudes from 65504 + 16 up overflow to inf."""
+    x = float(x32)
+    sign = 0x8000 if math.copysign(1.0, x) < 0 else 0
+    a = abs(Fraction(x))
+    if a >= Fraction(65520):
+        return sign | 0x7C00
+    if a < Fraction(1, 2 ** 14):
+        q = Fraction(1, 2 ** 24)
+    else:
+        e = 0
+        while Fraction(2) ** e > a:
+            e -= 1
+        while Fraction(2) ** (e + 1) <= a:
+            e += 1
+        q = Fraction(2) ** (e - 10)
+    k = a / q
+    fl = k.numerator // k.denominator
+    rem = k - fl
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and fl % 2 == 1):
+        fl += 1
+    return sign | int(np.float16(float(fl * q)).view(np.uint16))
+
+
+def test_narrow_fp16_exact_rounding():
+    rng = np.random.default_rng(6)
+    vals = np.concatenate([
+        rng.standard_normal(3000) * 10.0 ** rng.integers(-9, 6, 3000),
+        np.array([65504.0, 65519.99, 65520.0, 6.1035156e-05, 5.96e-08, 2.98e-08, 2.99e-08,
+                  -0.0, 0.0, 1.0 + 2 ** -11, 1.0 + 3 * 2 ** -11]),
+    ]).astype(np.float32)
+    got = O.narrow(vals, O.FP16)
+    for x, g in zip(vals, got):
+        want = _fp16_rne_exact(x)
+        assert int(g) == want, (float(x), hex(int(g)), hex(want))
+
+
+def test_nonfinite_detection_exhaustive():
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    m16 = O.nonfinite_mask(bits, O.FP16)
+    assert (m16 == ~np.isfinite(bits.view(np.float16))).all() and m16.sum() == 2048
+    mb = O.nonfinite_mask(bits, O.BF16)
+    ref = np.array([not math.isfinite(struct.unpack(">f", struct.pack(">HH", h, 0))[0])
+                    for h in range(65536)])
+    assert (mb == ref).all() and mb.sum() == 256
+    rng = np.random.default_rng(1)
+    u = rng.integers(0, 2 ** 32, 200000, dtype=np.uint64).astype(np.uint32)
+    u[:4] = [0x7F800000, 0xFF800000, 0x7FC00000, 0x7F7FFFFF]
+    assert (O.nonfinite_mask(u.view(np.float32), O.FP32) == ~np.isfinite(u.view(np.float32))).all()
+
+
+# ---------------------------------------------------------------- norm and clip
+
+@pytest.mark.parametrize("dtype", [O.FP16, O.BF16, O.FP32])
+def test_sum_of_squares_exact(dtype):
+    rng = np.random.default_rng(7)
+    for n in (1, 5, 333, 4096):
+        x64 = rng.standard_normal(n) * 10.0 ** rng.integers(-3, 3, n)
+        if dtype == O.FP16:
+            x = x64.astype(np.float16).view(np.uint16)
+        elif dtype == O.BF16:
+            x = (x64.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+        else:
+            x = x64.astype(np.float32)
+        vals = O.widen(x, dtype)
+        exact = sum((Fraction(float(v)) ** 2 for v in vals), Fraction(0))
+        got = O.sum_of_squares(x, dtype)
+        assert abs(Fraction(got) - exact) <= exact * Fraction(n + 1, 2 ** 53)
+
+
+def test_norm_special_cases():
+    z = np.zeros(1000, np.float32)
+    assert O.sum_of_squares(z, O.FP32) == 0.0
+    x = np.zeros(999, np.float16)
+    x[417] = np.float16(-3.5)
+    bits = x.view(np.uint16)
+    s = O.sum_of_squares(bits, O.FP16)
+    assert s == 12.25
+    norm, coef, gs = O.clip_scalars(s, 2.0 ** 10, 4, 0.0)
+    assert norm == 3.5 / (2 ** 10 * 4) and coef == 1.0 and gs == np.float32(1.0 / 4096)
+    rng = np.random.default_rng(3)
+    y = rng.standard_normal(5000).astype(np.float32)
+    a = O.sum_of_squares(y, O.FP32)
+    b = O.sum_of_squares(y[rng.permutation(5000)], O.FP32)
+    assert abs(a - b) <= 1e-15 * a
+
+
+def test_clip_brings_norm_to_max():
+    rng = np.random.default_rng(4)
+    x = (rng.standard_normal(20000) * 0.05 * 1024).astype(np.float16).view(np.uint16)
+    S, K, mx = 1024.0, 2, 1.0
+    s = O.sum_of_squares(x, O.FP16)
+    norm, coef, gs = O.clip_scalars(s, S, K, mx)
+    assert norm > mx and coef < 1.0
+    g = O.widen(x, O.FP16).astype(np.float64) * float(gs)
+    assert abs(math.sqrt(float(np.sum(g * g))) - mx) < 1e-6
+    # below the threshold nothing is clipped
+    _, coef2, gs2 = O.clip_scalars(s, S, K, 10 * norm)
+    assert coef2 == 1.0 and gs2 == np.float32(1.0 / (S * K))
+
+
+def test_overflow_and_norm_flags():
+    x = np.ones(100, np.float16)
+    x[37] = np.inf
+    r = O.overflow_and_norm(x.view(np.uint16), O.FP16, 1.0, 1, 1.0)
+    assert r["overflow"] == 1
+    x[37] = np.nan
+    assert O.overflow_and_norm(x.view(np.uint16), O.FP16, 1.0, 1, 1.0)["overflow"] == 1
+    x[37] = 65504
+    assert O.overflow_and_norm(x.view(np.uint16), O.FP16, 1.0, 1, 1.0)["overflow"] == 0
+
+
+# ---------------------------------------------------------------- accumulation
+
+def test_accumulate_identical_microbatches():
+    rng = np.random.default_rng(8)
+    numels = [37, 1000, 5]
+    src = [(rng.standard_normal(n) * 1e-3 * 2 ** 14).astype(np.float16).view(np.uint16)
+           for n in numels]
+    ent = O.shard_entries(numels, 8, 0, O.flat_layout(numels, 8)[1])
+    for K in (1, 2, 4, 16):
+        acc = np.full(O.flat_layout(numels, 8)[1], np.float32(np.nan))
+        O.flatten_accumulate(src, O.FP16, ent, acc, overwrite=True)
+        for _ in range(K - 1):
+            O.flatten_accumulate(src, O.FP16, ent, acc, overwrite=False)
+        for t, s, n, d in ent:
+            assert (acc[d:d + n] / np.float32(K) == O.widen(src[t], O.FP16)).all()
+    bucket = np.zeros(O.flat_layout(numels, 8)[1], np.uint16)
+    O.flatten_copy(src, ent, bucket)
+    assert (bucket[ent[1][3]:ent[1][3] + 1000] == src[1]).all()
+
+
+def test_accumulated_step_equals_single_step():
+    """K identical micro-batches with the mean folded into grad_scale give the
+    same update, bit for bit, as one micro-batch."""
+    rng = np.random.default_rng(9)
+    n = 3000
+    x = (rng.standard_normal(n) * 1e-3 * 2 ** 14).astype(np.float16).view(np.uint16)
+    master = (rng.standard_normal(n) * 0.02).astype(np.float32)
+    m = np.zeros(n, np.float32)
+    v = np.zeros(n, np.float32)
+    hp = O.AdamW()
+    st = O.scaler_init(initial_scale_power=14)
+    r1 = O.optimizer_step(x, O.FP16, master, m, v, st, hp, 1.0, 1, O.FP16)
+    acc = O.widen(x, O.FP16).copy()
+    for _ in range(15):
+        acc = acc + O.widen(x, O.FP16)
+    r16 = O.optimizer_step(acc, O.FP32, master, m, v, st, hp, 1.0, 16, O.FP16)
+    for a, b in zip(r1[:4], r16[:4]):
+        assert (a.view(np.uint32 if a.dtype == np.float32 else np.uint16) ==
+                b.view(np.uint32 if b.dtype == np.float32 else np.uint16)).all()
+
+
+# ---------------------------------------------------------------- loss scaler
+
+def test_scaler_tiny_config_trajectory():
+    """Five steps, +inf in step 3's grads, dynamic scaler from 2^16 with
+    hysteresis 1: the scales in force are 2^16, 2^16, 2^16, 2^15, 2^15 and Adam
+    steps 1, 2, (skipped), 3, 4 are applied."""
+    st = O.scaler_init(initial_scale_power=16, window=1000, hysteresis=1)
+    scales, ts = [], []
+    for k in range(1, 6):
+        scales.append(st.scale)
+        st = O.scaler_update(st, 1 if k == 3 else 0, 0.9, 0.999)
+        ts.append(None if st.last_skip else st.t)
+    assert scales == [2.0 ** 16] * 3 + [2.0 ** 15] * 2
+    assert ts == [1, 2, None, 3, 4]
+
+
+def _scale_by_runs(seq, init, W, H, mn):
+    """Independent statement of the scaler: walk maximal runs of equal flags.
+    A clean run of length L grows the scale floor((g0 + L) / W) times, where g0
+    is the clean count carried in (0 after any overflow). An overflow run of
+    length R halves the scale once per H overflows in it, floored at min."""
+    scale = init
+    carried = 0
+    i = 0
+    while i < len(seq):
+        j = i
+        while j < len(seq) and seq[j] == seq[i]:
+            j += 1
+        L = j - i
+        if seq[i] == 0:
+            total = carried + L
+            scale *= 2.0 ** (total // W)
+            carried = total % W
+        else:
+            for _ in range(L // H):
+                scale = max(scale / 2.0, mn)
+            carried = 0
+        i = j
+    return scale
+
+
+def test_scaler_brute_force_all_sequences():
+    import itertools
+    for W in (1, 2, 3):
+        for H in (1, 2):
+            for L in range(0, 11):
+                for seq in itertools.product((0, 1), repeat=L):
+                    st = O.scaler_init(initial_scale_power=4, window=W, hysteresis=H, min_scale=1.0)
+                    for f in seq:
+                        st = O.scaler_update(st, f, 0.9, 0.999)
+                    assert st.scale == _scale_by_runs(seq, 16.0, W, H, 1.0), (W, H, seq)
+                    assert st.t == len(seq) - sum(seq)
+
+
+def test_scaler_static_and_floor():
+    st = O.scaler_init(dynamic=False, static_scale=1.0)
+    for f in (1, 0, 1, 1, 0):
+        st = O.scaler_update(st, f, 0.9, 0.999)
+        assert st.scale == 1.0 and st.last_skip == f
+    assert st.t == 2
+    st = O.scaler_init(initial_scale_power=2, hysteresis=1, min_scale=1.0)
+    for _ in range(6):
+        st = O.scaler_update(st, 1, 0.9, 0.999)
+        assert st.last_skip == 1
+    assert st.scale == 1.0 and st.t == 0
+
+
+def test_beta_powers():
+    st = O.scaler_init()
+    for _ in range(50):
+        st = O.scaler_update(st, 0, 0.9, 0.999)
+    b1 = Fraction(float(np.float32(0.9)))
+    b2 = Fraction(float(np.float32(0.999)))
+    assert abs(Fraction(st.beta1_pow) - b1 ** 50) <= b1 ** 50 * Fraction(60, 2 ** 53)
+    assert abs(Fraction(st.beta2_pow) - b2 ** 50) <= b2 ** 50 * Fraction(60, 2 ** 53)
+
+
+# ---------------------------------------------------------------- AdamW
+
+def _ulp32(x):
+    x = np.abs(np.asarray(x, np.float32))
+    return np.spacing(np.maximum(x, np.float32(1.1754944e-38))).astype(np.float64)
+
+
+@pytest.mark.parametrize("sigma", [1e-8, 1e-6, 1e-3, 1.0])
+def test_adamw_first_step_closed_form(sigma):
+    """With zero moments at t = 0 the bias-corrected first update is
+    lr * g / (|g| + eps)."""
+    rng = np.random.default_rng(11)
+    n = 100000
+    g = (rng.standard_normal(n) * sigma).astype(np.float32)
+    hp = O.AdamW(lr=1e-3, weight_decay=0.01)
+    c = O.adamw_constants(hp, 1.0, 1.0)
+    p, m, v = O.adamw_update(g, O.FP32, np.float32(1.0), np.zeros(n, np.float32),
+                             np.zeros(n, np.float32), np.zeros(n, np.float32), c)
+    g64 = g.astype(np.float64)
+    closed = -1e-3 * g64 / (np.abs(g64) + 1e-8)
+    err = np.abs(p.astype(np.float64) - closed) / _ulp32(np.float32(1e-3))
+    assert err.max() <= 4.0
+
+
+def test_bias_correction_cancels_at_t1():
+    c = O.adamw_constants(O.AdamW(), 1.0, 1.0)
+    assert np.float32(1.0 - float(np.float32(0.9))) == c["omb1"]
+    assert np.float32(1.0 - float(np.float32(0.999))) == c["omb2"]
+
+
+def _adamw_decimal(g, p, m, v, lr, b1, b2, eps, wd, b1pow, b2pow):
+    """Real-number AdamW (decoupled decay, bias correction) in 60-digit
+    decimal arithmetic from the exact values of the fp32 inputs."""
+    D = decimal.Decimal
+    g, p, m, v = D(float(g)), D(float(p)), D(float(m)), D(float(v))
+    lr, b1, b2, eps, wd = (D(float(np.float32(t))) for t in (lr, b1, b2, eps, wd))
+    bp1 = D(b1pow) * b1
+    bp2 = D(b2pow) * b2
+    m1 = b1 * m + (1 - b1) * g
+    v1 = b2 * v + (1 - b2) * g * g
+    upd = (lr / (1 - bp1)) * m1 / (v1.sqrt() / (1 - bp2).sqrt() + eps)
+    return p * (1 - lr * wd) - upd, m1, v1, abs(upd), abs(p * (1 - lr * wd))
+
+
+def test_adamw_against_high_precision():
+    decimal.getcontext().prec = 60
+    rng = np.random.default_rng(12)
+    n = 2048
+    hp = O.AdamW(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01)
+    for t_prev, gsig in ((0, 1e-3), (1, 2e-3), (7, 1.0), (100, 1e-7)):
+        b1p = float(np.float32(0.9)) ** t_prev
+        b2p = float(np.float32(0.999)) ** t_prev
+        g = (rng.standard_normal(n) * gsig).astype(np.float32)
+        p = (rng.standard_normal(n) * 0.02).astype(np.float32)
+        m = (rng.standard_normal(n) * gsig * 0.1).astype(np.float32) if t_prev else np.zeros(n, np.float32)
+        v = ((rng.standard_normal(n) * gsig) ** 2 * 1e-3).astype(np.float32) if t_prev else np.zeros(n, np.float32)
+        c = O.adamw_constants(hp, b1p, b2p)
+        P, M, V = O.adamw_update(g, O.FP32, np.float32(1.0), p, m, v, c)
+        for i in range(n):
+            pe, me, ve, au, ap = _adamw_decimal(g[i], p[i], m[i], v[i], hp.lr, hp.beta1, hp.beta2,
+                                                hp.eps, hp.weight_decay, b1p, b2p)
+            # m: three roundings; the sum may cancel, so bound by its operands
+            bm = _ulp32(np.float32(0.9) * m[i]) + _ulp32(np.float32(0.1) * g[i]) + _ulp32(M[i])
+            assert abs(decimal.Decimal(float(M[i])) - me) <= decimal.Decimal(float(bm))
+            # v: all terms non-negative, a few roundings relative to the result
+            assert abs(decimal.Decimal(float(V[i])) - ve) <= decimal.Decimal(2.5 * _ulp32(V[i]))
+            # p: error bounded by a few ulp of the larger operand of the last subtraction
+            bound = 6.0 * max(_ulp32(np.float32(float(au))), _ulp32(np.float32(float(ap)))) + _ulp32(P[i])
+            assert abs(decimal.Decimal(float(P[i])) - pe) <= decimal.Decimal(float(bound)), (t_prev, i)
+
+
+def test_adamw_special_cases():
+    hp = O.AdamW()
+    c = O.adamw_constants(hp, 0.9, 0.999)
+    p0 = np.array([0.5, -0.25, 0.0, 1e-20], np.float32)
+    m0 = np.array([1e-3, 0.0, -2e-4, 0.0], np.float32)
+    v0 = np.array([1e-6, 0.0, 1e-8, 0.0], np.float32)
+    P, M, V = O.adamw_update(np.zeros(4, np.float32), O.FP32, np.float32(1.0), p0, m0, v0, c)
+    assert (M == c["b1"] * m0).all() and (V == c["b2"] * v0).all()
+    assert P[1] == p0[1] * c["decay"] and P[3] == p0[3] * c["decay"]
+    # large |g|: the Adam term has magnitude close to lr
+    g = np.array([3.0, -5.0], np.float32)
+    cc = O.adamw_constants(hp, 1.0, 1.0)
+    P, _, _ = O.adamw_update(g, O.FP32, np.float32(1.0), np.array([0.1, 0.1], np.float32),
+                             np.zeros(2, np.float32), np.zeros(2, np.float32), cc)
+    d = P - np.float32(0.1) * cc["decay"]
+    assert np.allclose(d, [-1e-3, 1e-3], rtol=1e-5)
+
+
+def test_zero1_demo_update():
+    """Demo variant: no bias correction, no decay, lr 0.01, every grad 1/4.
+    Each element moves down by lr*0.1*g / (sqrt(0.001)*g + 1e-8)."""
+    d = GOLDEN["zero1_demo"]
+    hp = O.AdamW(lr=d["lr"], beta1=d["beta1"], beta2=d["beta2"], eps=d["eps"], weight_decay=0.0)
+    c = O.adamw_constants(hp, 1.0, 1.0, bias_correction=False)
+    n = sum(d["sizes"])
+    g = np.full(n, 1.0 / d["world_size"], np.float32)
+    p0 = np.random.default_rng(0).standard_normal(n).astype(np.float32)
+    P, _, _ = O.adamw_update(g, O.FP32, np.float32(1.0), p0, np.zeros(n, np.float32),
+                             np.zeros(n, np.float32), c)
+    decimal.getcontext().prec = 40
+    D = decimal.Decimal
+    gg = D(1) / D(4)
+    closed = D("0.01") * D("0.1") * gg / (D("0.001").sqrt() * gg + D("1e-8"))
+    assert abs(float(closed) - 0.0316227366) < 1e-10
+    drop = p0.astype(np.float64) - P.astype(np.float64)
+    assert np.max(np.abs(drop - float(closed))) <= 2 * np.max(_ulp32(p0)) + 1e-9
+
+
+# ---------------------------------------------------------------- whole step
+
+def test_stage1_concat_invariant():
+    rng = np.random.default_rng(13)
+    numels = [int(s) for s in rng.integers(1, 5000, 9)]
+    _, total = O.flat_layout(numels, 64)
+    x = np.zeros(total, np.uint16)
+    off, _ = O.flat_layout(numels, 64)
+    for o, n in zip(off, numels):
+        x[o:o + n] = (rng.standard_normal(n) * 1e-3 * 2 ** 16).astype(np.float16).view(np.uint16)
+    master = np.zeros(total, np.float32)
+    for o, n in zip(off, numels):
+        master[o:o + n] = (rng.standard_normal(n) * 0.02).astype(np.float32)
+    hp = O.AdamW()
+    st = O.scaler_init()
+    full = O.optimizer_step(x, O.FP16, master, np.zeros(total, np.float32),
+                            np.zeros(total, np.float32), st, hp, 1.0, 1, O.FP16)
+    for N in (1, 2, 3, 4, 7, 8):
+        padded = O.align_up(total, N * 64)
+        xp = np.concatenate([x, np.zeros(padded - total, np.uint16)])
+        mp = np.concatenate([master, np.zeros(padded - total, np.float32)])
+        ssq = 0.0
+        pieces = []
+        for r in range(N):
+            lo, hi = O.shard_range(total, N, r, 64)
+            ssq += O.sum_of_squares(xp[lo:hi], O.FP16)
+            pieces.append((lo, hi))
+        assert abs(ssq - full[5]["sumsq"]) <= 1e-12 * full[5]["sumsq"]
+        norm, coef, gs = O.clip_scalars(full[5]["sumsq"], st.scale, 1, 1.0)
+        c = O.adamw_constants(hp, st.beta1_pow, st.beta2_pow)
+        outs = [O.adamw_update(xp[lo:hi], O.FP16, gs, mp[lo:hi], np.zeros(hi - lo, np.float32),
+                               np.zeros(hi - lo, np.float32), c) for lo, hi in pieces]
+        for k in range(3):
+            cat = np.concatenate([o[k] for o in outs])[:total]
+            assert (cat.view(np.uint32) == full[k].view(np.uint32)).all()
+        # padding stays exactly zero
+        assert (np.concatenate([o[0] for o in outs])[total:] == 0).all()
+
+
+def test_overflow_step_leaves_state():
+    rng = np.random.default_rng(14)
+    n = 777
+    x = (rng.standard_normal(n) * 1e-3 * 2 ** 16).astype(np.float16)
+    x[n - 1] = np.inf
+    master = (rng.standard_normal(n) * 0.02).astype(np.float32)
+    m = (rng.standard_normal(n) * 1e-4).astype(np.float32)
+    v = (rng.standard_normal(n) ** 2 * 1e-7).astype(np.float32)
+    st = O.scaler_init(t=5, beta1_pow=0.9 ** 5, beta2_pow=0.999 ** 5)
+    r = O.optimizer_step(x.view(np.uint16), O.FP16, master.copy(), m.copy(), v.copy(), st,
+                         O.AdamW(), 1.0, 1, O.FP16)
+    assert r[3] is None
+    assert (r[0] == master).all() and (r[1] == m).all() and (r[2] == v).all()
+    assert r[4].scale == st.scale / 2 and r[4].t == 5 and r[4].last_skip == 1
+    assert r[4].beta1_pow == st.beta1_pow
