@@ -1,0 +1,282 @@
+"""Benchmark of one data-parallel rank's ZeRO mixed-precision optimizer step
+on one MI355X.
+
+A step is one pass of the whole hot path over the rank's shard:
+  zds_grad_accumulate (copy the per-tensor grads into the flat bucket),
+  zds_overflow_and_norm, zds_adam_step, zds_loss_scaler_update.
+Default workload: the Llama-7B-shaped Stage-1 shard at N = 8 (rank 0: 33
+table entries, 842,301,440 params), bf16 grads N(0, 2e-3), fp32 master
+N(0, 0.02), moments shaped like one prior step, static loss scale 1, clip
+1.0, AdamW lr 1e-3 (0.9, 0.999) eps 1e-8 wd 0.01, bf16 params out.
+
+Prints one JSON line. `value` is params updated per second over the timed
+steps (inputs resident in HBM); `roofline` is for the dominant kernel
+(zds_adam_step, 28 algorithmic bytes per param for 16-bit grads), timed with
+HIP events on the stream it runs on; `cpu_baseline` times the CPU oracle on a
+bounded sample of the same workload on the host.
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+METRIC = "params updated/sec and achieved HBM GB/s (% of peak) per ZeRO Adam step"
+HBM_PEAK_GBS = 8000.0
+
+
+def _parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="llama7b_s1",
+                    choices=["llama7b_s1", "llama7b_s1_accum16", "llama7b_whole_1024", "llama65b_s1", "tiny"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample", type=int, default=1 << 24, help="oracle sample size (params)")
+    ap.add_argument("--cpu-repeats", type=int, default=8, help="oracle passes over the sample")
+    return ap.parse_args()
+
+
+# ------------------------------------------------------------------ workloads
+
+def _workload(name):
+    from workloads import llama_7b_tensors, llama_65b_tensors, llama_7b_split_1024, tiny_shard_sizes
+    if name == "llama7b_s1":
+        return dict(tensors=llama_7b_tensors(), world=8, rank=0, gdt="bf16", pdt="bf16", sigma=2e-3,
+                    accum=1, scale=None, prior=True, mode="copy")
+    if name == "llama7b_s1_accum16":
+        return dict(tensors=llama_7b_tensors(), world=8, rank=0, gdt="fp16", pdt="fp16", sigma=1e-3,
+                    accum=16, scale=14, prior=True, mode="accumulate")
+    if name == "llama7b_whole_1024":
+        return dict(tensors=llama_7b_split_1024(), world=1, rank=0, gdt="fp16", pdt="fp16", sigma=1e-3,
+                    accum=1, scale=16, prior=False, mode="copy")
+    if name == "llama65b_s1":
+        return dict(tensors=llama_65b_tensors(), world=8, rank=0, gdt="bf16", pdt="bf16", sigma=1e-3,
+                    accum=1, scale=None, prior=True, mode="copy")
+    return dict(tensors=tiny_shard_sizes(), world=1, rank=0, gdt="fp16", pdt="fp16", sigma=1e-3,
+                accum=1, scale=16, prior=False, mode="copy")
+
+
+def _bytes_per_param(w):
+    """Algorithmic HBM bytes per param of each kernel of one step."""
+    g = 2
+    if w["mode"] == "accumulate":
+        acc = 6 + 10 * (w["accum"] - 1)      # overwrite once, then accumulate
+        return dict(accumulate=acc / w["accum"], accum_total=acc, norm=4, adam=30)
+    return dict(accumulate=2 * g, accum_total=2 * g, norm=g, adam=28)
+
+
+# ------------------------------------------------------------------ GPU part
+
+def run_gpu(args, w):
+    import torch
+    from zero_sharded_mixed_tensor_amd import zds
+    from zero_sharded_mixed_tensor_amd.step import ShardStep
+
+    tdt = {"fp16": torch.float16, "bf16": torch.bfloat16}
+    numels = [n for _, n in w["tensors"]]
+    _, total = zds.zds_flat_layout(numels, 64)
+    lo, hi = zds.zds_shard_range(total, w["world"], w["rank"], 64)
+    n = hi - lo
+    plan = zds.zds_plan_create(numels, 64, lo, hi)
+    ents = plan.entries()
+    dev = torch.device("cuda", 0)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(1234)
+
+    # per-tensor grads of the tensors this shard touches (whole tensors)
+    srcs = [None] * len(numels)
+    for t, _, _, _ in ents:
+        srcs[t] = torch.empty(numels[t], dtype=tdt[w["gdt"]], device=dev)
+    scale = 1.0 if w["scale"] is None else 2.0 ** w["scale"]
+
+    def fill_grads(k):
+        g = torch.Generator(device=dev)
+        g.manual_seed(5000 + k)
+        for s in srcs:
+            if s is not None:
+                s.normal_(0.0, w["sigma"] * scale, generator=g)
+
+    fill_grads(0)
+    master = torch.empty(n, dtype=torch.float32, device=dev).normal_(0.0, 0.02, generator=gen)
+    if w["prior"]:
+        m = torch.empty(n, dtype=torch.float32, device=dev).normal_(0.0, 0.1 * w["sigma"], generator=gen)
+        v = torch.empty(n, dtype=torch.float32, device=dev).normal_(0.0, w["sigma"], generator=gen)
+        v.mul_(v).mul_(0.001)
+        t0, b1p, b2p = 1, float(torch.tensor(0.9, dtype=torch.float32)), float(torch.tensor(0.999, dtype=torch.float32))
+    else:
+        m = torch.zeros(n, dtype=torch.float32, device=dev)
+        v = torch.zeros(n, dtype=torch.float32, device=dev)
+        t0, b1p, b2p = 0, 1.0, 1.0
+    p16 = master.to(tdt[w["pdt"]])
+    if w["mode"] == "accumulate":
+        bucket = torch.zeros(n, dtype=torch.float32, device=dev)
+    else:
+        bucket = torch.zeros(n, dtype=tdt[w["gdt"]], device=dev)
+    cfg = (zds.scaler_config(dynamic=False, static_scale=1.0) if w["scale"] is None
+           else zds.scaler_config(initial_scale_power=w["scale"], window=1000, hysteresis=1))
+    st = ShardStep(n, zds.hparams(), cfg, max_norm=1.0, accum_steps=w["accum"], t0=t0,
+                   beta1_pow0=b1p, beta2_pow0=b2p)
+    torch.cuda.synchronize()
+
+    ev = {k: [] for k in ("accumulate", "norm", "adam", "scaler")}
+
+    def one_step(record):
+        def mark():
+            e = torch.cuda.Event(enable_timing=True)
+            e.record()
+            return e
+        e0 = mark() if record else None
+        if w["mode"] == "accumulate":
+            for k in range(w["accum"]):
+                zds.zds_grad_accumulate(plan, srcs, bucket, zds.ZDS_OVERWRITE if k == 0 else zds.ZDS_ACCUMULATE)
+        else:
+            zds.zds_grad_accumulate(plan, srcs, bucket, zds.ZDS_COPY)
+        e1 = mark() if record else None
+        st.norm(bucket)
+        e2 = mark() if record else None
+        st.adam(bucket, master, m, v, p16)
+        e3 = mark() if record else None
+        st.scaler()
+        e4 = mark() if record else None
+        if record:
+            ev["accumulate"].append((e0, e1))
+            ev["norm"].append((e1, e2))
+            ev["adam"].append((e2, e3))
+            ev["scaler"].append((e3, e4))
+
+    for _ in range(args.warmup):
+        one_step(False)
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for _ in range(args.steps):
+        one_step(True)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t_start
+    state = st.read_state()
+    sc = st.read_scalars()
+    if sc.overflow or state.steps_skipped:
+        raise SystemExit("unexpected overflow in the benchmark workload")
+
+    bpp = _bytes_per_param(w)
+    kern = {}
+    for k, pairs in ev.items():
+        ms = sum(a.elapsed_time(b) for a, b in pairs) / len(pairs)
+        entry = {"ms_avg": round(ms, 5)}
+        if k == "accumulate":
+            entry["gbs"] = round(bpp["accum_total"] * n / (ms * 1e-3) / 1e9, 1)
+        elif k in ("norm", "adam"):
+            entry["gbs"] = round(bpp[k] * n / (ms * 1e-3) / 1e9, 1)
+        kern[k] = entry
+    adam_ms = kern["adam"]["ms_avg"]
+    achieved = 28.0 * n / (adam_ms * 1e-3) / 1e9 if w["mode"] != "accumulate" else 30.0 * n / (adam_ms * 1e-3) / 1e9
+    step_bytes = (bpp["accum_total"] + bpp["norm"] + bpp["adam"]) * n
+    ms_per_step = elapsed / args.steps * 1e3
+    return dict(n=n, entries=len(ents), elapsed=elapsed, ms_per_step=ms_per_step, kernels=kern,
+                adam_gbs=achieved, step_gbs=step_bytes / (elapsed / args.steps) / 1e9,
+                step_bytes_per_param=bpp["accum_total"] + bpp["norm"] + bpp["adam"],
+                adam_bytes_per_param=28 if w["mode"] != "accumulate" else 30)
+
+
+# ------------------------------------------------------------------ CPU oracle part
+
+def run_cpu_baseline(w, sample, repeats):
+    """Time the oracle's step (flatten copy, overflow + norm, AdamW + cast,
+    scaler update) `repeats` times on the first `sample` params of the same
+    workload, with inputs generated before timing. Single process: NumPy's
+    elementwise kernels use one thread."""
+    import numpy as np
+    import oracle as O
+    from workloads import draw_grads, draw_master, draw_prior_moments
+
+    n = sample
+    g = draw_grads(n, w["gdt"], w["sigma"], 1.0 if w["scale"] is None else 2.0 ** w["scale"], 1, 2, 0)
+    master = draw_master(n, 0.02, 1, 2)
+    if w["prior"]:
+        m, v = draw_prior_moments(n, w["sigma"], 1, 2)
+        st = O.scaler_init(dynamic=w["scale"] is not None, initial_scale_power=w["scale"] or 0,
+                           static_scale=1.0, t=1, beta1_pow=float(np.float32(0.9)),
+                           beta2_pow=float(np.float32(0.999)))
+    else:
+        m = np.zeros(n, np.float32)
+        v = np.zeros(n, np.float32)
+        st = O.scaler_init(dynamic=w["scale"] is not None, initial_scale_power=w["scale"] or 0,
+                           static_scale=1.0)
+    ent = [(0, 0, n, 0)]
+    bucket = np.zeros(n, np.uint16)
+    t0 = time.perf_counter()
+    for _ in range(repeats):
+        O.flatten_copy([g], ent, bucket)
+        r = O.optimizer_step(bucket, w["gdt"], master, m, v, st, O.AdamW(), 1.0, 1, w["pdt"])
+        assert r[3] is not None
+    dt = time.perf_counter() - t0
+    return dict(value=n * repeats / dt, seconds=dt, n=n, repeats=repeats)
+
+
+def main():
+    args = _parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(the step shards by running this same kernel set on each rank's "
+              "slice); run with --gpus 1.", file=sys.stderr)
+        return 2
+    w = _workload(args.workload)
+    r = run_gpu(args, w)
+    out = {
+        "metric": METRIC,
+        "value": round(r["n"] * args.steps / r["elapsed"], 1),
+        "unit": "params/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(r["ms_per_step"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": args.workload,
+            "params": r["n"],
+            "table_entries": r["entries"],
+            "grad_dtype": w["gdt"],
+            "param_dtype": w["pdt"],
+            "state_dtype": "fp32",
+            "accum_steps": w["accum"],
+            "loss_scale": "static 1" if w["scale"] is None else "dynamic 2^%d" % w["scale"],
+            "clip": 1.0,
+            "step_bytes_per_param": r["step_bytes_per_param"],
+        },
+        "step_gbs": round(r["step_gbs"], 1),
+        "step_hbm_frac": round(r["step_gbs"] / HBM_PEAK_GBS, 4),
+        "kernels": r["kernels"],
+        "roofline": {
+            "kernel": "zds_adam_step",
+            "bound": "hbm",
+            "achieved": round(r["adam_gbs"], 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(r["adam_gbs"] / HBM_PEAK_GBS, 4),
+            "bytes_per_param": r["adam_bytes_per_param"],
+            "traffic": None,
+        },
+    }
+    if not args.no_cpu_baseline:
+        c = run_cpu_baseline(w, args.cpu_sample, args.cpu_repeats)
+        out["cpu_baseline"] = {
+            "value": round(c["value"], 1),
+            "unit": "params/s",
+            "cores": 1,
+            "kind": "oracle",
+            "sample": "%d passes of one whole oracle step (copy, overflow+norm, AdamW, cast, scaler) "
+                      "over the first %d params of the same workload, %.1f s"
+                      % (c["repeats"], c["n"], c["seconds"]),
+        }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

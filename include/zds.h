@@ -1,0 +1,267 @@
+/*
+ * zds.h - C ABI of the ZeRO-sharded mixed-precision optimizer-step library
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * One data-parallel rank's share of the ZeRO optimizer step, on the rank's
+ * contiguous shard of the flat parameter buffer:
+ *
+ *   per micro-batch   zds_grad_accumulate     flatten / accumulate grads
+ *   per step          zds_overflow_and_norm   inf/NaN flag, global L2 norm, clip
+ *                     zds_adam_step           fused AdamW + unscale/clip + cast
+ *                     zds_loss_scaler_update  dynamic loss-scale state machine
+ *
+ * Pages the operations are taken from (cited by title and section):
+ *   [algomooc] algomooc.com interview answer on the DeepSpeed framework
+ *   [aidhplus] aidhplus.com "DeepSpeed" overview
+ *   [csdn]     devpress.csdn.net DeepSpeed distributed-training tutorial
+ *   [aiqz]     aiqz.cc "DeepSpeed ZeRO引擎深入"
+ *   [ch01]     jwzheng96.github.io llm-train-tutorials, DeepSpeed chapter 1
+ * The training loop of [csdn] §3.3 replaces loss.backward() by
+ * engine.backward(loss) and optimizer.step() by engine.step(); here
+ * engine.backward's gradient handling is zds_grad_accumulate and
+ * engine.step is the other three calls, in the order listed above, on one
+ * stream.
+ *
+ * Conventions for every function:
+ *  - Plain C types only. Pointers documented as "device" are HIP device
+ *    pointers the caller allocated and owns; the library never frees them.
+ *    "host" pointers are read (or written) before the call returns.
+ *  - `stream` is a hipStream_t (NULL selects the null stream). Hot calls only
+ *    enqueue work on it and never synchronise the host; the caller keeps the
+ *    buffers alive until the stream has run the work.
+ *  - Arguments are checked before anything is launched. On failure nothing is
+ *    enqueued, a status other than ZDS_OK is returned and zds_last_error()
+ *    holds a message (thread-local, valid until the next call on that thread).
+ *  - Zero-length inputs return ZDS_OK and launch nothing, except
+ *    zds_overflow_and_norm, which still writes the scalars of an empty shard.
+ *  - No C++ exception crosses this interface.
+ */
+#ifndef ZDS_H
+#define ZDS_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ZDS_ABI_VERSION 1
+
+typedef enum zds_status {
+  ZDS_OK = 0,
+  ZDS_EINVAL = 1, /* bad argument: null pointer, bad enum, size, range */
+  ZDS_EALIGN = 2, /* a pointer is not aligned to its element size */
+  ZDS_ENOMEM = 3, /* the library could not allocate its own memory */
+  ZDS_EHIP = 4    /* a HIP runtime call or kernel launch failed */
+} zds_status;
+
+typedef enum zds_dtype { ZDS_FP16 = 0, ZDS_BF16 = 1, ZDS_FP32 = 2 } zds_dtype;
+
+typedef enum zds_accum_mode {
+  ZDS_COPY = 0,       /* dst[j]  = src[j]          16-bit -> same 16-bit type */
+  ZDS_OVERWRITE = 1,  /* dst[j]  = fp32(src[j])    first micro-batch          */
+  ZDS_ACCUMULATE = 2  /* dst[j] += fp32(src[j])    later micro-batches        */
+} zds_accum_mode;
+
+/* AdamW hyperparameters ([csdn] §3.2 optimizer block: lr, betas, eps,
+ * weight_decay). Used as fp32 values. */
+typedef struct zds_adamw_hparams {
+  float lr;
+  float beta1;
+  float beta2;
+  float eps;
+  float weight_decay;
+} zds_adamw_hparams;
+
+/* Loss-scaler configuration ([csdn] §3.2 fp16 block: loss_scale 0 selects the
+ * dynamic scaler; loss_scale_window, initial_scale_power, hysteresis,
+ * min_loss_scale). With dynamic == 0 the scale stays at static_scale (the
+ * bf16 case). */
+typedef struct zds_scaler_config {
+  int32_t dynamic;
+  int32_t initial_scale_power; /* initial scale = 2^power (dynamic)        */
+  int32_t window;              /* clean steps before the scale doubles     */
+  int32_t hysteresis;          /* overflows in a row before it halves (>=1) */
+  float min_scale;
+  float static_scale;
+} zds_scaler_config;
+
+/* Device-resident step state, 64 bytes. Written only by
+ * zds_step_state_init / zds_loss_scaler_update (or their host twins). */
+typedef struct zds_step_state {
+  float scale;            /* loss scale S in force for the next step        */
+  int32_t good_steps;     /* clean steps since the scale last changed       */
+  int32_t hyst_left;      /* overflows still tolerated before a halving     */
+  int32_t window;
+  int32_t hysteresis;
+  float min_scale;
+  int32_t dynamic;
+  uint32_t last_skip;     /* 1 if the last step was skipped (overflow)      */
+  int64_t t;              /* Adam steps applied                             */
+  double beta1_pow;       /* beta1^t (float64 running product)              */
+  double beta2_pow;       /* beta2^t                                        */
+  uint32_t steps_seen;    /* steps taken, skipped ones included             */
+  uint32_t steps_skipped;
+} zds_step_state;
+
+/* Device-resident per-step scalars, 32 bytes, written by
+ * zds_overflow_and_norm and read by zds_adam_step / zds_loss_scaler_update. */
+typedef struct zds_step_scalars {
+  uint32_t overflow;   /* 1 if any gradient element is inf or NaN           */
+  int32_t accum_steps; /* K used for the mean over micro-batches            */
+  double sumsq;        /* sum of x^2 over the raw (scaled, summed) grads    */
+  float norm;          /* sqrt(sumsq) / (S * K), before clipping            */
+  float clip_coef;     /* max_norm / (norm + 1e-6) if norm > max_norm, else 1 */
+  float grad_scale;    /* clip_coef / (S * K), the factor Adam applies      */
+  float scale_used;    /* S read from the step state                        */
+} zds_step_scalars;
+
+/* ---------------------------------------------------------------------------
+ * Host-only geometry (no GPU needed).
+ * Flat layout: tensor i starts at the next multiple of flat_align elements
+ * after tensor i-1 ends; the total is padded to flat_align too ([csdn] §3.2
+ * contiguous_gradients; [aiqz] 通信优化, grads packed into buckets).
+ * ------------------------------------------------------------------------- */
+
+/* offsets_out (host, num_tensors entries, may be NULL) receives each tensor's
+ * flat offset; *total_out the padded flat length. flat_align >= 1. */
+zds_status zds_flat_layout(const int64_t *numel, int32_t num_tensors, int32_t flat_align,
+                           int64_t *offsets_out, int64_t *total_out);
+
+/* Stage-1 shard of `rank` among `world` ranks ([csdn] §2.1 and §2.4: each rank
+ * keeps and updates only its part of the optimizer state): the flat buffer is
+ * padded to a multiple of world * flat_align and cut into `world` equal
+ * contiguous slices; [*lo, *hi) is rank's slice. */
+zds_status zds_shard_range(int64_t flat_total, int32_t world, int32_t rank, int32_t flat_align,
+                           int64_t *lo, int64_t *hi);
+
+/* The pieces of tensors that lie inside flat range [lo, hi): for entry e,
+ * out[4e..4e+3] = {tensor index, start inside the tensor, length, destination
+ * offset relative to lo}. out (host) holds room for max_entries entries;
+ * *count receives the number of entries (even when it exceeds max_entries,
+ * in which case ZDS_EINVAL is returned and out holds the first max_entries). */
+zds_status zds_shard_entries(const int64_t *numel, int32_t num_tensors, int32_t flat_align,
+                             int64_t lo, int64_t hi, int64_t *out, int32_t max_entries,
+                             int32_t *count);
+
+/* ---------------------------------------------------------------------------
+ * Gradient plan: the tensor table of one flat range, kept on the device so
+ * that one launch covers all tensors ([aiqz] 通信优化: a fixed cost per call
+ * dominates when there are hundreds of small grad tensors).
+ * ------------------------------------------------------------------------- */
+
+typedef struct zds_plan zds_plan;
+
+/* Builds the plan for flat range [lo, hi) of the layout of numel[0..T) with
+ * flat_align. Allocates the plan's device table and a small pinned staging
+ * ring for per-call source pointers on the current device. Not called on the
+ * hot path. */
+zds_status zds_plan_create(zds_plan **out, const int64_t *numel, int32_t num_tensors,
+                           int32_t flat_align, int64_t lo, int64_t hi);
+void zds_plan_destroy(zds_plan *plan);
+int32_t zds_plan_num_entries(const zds_plan *plan);
+/* Entry e as {tensor, start, length, dst_offset}; see zds_shard_entries. */
+zds_status zds_plan_entry(const zds_plan *plan, int32_t e, int64_t *out4);
+
+/* Row a1. One micro-batch's grads into the rank's flat buffer, one launch.
+ *   src_ptrs  host array of num_tensors device pointers; src_ptrs[t] points at
+ *             element 0 of tensor t (only tensors with plan entries are read;
+ *             others may be NULL). Element size alignment required.
+ *   src_dtype ZDS_FP16 / ZDS_BF16 (ZDS_FP32 allowed for the fp32 modes).
+ *   dst       device, hi - lo elements of dst_dtype: a 16-bit bucket of
+ *             src_dtype for ZDS_COPY, an fp32 accumulator otherwise.
+ *             Padding elements between tensors are never written.
+ * Definition: [csdn] §2.3, micro-batch grads summed in memory before one
+ * update; the fp32 add rounds to nearest even. The plan's pinned staging ring
+ * makes the call safe to repeat without waiting; a plan must not be used from
+ * two host threads at once. */
+zds_status zds_grad_accumulate(zds_plan *plan, const void *const *src_ptrs, zds_dtype src_dtype,
+                               void *dst, zds_dtype dst_dtype, zds_accum_mode mode, void *stream);
+
+/* Row a2. Size in bytes of the workspace zds_overflow_and_norm needs for n
+ * elements. */
+size_t zds_workspace_bytes(int64_t n);
+
+/* Row a2. Overflow flag and global L2 norm of n grads (device, dtype), and the
+ * clip/unscale factor for the step.
+ *   accum_steps K >= 1: the grads are the sum of K micro-batches; the step
+ *               uses their mean ([csdn] §2.3: the accumulated grad stands for
+ *               the big batch's grad).
+ *   max_norm    clip threshold; <= 0 disables clipping.
+ *   state_dev   device, supplies the loss scale S ([csdn] §2.2 loss scaling).
+ *   out_dev     device, receives zds_step_scalars.
+ *   ws, ws_bytes device workspace of at least zds_workspace_bytes(n).
+ * overflow = 1 iff some element is inf or NaN ([csdn] §2.2: overflow under the
+ * loss scale is detected). sumsq = sum of float64(x)^2 in a fixed order
+ * (run-to-run identical for the same n). norm, clip_coef and grad_scale are
+ * computed in float64 and rounded once to fp32. */
+zds_status zds_overflow_and_norm(const void *grads, zds_dtype dtype, int64_t n,
+                                 int32_t accum_steps, float max_norm,
+                                 const zds_step_state *state_dev, zds_step_scalars *out_dev,
+                                 void *ws, size_t ws_bytes, void *stream);
+
+/* Row a4. Fused AdamW on the fp32 master shard with unscale/clip and the cast
+ * back to 16 bits ([csdn] §2.2 and [aiqz] 混合精度: the update runs on the
+ * fp32 master copy; [csdn] §3.2 AdamW; [aiqz] Python 演示: the moment
+ * recurrences). Per element, in fp32 with one rounding per operation:
+ *   g = x * grad_scale; m = b1*m + (1-b1)*g; v = b2*v + (1-b2)*(g*g);
+ *   denom = sqrt(v)/sqrt(1-b2^t) + eps; p = p*(1-lr*wd);
+ *   p = p - (lr/(1-b1^t))*(m/denom); params_out = round_nearest_even(p)
+ * with t = state.t + 1 and the step scalars derived in float64, each rounded
+ * once to fp32. If scalars_dev->overflow is set every element is left
+ * untouched (the step is skipped on the device; no host sync).
+ *   grads       device, n elements of grad_dtype (16-bit, or the fp32 accumulator)
+ *   master, exp_avg, exp_avg_sq   device fp32, n elements, updated in place
+ *   params_out  device, n elements of param_dtype (FP16/BF16), write-only;
+ *               NULL skips the cast.
+ * The state is read, not advanced: zds_loss_scaler_update commits t. */
+zds_status zds_adam_step(const zds_adamw_hparams *hp, const void *grads, zds_dtype grad_dtype,
+                         float *master, float *exp_avg, float *exp_avg_sq, void *params_out,
+                         zds_dtype param_dtype, int64_t n, const zds_step_scalars *scalars_dev,
+                         const zds_step_state *state_dev, void *stream);
+
+/* Row a3. Initialise the device step state from cfg with Adam step count t0
+ * and powers beta1^t0, beta2^t0 (1, 1 for a fresh optimizer). */
+zds_status zds_step_state_init(zds_step_state *state_dev, const zds_scaler_config *cfg, int64_t t0,
+                               double beta1_pow0, double beta2_pow0, void *stream);
+
+/* Row a3. Advance the state after a step ([csdn] §2.2: lower the scale on
+ * overflow, raise it once stable; [csdn] §3.2 fp16 fields; [aidhplus] dynamic
+ * loss scaling). Dynamic mode, with the flag from scalars_dev:
+ *   overflow: skip; good_steps = 0; if hyst_left <= 1 the scale halves (not
+ *             below min_scale) and hyst_left = hysteresis, else hyst_left -= 1.
+ *   clean:    t += 1; beta powers *= (double)beta (fp32 hp values);
+ *             hyst_left = hysteresis; good_steps += 1 and when it reaches
+ *             window the scale doubles and good_steps = 0.
+ * Static mode: the scale never changes; an overflow still skips the step. */
+zds_status zds_loss_scaler_update(zds_step_state *state_dev, const zds_step_scalars *scalars_dev,
+                                  const zds_adamw_hparams *hp, void *stream);
+
+/* Host twins of the two state functions above, on a host struct; the same
+ * code as the device path. */
+zds_status zds_step_state_init_host(zds_step_state *state, const zds_scaler_config *cfg,
+                                    int64_t t0, double beta1_pow0, double beta2_pow0);
+zds_status zds_loss_scaler_update_host(zds_step_state *state, uint32_t overflow,
+                                       const zds_adamw_hparams *hp);
+
+/* The fp32 step constants zds_adam_step derives for the step after `state`:
+ * out5 (host) = {step_size, bc2_sqrt, decay, 1-beta1, 1-beta2}. Host code path
+ * shared with the kernel. */
+zds_status zds_adam_constants_host(const zds_adamw_hparams *hp, const zds_step_state *state,
+                                   float *out5);
+
+/* Clip arithmetic of zds_overflow_and_norm on the host: from sumsq, S, K and
+ * max_norm fill out (overflow, norm, clip_coef, grad_scale, scale_used). */
+zds_status zds_clip_scalars_host(double sumsq, float scale, int32_t accum_steps, float max_norm,
+                                 zds_step_scalars *out);
+
+const char *zds_last_error(void);
+const char *zds_status_string(zds_status status);
+int32_t zds_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ZDS_H */

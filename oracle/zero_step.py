@@ -246,7 +246,9 @@ def overflow_and_norm(x, dtype, scale, accum_steps, max_norm):
 # Readings: factor 2 both ways; grow after `window` consecutive clean steps;
 # halve when `hysteresis` overflows have come in a row (clean steps reset the
 # count); never below min_scale; an overflow always skips the step, which
-# leaves the Adam step counter and beta powers untouched.
+# leaves the Adam step counter and beta powers untouched. The scale is kept as
+# an fp32 power of two, so growth stops at 2^127 (no cap is stated; this only
+# keeps it finite).
 # ---------------------------------------------------------------------------
 
 @dataclass(frozen=True)
@@ -290,7 +292,9 @@ def scaler_update(st, overflow, beta1, beta2):
         return st
     good = st.good_steps + 1
     if good == st.window:
-        return replace(st, scale=st.scale * 2.0, good_steps=0, hyst_left=st.hysteresis)
+        # the scale is an fp32 power of two: it saturates at 2^127
+        return replace(st, scale=min(st.scale * 2.0, 2.0 ** 127), good_steps=0,
+                       hyst_left=st.hysteresis)
     return replace(st, good_steps=good, hyst_left=st.hysteresis)
 
 

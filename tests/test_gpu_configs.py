@@ -1,0 +1,220 @@
+"""Whole-step GPU runs of the workload shapes against the free-running oracle:
+the tiny 64-tensor shard over 5 steps with an overflow at step 3, gradient
+accumulation over 16 micro-batches, a 1,024-tensor table over 20 steps with a
+seeded overflow schedule, and a bf16 Stage-1 shard with prior moments. The
+large shapes run at reduced size here; full-size runs are in
+test_gpu_fullsize.py."""
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from tests.util import assert_p16_close, assert_state_close, to_dev, to_host
+from workloads import draw_grads, draw_master, draw_prior_moments, tiny_shard_sizes
+
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():
+    pytest.skip("no GPU", allow_module_level=True)
+
+from zero_sharded_mixed_tensor_amd import zds  # noqa: E402
+from zero_sharded_mixed_tensor_amd.step import ShardStep  # noqa: E402
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def _flat_master(numels, align, seed, cfg):
+    offs, total = O.flat_layout(numels, align)
+    full = draw_master(total, 0.02, seed, cfg)
+    master = np.zeros(total, np.float32)
+    for o, n in zip(offs, numels):
+        master[o:o + n] = full[o:o + n]
+    return offs, total, master
+
+
+def _compare(tag, got, want_state, want_sc, osc, ost, st):
+    P, M, V, OUT = got
+    oP, oM, oV, oOUT = want_state
+    assert st.last_skip == ost.last_skip and st.t == ost.t, tag
+    assert st.scale == np.float32(ost.scale), tag
+    assert want_sc.overflow == osc["overflow"], tag
+    if not osc["overflow"]:
+        assert want_sc.grad_scale == osc["grad_scale"], tag
+        assert abs(float(want_sc.norm) - float(osc["norm"])) <= 1e-6 * float(osc["norm"]), tag
+    assert_state_close(tag + " master", P, oP, 2)
+    assert_state_close(tag + " exp_avg", M, oM, 2)
+    assert_state_close(tag + " exp_avg_sq", V, oV, 2)
+    if OUT is not None and oOUT is not None:
+        assert_p16_close(tag + " params", OUT, oOUT, 1)
+
+
+@pytest.mark.parametrize("inf_at", ["seeded", "first", "last"])
+def test_tiny_shard_five_steps(inf_at):
+    """64 tensors (log-uniform sizes, seed 0), fp16 grads N(0, 1e-3) x scale,
+    AdamW lr 1e-3, clip 1.0, dynamic scale from 2^16 with hysteresis 1; +inf
+    in step 3's grads skips that step and halves the scale."""
+    say("tiny shard 5 steps, inf at", inf_at)
+    numels = [n for _, n in tiny_shard_sizes()]
+    offs, total, master = _flat_master(numels, 64, 0, 1)
+    hp = O.AdamW()
+    plan = zds.zds_plan_create(numels, 64, 0, total)
+    ent = O.shard_entries(numels, 64, 0, total)
+    st = ShardStep(total, zds.hparams(), zds.scaler_config(initial_scale_power=16, window=1000,
+                                                          hysteresis=1), max_norm=1.0)
+    dP = to_dev(master, "fp32")
+    dM = torch.zeros(total, dtype=torch.float32, device="cuda")
+    dV = torch.zeros(total, dtype=torch.float32, device="cuda")
+    dOUT = to_dev(O.narrow(master, "fp16"), "fp16")
+    bucket = torch.zeros(total, dtype=torch.float16, device="cuda")
+    oP, oM, oV = master.copy(), np.zeros(total, np.float32), np.zeros(total, np.float32)
+    oOUT = O.narrow(master, "fp16")
+    ost = O.scaler_init(initial_scale_power=16, window=1000, hysteresis=1)
+    scales, applied = [], []
+    for k in range(1, 6):
+        S = ost.scale
+        scales.append(S)
+        srcs = [draw_grads(n, "fp16", 1e-3, S, 0, 1, k, offset=o) for o, n in zip(offs, numels)]
+        if k == 3:
+            t = {"seeded": int(np.random.default_rng(3).integers(0, 64)), "first": 0, "last": 63}[inf_at]
+            pos = {"seeded": int(np.random.default_rng(4).integers(0, numels[t])), "first": 0,
+                   "last": numels[63] - 1}[inf_at]
+            srcs[t][pos] = 0x7C00
+        zds.zds_grad_accumulate(plan, [to_dev(s, "fp16") for s in srcs], bucket, zds.ZDS_COPY)
+        st.step(bucket, dP, dM, dV, dOUT)
+        torch.cuda.synchronize()
+        flat = O.flatten_copy(srcs, ent, np.zeros(total, np.uint16))
+        assert (to_host(bucket) == flat).all()
+        oP, oM, oV, out16, ost, osc = O.optimizer_step(flat, "fp16", oP, oM, oV, ost, hp, 1.0, 1, "fp16")
+        if out16 is not None:
+            oOUT = out16
+        applied.append(None if ost.last_skip else ost.t)
+        _compare("step %d" % k, (to_host(dP), to_host(dM), to_host(dV), to_host(dOUT)),
+                 (oP, oM, oV, oOUT), st.read_scalars(), osc, ost, st.read_state())
+    assert scales == [2.0 ** 16] * 3 + [2.0 ** 15] * 2
+    assert applied == [1, 2, None, 3, 4]
+    plan.close()
+
+
+def test_gradient_accumulation_sixteen_microbatches():
+    """16 micro-batches of fp16 grads N(0, 1e-3) x 2^14 accumulated in fp32,
+    then overflow check, clip at 1.0 and AdamW (t = 2, prior moments), on a
+    reduced Stage-1 shard of 10 tensors."""
+    say("accumulation K=16")
+    rng = np.random.default_rng(21)
+    numels = [int(x) for x in rng.integers(1000, 60000, 10)]
+    _, total = O.flat_layout(numels, 64)
+    lo, hi = O.shard_range(total, 3, 1, 64)
+    ent = O.shard_entries(numels, 64, lo, hi)
+    L = hi - lo
+    plan = zds.zds_plan_create(numels, 64, lo, hi)
+    offs, _ = O.flat_layout(numels, 64)
+    acc = torch.empty(L, dtype=torch.float32, device="cuda")
+    wacc = np.zeros(L, np.float32)
+    for k in range(16):
+        srcs = [draw_grads(n, "fp16", 1e-3, 2.0 ** 14, 2, 3, k, offset=o) for o, n in zip(offs, numels)]
+        zds.zds_grad_accumulate(plan, [to_dev(s, "fp16") for s in srcs], acc,
+                                zds.ZDS_OVERWRITE if k == 0 else zds.ZDS_ACCUMULATE)
+        O.flatten_accumulate(srcs, "fp16", ent, wacc, overwrite=(k == 0))
+    # padding inside the range is never written by the accumulate: zero it as
+    # the caller must (the oracle's buffer starts at zero)
+    pad = np.ones(L, bool)
+    for t, s, n, d in ent:
+        pad[d:d + n] = False
+    acc[torch.from_numpy(pad).cuda()] = 0.0
+    master = draw_master(L, 0.02, 2, 3)
+    m, v = draw_prior_moments(L, 1e-3, 2, 3)
+    master[pad] = 0
+    m[pad] = 0
+    v[pad] = 0
+    b1, b2 = float(np.float32(0.9)), float(np.float32(0.999))
+    st = ShardStep(L, zds.hparams(), zds.scaler_config(initial_scale_power=14), max_norm=1.0,
+                   accum_steps=16, t0=1, beta1_pow0=b1, beta2_pow0=b2)
+    dP, dM, dV = to_dev(master, "fp32"), to_dev(m, "fp32"), to_dev(v, "fp32")
+    dOUT = torch.zeros(L, dtype=torch.float16, device="cuda")
+    st.step(acc, dP, dM, dV, dOUT)
+    torch.cuda.synchronize()
+    assert (to_host(acc).view(np.uint32) == wacc.view(np.uint32)).all()
+    ost = O.scaler_init(initial_scale_power=14, t=1, beta1_pow=b1, beta2_pow=b2)
+    oP, oM, oV, oOUT, ost, osc = O.optimizer_step(wacc, "fp32", master, m, v, ost, O.AdamW(), 1.0, 16, "fp16")
+    assert osc["coef"] < 1.0  # the clip is active
+    _compare("accum", (to_host(dP), to_host(dM), to_host(dV), to_host(dOUT)), (oP, oM, oV, oOUT),
+             st.read_scalars(), osc, ost, st.read_state())
+    plan.close()
+
+
+def test_thousand_tensor_table_twenty_steps():
+    """1,024 tensors (reduced sizes, norms-like 4096-element pieces among
+    them), fp16 grads, copy into a flat bucket, 20 steps with a seeded
+    overflow schedule: Bernoulli(0.001) per step plus one forced overflow at a
+    seeded step in [2, 19], inf and NaN alternately."""
+    say("1024-tensor table, 20 steps")
+    rng = np.random.default_rng(1024)
+    numels = [4096 if i % 15 == 14 else int(rng.integers(64, 3000)) for i in range(1024)]
+    offs, total, master = _flat_master(numels, 64, 4, 4)
+    plan = zds.zds_plan_create(numels, 64, 0, total)
+    assert plan.num_entries == 1024
+    ent = O.shard_entries(numels, 64, 0, total)
+    sched = np.random.default_rng(17)
+    forced = int(sched.integers(2, 20))
+    over = [(k == forced) or (sched.random() < 0.001) for k in range(1, 21)]
+    st = ShardStep(total, zds.hparams(), zds.scaler_config(initial_scale_power=16, window=1000), max_norm=1.0)
+    dP = to_dev(master, "fp32")
+    dM = torch.zeros(total, dtype=torch.float32, device="cuda")
+    dV = torch.zeros(total, dtype=torch.float32, device="cuda")
+    dOUT = torch.zeros(total, dtype=torch.float16, device="cuda")
+    bucket = torch.zeros(total, dtype=torch.float16, device="cuda")
+    oP, oM, oV = master.copy(), np.zeros(total, np.float32), np.zeros(total, np.float32)
+    oOUT = np.zeros(total, np.uint16)
+    ost = O.scaler_init(initial_scale_power=16, window=1000)
+    nov = 0
+    traj = []
+    for k in range(1, 21):
+        srcs = [draw_grads(n, "fp16", 1e-3, ost.scale, 4, 4, k, offset=o) for o, n in zip(offs, numels)]
+        if over[k - 1]:
+            t = int(sched.integers(0, 1024))
+            srcs[t][int(sched.integers(0, numels[t]))] = 0x7C00 if nov % 2 == 0 else 0x7E00
+            nov += 1
+        zds.zds_grad_accumulate(plan, [to_dev(s, "fp16") for s in srcs], bucket, zds.ZDS_COPY)
+        st.step(bucket, dP, dM, dV, dOUT)
+        flat = O.flatten_copy(srcs, ent, np.zeros(total, np.uint16))
+        oP, oM, oV, out16, ost, osc = O.optimizer_step(flat, "fp16", oP, oM, oV, ost, O.AdamW(), 1.0, 1, "fp16")
+        if out16 is not None:
+            oOUT = out16
+        torch.cuda.synchronize()
+        gst = st.read_state()
+        traj.append(gst.scale)
+        _compare("step %d" % k, (to_host(dP), to_host(dM), to_host(dV), to_host(dOUT)),
+                 (oP, oM, oV, oOUT), st.read_scalars(), osc, ost, gst)
+    assert min(traj) < 2.0 ** 16  # the trajectory contains a halving
+    plan.close()
+
+
+def test_bf16_stage1_shard_prior_moments():
+    """Reduced Llama-like shard: bf16 grads N(0, 2e-3), static scale 1, clip
+    1.0, m and v from a prior step (t = 1 -> 2), bf16 params out."""
+    say("bf16 stage-1 shard, one step")
+    numels = [4096 * 40, 4096 * 12, 4096 * 12, 4096, 4096 * 30, 4096 * 30]
+    _, total = O.flat_layout(numels, 64)
+    lo, hi = O.shard_range(total, 8, 5, 64)
+    L = hi - lo
+    g = draw_grads(L, "bf16", 2e-3, 1.0, 6, 2, 0)
+    master = draw_master(L, 0.02, 6, 2)
+    m, v = draw_prior_moments(L, 2e-3, 6, 2)
+    b1, b2 = float(np.float32(0.9)), float(np.float32(0.999))
+    st = ShardStep(L, zds.hparams(), zds.scaler_config(dynamic=False, static_scale=1.0), max_norm=1.0,
+                   t0=1, beta1_pow0=b1, beta2_pow0=b2)
+    dP, dM, dV = to_dev(master, "fp32"), to_dev(m, "fp32"), to_dev(v, "fp32")
+    dOUT = torch.zeros(L, dtype=torch.bfloat16, device="cuda")
+    st.step(to_dev(g, "bf16"), dP, dM, dV, dOUT)
+    torch.cuda.synchronize()
+    ost = O.scaler_init(dynamic=False, static_scale=1.0, t=1, beta1_pow=b1, beta2_pow=b2)
+    oP, oM, oV, oOUT, ost, osc = O.optimizer_step(g, "bf16", master, m, v, ost, O.AdamW(), 1.0, 1, "bf16")
+    assert osc["coef"] < 1.0
+    _compare("bf16 shard", (to_host(dP), to_host(dM), to_host(dV), to_host(dOUT)), (oP, oM, oV, oOUT),
+             st.read_scalars(), osc, ost, st.read_state())

@@ -1,0 +1,129 @@
+// Row a1: multi-tensor flatten / accumulate into the rank's flat buffer.
+//
+// Backward produces many small gradient tensors; packing them into one
+// contiguous bucket (devpress.csdn.net DeepSpeed tutorial §3.2,
+// contiguous_gradients; aiqz.cc "DeepSpeed ZeRO引擎深入", 通信优化) and summing
+// micro-batches in memory before a single update (same tutorial §2.3) are done
+// here in one launch over the plan's device-side tensor table.
+//
+// Work is cut into chunks of kAccumChunk elements that never straddle two
+// table entries; chunk c belongs to the entry e with chunk0[e] <= c <
+// chunk0[e+1], found by a binary search on uniform (scalar) loads. Inside a
+// chunk each thread moves groups of 8 elements with 16-byte accesses when the
+// source and destination of the entry are 16-byte aligned, else element by
+// element. Bytes per element: copy 2+2, overwrite 2+4, accumulate 2+4+4.
+#include "zds_device.h"
+#include "zds_internal.h"
+
+#ifndef ZDS_ACC_BLOCK
+#define ZDS_ACC_BLOCK 256
+#endif
+#ifndef ZDS_ACC_WAVES_PER_CU
+#define ZDS_ACC_WAVES_PER_CU 32
+#endif
+
+namespace zds {
+
+struct AccArgs {
+  const int64_t *table;
+  int32_t num_entries;
+  int64_t total_chunks;
+  const void *const *ptrs;
+  void *dst;
+};
+
+__device__ __forceinline__ int find_entry(const int64_t *chunk0, int32_t E, int64_t c) {
+  int lo = 0, hi = E;  // chunk0[lo] <= c < chunk0[hi]
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (chunk0[mid] <= c) lo = mid; else hi = mid;
+  }
+  return lo;
+}
+
+// MODE: ZDS_COPY (16-bit -> same 16-bit), ZDS_OVERWRITE / ZDS_ACCUMULATE
+// (SD -> fp32).
+template <int SD, int MODE>
+__global__ void __launch_bounds__(ZDS_ACC_BLOCK) accumulate_kernel(AccArgs a) {
+  const int32_t E = a.num_entries;
+  const int64_t *start = a.table;
+  const int64_t *len = a.table + E;
+  const int64_t *dsto = a.table + 2 * E;
+  const int64_t *chunk0 = a.table + 3 * E;
+  for (int64_t c = blockIdx.x; c < a.total_chunks; c += gridDim.x) {
+    const int e = find_entry(chunk0, E, c);
+    const int64_t local = (c - chunk0[e]) * kAccumChunk;
+    const int64_t rem = len[e] - local;
+    const int64_t cnt = rem < kAccumChunk ? rem : kAccumChunk;
+    const char *src = static_cast<const char *>(a.ptrs[e]) + (start[e] + local) * (SD == ZDS_FP32 ? 4 : 2);
+    const int64_t d0 = dsto[e] + local;
+    if (MODE == ZDS_COPY) {
+      uint16_t *dst = static_cast<uint16_t *>(a.dst) + d0;
+      const uint16_t *s = reinterpret_cast<const uint16_t *>(src);
+      if (aligned(s, 16) && aligned(dst, 16)) {
+        const int64_t groups = cnt >> 3;
+        for (int64_t i = threadIdx.x; i < groups; i += ZDS_ACC_BLOCK)
+          st_stream(reinterpret_cast<u32x4 *>(dst) + i, ld_stream(reinterpret_cast<const u32x4 *>(s) + i));
+        for (int64_t j = (groups << 3) + threadIdx.x; j < cnt; j += ZDS_ACC_BLOCK) dst[j] = s[j];
+      } else {
+        for (int64_t j = threadIdx.x; j < cnt; j += ZDS_ACC_BLOCK) dst[j] = s[j];
+      }
+    } else {
+      float *dst = static_cast<float *>(a.dst) + d0;
+      if (aligned(src, 16) && aligned(dst, 16)) {
+        const int64_t groups = cnt >> 3;
+        for (int64_t i = threadIdx.x; i < groups; i += ZDS_ACC_BLOCK) {
+          float x[8];
+          load8<SD>(src, i, x);
+          if (MODE == ZDS_ACCUMULATE) {
+            float y[8];
+            load8f(dst, i, y);
+#pragma unroll
+            for (int k = 0; k < 8; ++k) x[k] = y[k] + x[k];
+          }
+          store8f(dst, i, x);
+        }
+        for (int64_t j = (groups << 3) + threadIdx.x; j < cnt; j += ZDS_ACC_BLOCK) {
+          const float x = widen1<SD>(src, j);
+          dst[j] = MODE == ZDS_ACCUMULATE ? dst[j] + x : x;
+        }
+      } else {
+        for (int64_t j = threadIdx.x; j < cnt; j += ZDS_ACC_BLOCK) {
+          const float x = widen1<SD>(src, j);
+          dst[j] = MODE == ZDS_ACCUMULATE ? dst[j] + x : x;
+        }
+      }
+    }
+  }
+}
+
+template <int SD, int MODE>
+static void go(int grid, hipStream_t s, const AccArgs &a) {
+  hipLaunchKernelGGL((accumulate_kernel<SD, MODE>), dim3(grid), dim3(ZDS_ACC_BLOCK), 0, s, a);
+}
+
+zds_status launch_accumulate(const PlanDev &p, const void *const *dev_ptrs, zds_dtype src,
+                             void *dst, zds_dtype /*dst_dtype*/, zds_accum_mode mode,
+                             hipStream_t stream) {
+  if (p.num_entries == 0 || p.total_chunks == 0) return ZDS_OK;
+  AccArgs a{p.table, p.num_entries, p.total_chunks, dev_ptrs, dst};
+  int64_t grid = static_cast<int64_t>(device_cu_count()) * ZDS_ACC_WAVES_PER_CU * 64 / ZDS_ACC_BLOCK;
+  if (grid > p.total_chunks) grid = p.total_chunks;
+  if (grid < 1) grid = 1;
+  const int g = static_cast<int>(grid);
+  if (mode == ZDS_COPY) {
+    // fp16 and bf16 copies move the same bits
+    go<ZDS_FP16, ZDS_COPY>(g, stream, a);
+  } else if (mode == ZDS_OVERWRITE) {
+    if (src == ZDS_FP16) go<ZDS_FP16, ZDS_OVERWRITE>(g, stream, a);
+    else if (src == ZDS_BF16) go<ZDS_BF16, ZDS_OVERWRITE>(g, stream, a);
+    else go<ZDS_FP32, ZDS_OVERWRITE>(g, stream, a);
+  } else {
+    if (src == ZDS_FP16) go<ZDS_FP16, ZDS_ACCUMULATE>(g, stream, a);
+    else if (src == ZDS_BF16) go<ZDS_BF16, ZDS_ACCUMULATE>(g, stream, a);
+    else go<ZDS_FP32, ZDS_ACCUMULATE>(g, stream, a);
+  }
+  return check_launch("grad_accumulate kernel");
+}
+
+}  // namespace zds

@@ -1,0 +1,424 @@
+// The extern "C" boundary: argument checks, plans, host-only geometry and
+// the host twins of the scalar logic. Kernels live in the other files.
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "zds_internal.h"
+
+namespace zds {
+
+static thread_local std::string g_err;
+
+void clear_error() { g_err.clear(); }
+
+zds_status fail(zds_status s, const char *fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return s;
+}
+
+zds_status hip_fail(hipError_t e, const char *what) {
+  return fail(ZDS_EHIP, "%s: %s (%d)", what, hipGetErrorString(e), static_cast<int>(e));
+}
+
+zds_status check_launch(const char *what) {
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return hip_fail(e, what);
+  return ZDS_OK;
+}
+
+int device_cu_count() {
+  static std::mutex mu;
+  static std::vector<int> cache;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  std::lock_guard<std::mutex> lock(mu);
+  if (static_cast<int>(cache.size()) <= dev) cache.resize(dev + 1, 0);
+  if (cache[dev] == 0) {
+    int cu = 0;
+    if (hipDeviceGetAttribute(&cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cu <= 0)
+      cu = 256;
+    cache[dev] = cu;
+  }
+  return cache[dev];
+}
+
+}  // namespace zds
+
+using namespace zds;
+
+// ---------------------------------------------------------------------------
+// Geometry (host only)
+// ---------------------------------------------------------------------------
+
+static int64_t align_up(int64_t x, int64_t a) { return ((x + a - 1) / a) * a; }
+
+extern "C" zds_status zds_flat_layout(const int64_t *numel, int32_t num_tensors, int32_t flat_align,
+                                      int64_t *offsets_out, int64_t *total_out) {
+  clear_error();
+  if (num_tensors < 0 || (num_tensors > 0 && !numel) || !total_out)
+    return fail(ZDS_EINVAL, "zds_flat_layout: null pointer or negative tensor count");
+  if (flat_align < 1) return fail(ZDS_EINVAL, "zds_flat_layout: flat_align must be >= 1");
+  int64_t pos = 0;
+  for (int32_t i = 0; i < num_tensors; ++i) {
+    if (numel[i] < 0) return fail(ZDS_EINVAL, "zds_flat_layout: numel[%d] < 0", i);
+    if (offsets_out) offsets_out[i] = pos;
+    pos = align_up(pos + numel[i], flat_align);
+  }
+  *total_out = pos;
+  return ZDS_OK;
+}
+
+extern "C" zds_status zds_shard_range(int64_t flat_total, int32_t world, int32_t rank,
+                                      int32_t flat_align, int64_t *lo, int64_t *hi) {
+  clear_error();
+  if (!lo || !hi) return fail(ZDS_EINVAL, "zds_shard_range: null output");
+  if (world < 1 || rank < 0 || rank >= world || flat_align < 1 || flat_total < 0)
+    return fail(ZDS_EINVAL, "zds_shard_range: need world >= 1, 0 <= rank < world, flat_align >= 1");
+  const int64_t padded = align_up(flat_total, static_cast<int64_t>(world) * flat_align);
+  const int64_t per = padded / world;
+  *lo = per * rank;
+  *hi = per * (rank + 1);
+  return ZDS_OK;
+}
+
+static zds_status compute_entries(const int64_t *numel, int32_t T, int32_t align, int64_t lo,
+                                  int64_t hi, std::vector<int64_t> &out) {
+  if (T < 0 || (T > 0 && !numel)) return fail(ZDS_EINVAL, "tensor table: null numel or T < 0");
+  if (align < 1) return fail(ZDS_EINVAL, "tensor table: flat_align must be >= 1");
+  if (lo < 0 || hi < lo) return fail(ZDS_EINVAL, "tensor table: need 0 <= lo <= hi");
+  out.clear();
+  int64_t pos = 0;
+  for (int32_t t = 0; t < T; ++t) {
+    if (numel[t] < 0) return fail(ZDS_EINVAL, "tensor table: numel[%d] < 0", t);
+    const int64_t a = pos > lo ? pos : lo;
+    const int64_t end = pos + numel[t];
+    const int64_t b = end < hi ? end : hi;
+    if (a < b) {
+      out.push_back(t);
+      out.push_back(a - pos);
+      out.push_back(b - a);
+      out.push_back(a - lo);
+    }
+    pos = align_up(end, align);
+  }
+  return ZDS_OK;
+}
+
+extern "C" zds_status zds_shard_entries(const int64_t *numel, int32_t num_tensors, int32_t flat_align,
+                                        int64_t lo, int64_t hi, int64_t *out, int32_t max_entries,
+                                        int32_t *count) {
+  clear_error();
+  if (!count || (max_entries > 0 && !out) || max_entries < 0)
+    return fail(ZDS_EINVAL, "zds_shard_entries: null output or negative max_entries");
+  std::vector<int64_t> e;
+  zds_status s = compute_entries(numel, num_tensors, flat_align, lo, hi, e);
+  if (s != ZDS_OK) return s;
+  const int32_t n = static_cast<int32_t>(e.size() / 4);
+  *count = n;
+  const int32_t k = n < max_entries ? n : max_entries;
+  if (k > 0) memcpy(out, e.data(), sizeof(int64_t) * 4 * k);
+  if (n > max_entries) return fail(ZDS_EINVAL, "zds_shard_entries: %d entries, room for %d", n, max_entries);
+  return ZDS_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Plans
+// ---------------------------------------------------------------------------
+
+static constexpr int kRing = 8;
+
+struct zds_plan {
+  int device = 0;
+  int32_t num_tensors = 0;
+  int32_t num_entries = 0;
+  std::vector<int64_t> entries;  // 4 per entry
+  int64_t total_chunks = 0;
+  int64_t *d_table = nullptr;
+  const void **d_ptrs = nullptr;  // kRing * E
+  const void **h_ptrs = nullptr;  // pinned, kRing * E
+  hipEvent_t ev[kRing] = {};
+  bool used[kRing] = {};
+  uint32_t next = 0;
+};
+
+static void plan_free(zds_plan *p) {
+  if (!p) return;
+  for (int i = 0; i < kRing; ++i)
+    if (p->ev[i]) (void)hipEventDestroy(p->ev[i]);
+  if (p->d_table) (void)hipFree(p->d_table);
+  if (p->d_ptrs) (void)hipFree(p->d_ptrs);
+  if (p->h_ptrs) (void)hipHostFree(p->h_ptrs);
+  delete p;
+}
+
+extern "C" zds_status zds_plan_create(zds_plan **out, const int64_t *numel, int32_t num_tensors,
+                                      int32_t flat_align, int64_t lo, int64_t hi) {
+  clear_error();
+  if (!out) return fail(ZDS_EINVAL, "zds_plan_create: null out");
+  *out = nullptr;
+  std::vector<int64_t> e;
+  zds_status s = compute_entries(numel, num_tensors, flat_align, lo, hi, e);
+  if (s != ZDS_OK) return s;
+  zds_plan *p = new (std::nothrow) zds_plan;
+  if (!p) return fail(ZDS_ENOMEM, "zds_plan_create: host allocation failed");
+  p->num_tensors = num_tensors;
+  p->entries = e;
+  const int32_t E = static_cast<int32_t>(e.size() / 4);
+  p->num_entries = E;
+  hipError_t he = hipGetDevice(&p->device);
+  if (he != hipSuccess) { plan_free(p); return hip_fail(he, "zds_plan_create: hipGetDevice"); }
+  std::vector<int64_t> table(3 * static_cast<size_t>(E) + E + 1);
+  int64_t chunks = 0;
+  for (int32_t i = 0; i < E; ++i) {
+    table[i] = e[4 * i + 1];
+    table[E + i] = e[4 * i + 2];
+    table[2 * E + i] = e[4 * i + 3];
+    table[3 * E + i] = chunks;
+    chunks += (e[4 * i + 2] + kAccumChunk - 1) / kAccumChunk;
+  }
+  table[4 * E] = chunks;
+  p->total_chunks = chunks;
+  const size_t tb = table.size() * sizeof(int64_t);
+  he = hipMalloc(reinterpret_cast<void **>(&p->d_table), tb);
+  if (he != hipSuccess) { plan_free(p); return fail(ZDS_ENOMEM, "zds_plan_create: hipMalloc table: %s", hipGetErrorString(he)); }
+  he = hipMemcpy(p->d_table, table.data(), tb, hipMemcpyHostToDevice);
+  if (he != hipSuccess) { plan_free(p); return hip_fail(he, "zds_plan_create: table upload"); }
+  const size_t pb = sizeof(void *) * kRing * (E > 0 ? E : 1);
+  he = hipMalloc(reinterpret_cast<void **>(&p->d_ptrs), pb);
+  if (he != hipSuccess) { plan_free(p); return fail(ZDS_ENOMEM, "zds_plan_create: hipMalloc ptrs: %s", hipGetErrorString(he)); }
+  he = hipHostMalloc(reinterpret_cast<void **>(&p->h_ptrs), pb, hipHostMallocDefault);
+  if (he != hipSuccess) { plan_free(p); return fail(ZDS_ENOMEM, "zds_plan_create: hipHostMalloc: %s", hipGetErrorString(he)); }
+  for (int i = 0; i < kRing; ++i) {
+    he = hipEventCreateWithFlags(&p->ev[i], hipEventDisableTiming);
+    if (he != hipSuccess) { plan_free(p); return hip_fail(he, "zds_plan_create: hipEventCreate"); }
+  }
+  *out = p;
+  return ZDS_OK;
+}
+
+extern "C" void zds_plan_destroy(zds_plan *plan) {
+  if (!plan) return;
+  for (int i = 0; i < kRing; ++i)
+    if (plan->used[i]) (void)hipEventSynchronize(plan->ev[i]);
+  plan_free(plan);
+}
+
+extern "C" int32_t zds_plan_num_entries(const zds_plan *plan) { return plan ? plan->num_entries : -1; }
+
+extern "C" zds_status zds_plan_entry(const zds_plan *plan, int32_t e, int64_t *out4) {
+  clear_error();
+  if (!plan || !out4) return fail(ZDS_EINVAL, "zds_plan_entry: null argument");
+  if (e < 0 || e >= plan->num_entries) return fail(ZDS_EINVAL, "zds_plan_entry: entry %d out of range", e);
+  memcpy(out4, &plan->entries[4 * static_cast<size_t>(e)], 4 * sizeof(int64_t));
+  return ZDS_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Hot calls
+// ---------------------------------------------------------------------------
+
+extern "C" zds_status zds_grad_accumulate(zds_plan *plan, const void *const *src_ptrs,
+                                          zds_dtype src_dtype, void *dst, zds_dtype dst_dtype,
+                                          zds_accum_mode mode, void *stream) {
+  clear_error();
+  if (!plan) return fail(ZDS_EINVAL, "zds_grad_accumulate: null plan");
+  if (!valid_dtype(src_dtype) || !valid_dtype(dst_dtype))
+    return fail(ZDS_EINVAL, "zds_grad_accumulate: bad dtype");
+  if (mode == ZDS_COPY) {
+    if (src_dtype == ZDS_FP32 || dst_dtype != src_dtype)
+      return fail(ZDS_EINVAL, "zds_grad_accumulate: copy mode needs the same 16-bit dtype on both sides");
+  } else if (mode == ZDS_OVERWRITE || mode == ZDS_ACCUMULATE) {
+    if (dst_dtype != ZDS_FP32) return fail(ZDS_EINVAL, "zds_grad_accumulate: accumulator must be fp32");
+  } else {
+    return fail(ZDS_EINVAL, "zds_grad_accumulate: bad mode %d", static_cast<int>(mode));
+  }
+  const int32_t E = plan->num_entries;
+  if (E == 0) return ZDS_OK;
+  if (!src_ptrs || !dst) return fail(ZDS_EINVAL, "zds_grad_accumulate: null src_ptrs or dst");
+  const uintptr_t es = static_cast<uintptr_t>(dtype_size(src_dtype));
+  if (!aligned(dst, static_cast<uintptr_t>(dtype_size(dst_dtype))))
+    return fail(ZDS_EALIGN, "zds_grad_accumulate: dst not aligned to its element size");
+  int dev = 0;
+  hipError_t he = hipGetDevice(&dev);
+  if (he != hipSuccess) return hip_fail(he, "zds_grad_accumulate: hipGetDevice");
+  if (dev != plan->device) return fail(ZDS_EINVAL, "zds_grad_accumulate: plan belongs to device %d, current is %d", plan->device, dev);
+  for (int32_t i = 0; i < E; ++i) {
+    const int64_t t = plan->entries[4 * static_cast<size_t>(i)];
+    const void *sp = src_ptrs[t];
+    if (!sp) return fail(ZDS_EINVAL, "zds_grad_accumulate: src_ptrs[%lld] is null", static_cast<long long>(t));
+    if (!aligned(sp, es)) return fail(ZDS_EALIGN, "zds_grad_accumulate: src_ptrs[%lld] misaligned", static_cast<long long>(t));
+  }
+  const uint32_t slot = plan->next % kRing;
+  if (plan->used[slot]) {
+    he = hipEventSynchronize(plan->ev[slot]);
+    if (he != hipSuccess) return hip_fail(he, "zds_grad_accumulate: staging slot wait");
+  }
+  const void **h = plan->h_ptrs + static_cast<size_t>(slot) * E;
+  const void **d = plan->d_ptrs + static_cast<size_t>(slot) * E;
+  for (int32_t i = 0; i < E; ++i) h[i] = src_ptrs[plan->entries[4 * static_cast<size_t>(i)]];
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  he = hipMemcpyAsync(d, h, sizeof(void *) * E, hipMemcpyHostToDevice, s);
+  if (he != hipSuccess) return hip_fail(he, "zds_grad_accumulate: pointer upload");
+  PlanDev pd{plan->d_table, E, plan->total_chunks};
+  zds_status st = launch_accumulate(pd, d, src_dtype, dst, dst_dtype, mode, s);
+  if (st != ZDS_OK) return st;
+  he = hipEventRecord(plan->ev[slot], s);
+  if (he != hipSuccess) return hip_fail(he, "zds_grad_accumulate: hipEventRecord");
+  plan->used[slot] = true;
+  plan->next += 1;
+  return ZDS_OK;
+}
+
+extern "C" size_t zds_workspace_bytes(int64_t n) {
+  return static_cast<size_t>(norm_grid(n < 0 ? 0 : n)) * sizeof(double);
+}
+
+extern "C" zds_status zds_overflow_and_norm(const void *grads, zds_dtype dtype, int64_t n,
+                                            int32_t accum_steps, float max_norm,
+                                            const zds_step_state *state_dev, zds_step_scalars *out_dev,
+                                            void *ws, size_t ws_bytes, void *stream) {
+  clear_error();
+  if (!valid_dtype(dtype)) return fail(ZDS_EINVAL, "zds_overflow_and_norm: bad dtype");
+  if (n < 0) return fail(ZDS_EINVAL, "zds_overflow_and_norm: n < 0");
+  if (accum_steps < 1) return fail(ZDS_EINVAL, "zds_overflow_and_norm: accum_steps must be >= 1");
+  if (!state_dev || !out_dev) return fail(ZDS_EINVAL, "zds_overflow_and_norm: null state or output");
+  if (!aligned(state_dev, 8) || !aligned(out_dev, 8))
+    return fail(ZDS_EALIGN, "zds_overflow_and_norm: state/output not 8-byte aligned");
+  if (n > 0 && !grads) return fail(ZDS_EINVAL, "zds_overflow_and_norm: null grads");
+  if (n > 0 && !aligned(grads, static_cast<uintptr_t>(dtype_size(dtype))))
+    return fail(ZDS_EALIGN, "zds_overflow_and_norm: grads misaligned");
+  if (!ws || ws_bytes < zds_workspace_bytes(n) || !aligned(ws, 8))
+    return fail(ZDS_EINVAL, "zds_overflow_and_norm: workspace of %zu bytes needed (8-byte aligned)", zds_workspace_bytes(n));
+  // n == 0 still writes the scalars: the norm of an empty shard is 0.
+  return launch_norm(grads, dtype, n, accum_steps, max_norm, state_dev, out_dev,
+                     static_cast<double *>(ws), static_cast<hipStream_t>(stream));
+}
+
+extern "C" zds_status zds_adam_step(const zds_adamw_hparams *hp, const void *grads, zds_dtype grad_dtype,
+                                    float *master, float *exp_avg, float *exp_avg_sq, void *params_out,
+                                    zds_dtype param_dtype, int64_t n, const zds_step_scalars *scalars_dev,
+                                    const zds_step_state *state_dev, void *stream) {
+  clear_error();
+  if (!hp) return fail(ZDS_EINVAL, "zds_adam_step: null hparams");
+  if (!valid_dtype(grad_dtype)) return fail(ZDS_EINVAL, "zds_adam_step: bad grad dtype");
+  if (params_out && param_dtype != ZDS_FP16 && param_dtype != ZDS_BF16)
+    return fail(ZDS_EINVAL, "zds_adam_step: param dtype must be fp16 or bf16");
+  if (n < 0) return fail(ZDS_EINVAL, "zds_adam_step: n < 0");
+  if (!(hp->beta1 >= 0.5f && hp->beta1 < 1.0f && hp->beta2 >= 0.5f && hp->beta2 < 1.0f))
+    return fail(ZDS_EINVAL, "zds_adam_step: betas must lie in [0.5, 1)");
+  if (!(hp->eps > 0.0f) || !(hp->lr >= 0.0f) || !(hp->weight_decay >= 0.0f))
+    return fail(ZDS_EINVAL, "zds_adam_step: need eps > 0, lr >= 0, weight_decay >= 0");
+  if (n == 0) return ZDS_OK;
+  if (!grads || !master || !exp_avg || !exp_avg_sq || !scalars_dev || !state_dev)
+    return fail(ZDS_EINVAL, "zds_adam_step: null pointer");
+  if (!aligned(grads, static_cast<uintptr_t>(dtype_size(grad_dtype))) || !aligned(master, 4) ||
+      !aligned(exp_avg, 4) || !aligned(exp_avg_sq, 4) || (params_out && !aligned(params_out, 2)) ||
+      !aligned(scalars_dev, 8) || !aligned(state_dev, 8))
+    return fail(ZDS_EALIGN, "zds_adam_step: pointer not aligned to its element size");
+  return launch_adam(*hp, grads, grad_dtype, master, exp_avg, exp_avg_sq, params_out, param_dtype, n,
+                     scalars_dev, state_dev, static_cast<hipStream_t>(stream));
+}
+
+static zds_status check_cfg(const zds_scaler_config *cfg) {
+  if (!cfg) return fail(ZDS_EINVAL, "null scaler config");
+  if (cfg->dynamic) {
+    if (cfg->window < 1 || cfg->hysteresis < 1)
+      return fail(ZDS_EINVAL, "scaler config: window and hysteresis must be >= 1");
+    if (cfg->initial_scale_power < -126 || cfg->initial_scale_power > 127)
+      return fail(ZDS_EINVAL, "scaler config: initial_scale_power out of fp32 range");
+    if (!(cfg->min_scale > 0.0f)) return fail(ZDS_EINVAL, "scaler config: min_scale must be > 0");
+  } else if (!(cfg->static_scale > 0.0f)) {
+    return fail(ZDS_EINVAL, "scaler config: static_scale must be > 0");
+  }
+  return ZDS_OK;
+}
+
+extern "C" zds_status zds_step_state_init(zds_step_state *state_dev, const zds_scaler_config *cfg,
+                                          int64_t t0, double beta1_pow0, double beta2_pow0, void *stream) {
+  clear_error();
+  if (!state_dev) return fail(ZDS_EINVAL, "zds_step_state_init: null state");
+  if (!aligned(state_dev, 8)) return fail(ZDS_EALIGN, "zds_step_state_init: state not 8-byte aligned");
+  zds_status s = check_cfg(cfg);
+  if (s != ZDS_OK) return s;
+  if (t0 < 0) return fail(ZDS_EINVAL, "zds_step_state_init: t0 < 0");
+  zds_step_state init;
+  state_from_config(init, *cfg, t0, beta1_pow0, beta2_pow0);
+  return launch_state_init(state_dev, init, static_cast<hipStream_t>(stream));
+}
+
+extern "C" zds_status zds_loss_scaler_update(zds_step_state *state_dev, const zds_step_scalars *scalars_dev,
+                                             const zds_adamw_hparams *hp, void *stream) {
+  clear_error();
+  if (!state_dev || !scalars_dev || !hp) return fail(ZDS_EINVAL, "zds_loss_scaler_update: null argument");
+  if (!aligned(state_dev, 8) || !aligned(scalars_dev, 8))
+    return fail(ZDS_EALIGN, "zds_loss_scaler_update: state/scalars not 8-byte aligned");
+  return launch_scaler(state_dev, scalars_dev, hp->beta1, hp->beta2, static_cast<hipStream_t>(stream));
+}
+
+extern "C" zds_status zds_step_state_init_host(zds_step_state *state, const zds_scaler_config *cfg,
+                                               int64_t t0, double beta1_pow0, double beta2_pow0) {
+  clear_error();
+  if (!state) return fail(ZDS_EINVAL, "zds_step_state_init_host: null state");
+  zds_status s = check_cfg(cfg);
+  if (s != ZDS_OK) return s;
+  if (t0 < 0) return fail(ZDS_EINVAL, "zds_step_state_init_host: t0 < 0");
+  state_from_config(*state, *cfg, t0, beta1_pow0, beta2_pow0);
+  return ZDS_OK;
+}
+
+extern "C" zds_status zds_loss_scaler_update_host(zds_step_state *state, uint32_t overflow,
+                                                  const zds_adamw_hparams *hp) {
+  clear_error();
+  if (!state || !hp) return fail(ZDS_EINVAL, "zds_loss_scaler_update_host: null argument");
+  scaler_transition(*state, overflow ? 1u : 0u, hp->beta1, hp->beta2);
+  return ZDS_OK;
+}
+
+extern "C" zds_status zds_adam_constants_host(const zds_adamw_hparams *hp, const zds_step_state *state,
+                                              float *out5) {
+  clear_error();
+  if (!hp || !state || !out5) return fail(ZDS_EINVAL, "zds_adam_constants_host: null argument");
+  const AdamConsts c = adam_constants(*hp, state->beta1_pow, state->beta2_pow);
+  out5[0] = c.step_size;
+  out5[1] = c.bc2_sqrt;
+  out5[2] = c.decay;
+  out5[3] = c.omb1;
+  out5[4] = c.omb2;
+  return ZDS_OK;
+}
+
+extern "C" zds_status zds_clip_scalars_host(double sumsq, float scale, int32_t accum_steps, float max_norm,
+                                            zds_step_scalars *out) {
+  clear_error();
+  if (!out) return fail(ZDS_EINVAL, "zds_clip_scalars_host: null output");
+  if (accum_steps < 1) return fail(ZDS_EINVAL, "zds_clip_scalars_host: accum_steps must be >= 1");
+  clip_scalars(sumsq, scale, accum_steps, max_norm, *out);
+  return ZDS_OK;
+}
+
+extern "C" const char *zds_last_error(void) { return g_err.c_str(); }
+
+extern "C" const char *zds_status_string(zds_status s) {
+  switch (s) {
+    case ZDS_OK: return "ok";
+    case ZDS_EINVAL: return "invalid argument";
+    case ZDS_EALIGN: return "misaligned pointer";
+    case ZDS_ENOMEM: return "out of memory";
+    case ZDS_EHIP: return "HIP error";
+  }
+  return "unknown status";
+}
+
+extern "C" int32_t zds_abi_version(void) { return ZDS_ABI_VERSION; }
+
+static_assert(sizeof(zds_step_state) == 64, "zds_step_state is 64 bytes");
+static_assert(sizeof(zds_step_scalars) == 32, "zds_step_scalars is 32 bytes");

@@ -1,0 +1,348 @@
+"""ctypes binding of libzds (include/zds.h), one Python function per C entry
+point and with the same name. Argument marshalling only: tensors are passed
+as device pointers, torch's current HIP stream as the stream, and every step
+of the optimizer path runs in the library's kernels.
+
+The library must have been built (python -m zero_sharded_mixed_tensor_amd.build);
+loading fails loudly otherwise. torch is imported first so that the library
+binds to the HIP runtime torch already loaded.
+"""
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libzds.so")
+
+ZDS_OK, ZDS_EINVAL, ZDS_EALIGN, ZDS_ENOMEM, ZDS_EHIP = 0, 1, 2, 3, 4
+ZDS_FP16, ZDS_BF16, ZDS_FP32 = 0, 1, 2
+ZDS_COPY, ZDS_OVERWRITE, ZDS_ACCUMULATE = 0, 1, 2
+
+STATE_BYTES = 64
+SCALARS_BYTES = 32
+
+
+class ZdsError(RuntimeError):
+    def __init__(self, status, msg):
+        super().__init__("zds status %d: %s" % (status, msg))
+        self.status = status
+
+
+class AdamWHparams(ctypes.Structure):
+    _fields_ = [("lr", ctypes.c_float), ("beta1", ctypes.c_float), ("beta2", ctypes.c_float),
+                ("eps", ctypes.c_float), ("weight_decay", ctypes.c_float)]
+
+
+class ScalerConfig(ctypes.Structure):
+    _fields_ = [("dynamic", ctypes.c_int32), ("initial_scale_power", ctypes.c_int32),
+                ("window", ctypes.c_int32), ("hysteresis", ctypes.c_int32),
+                ("min_scale", ctypes.c_float), ("static_scale", ctypes.c_float)]
+
+
+class StepState(ctypes.Structure):
+    _fields_ = [("scale", ctypes.c_float), ("good_steps", ctypes.c_int32),
+                ("hyst_left", ctypes.c_int32), ("window", ctypes.c_int32),
+                ("hysteresis", ctypes.c_int32), ("min_scale", ctypes.c_float),
+                ("dynamic", ctypes.c_int32), ("last_skip", ctypes.c_uint32),
+                ("t", ctypes.c_int64), ("beta1_pow", ctypes.c_double),
+                ("beta2_pow", ctypes.c_double), ("steps_seen", ctypes.c_uint32),
+                ("steps_skipped", ctypes.c_uint32)]
+
+
+class StepScalars(ctypes.Structure):
+    _fields_ = [("overflow", ctypes.c_uint32), ("accum_steps", ctypes.c_int32),
+                ("sumsq", ctypes.c_double), ("norm", ctypes.c_float),
+                ("clip_coef", ctypes.c_float), ("grad_scale", ctypes.c_float),
+                ("scale_used", ctypes.c_float)]
+
+
+assert ctypes.sizeof(StepState) == STATE_BYTES and ctypes.sizeof(StepScalars) == SCALARS_BYTES
+
+_P = ctypes.c_void_p
+_I32, _I64, _U32 = ctypes.c_int32, ctypes.c_int64, ctypes.c_uint32
+_PI64 = ctypes.POINTER(ctypes.c_int64)
+_SIGS = {
+    "zds_flat_layout": (_I32, [_PI64, _I32, _I32, _PI64, _PI64]),
+    "zds_shard_range": (_I32, [_I64, _I32, _I32, _I32, _PI64, _PI64]),
+    "zds_shard_entries": (_I32, [_PI64, _I32, _I32, _I64, _I64, _PI64, _I32,
+                                 ctypes.POINTER(ctypes.c_int32)]),
+    "zds_plan_create": (_I32, [ctypes.POINTER(_P), _PI64, _I32, _I32, _I64, _I64]),
+    "zds_plan_destroy": (None, [_P]),
+    "zds_plan_num_entries": (_I32, [_P]),
+    "zds_plan_entry": (_I32, [_P, _I32, _PI64]),
+    "zds_grad_accumulate": (_I32, [_P, ctypes.POINTER(_P), _I32, _P, _I32, _I32, _P]),
+    "zds_workspace_bytes": (ctypes.c_size_t, [_I64]),
+    "zds_overflow_and_norm": (_I32, [_P, _I32, _I64, _I32, ctypes.c_float, _P, _P, _P,
+                                     ctypes.c_size_t, _P]),
+    "zds_adam_step": (_I32, [ctypes.POINTER(AdamWHparams), _P, _I32, _P, _P, _P, _P, _I32, _I64,
+                             _P, _P, _P]),
+    "zds_step_state_init": (_I32, [_P, ctypes.POINTER(ScalerConfig), _I64, ctypes.c_double,
+                                   ctypes.c_double, _P]),
+    "zds_loss_scaler_update": (_I32, [_P, _P, ctypes.POINTER(AdamWHparams), _P]),
+    "zds_step_state_init_host": (_I32, [ctypes.POINTER(StepState), ctypes.POINTER(ScalerConfig),
+                                        _I64, ctypes.c_double, ctypes.c_double]),
+    "zds_loss_scaler_update_host": (_I32, [ctypes.POINTER(StepState), _U32,
+                                           ctypes.POINTER(AdamWHparams)]),
+    "zds_adam_constants_host": (_I32, [ctypes.POINTER(AdamWHparams), ctypes.POINTER(StepState),
+                                       ctypes.POINTER(ctypes.c_float)]),
+    "zds_clip_scalars_host": (_I32, [ctypes.c_double, ctypes.c_float, _I32, ctypes.c_float,
+                                     ctypes.POINTER(StepScalars)]),
+    "zds_last_error": (ctypes.c_char_p, []),
+    "zds_status_string": (ctypes.c_char_p, [_I32]),
+    "zds_abi_version": (_I32, []),
+}
+
+
+def _load(path=LIB_PATH):
+    if not os.path.exists(path):
+        raise ImportError("libzds.so is not built at %s; run "
+                          "`python -m zero_sharded_mixed_tensor_amd.build`" % path)
+    lib = ctypes.CDLL(path)
+    for name, (res, args) in _SIGS.items():
+        f = getattr(lib, name)
+        f.restype = res
+        f.argtypes = args
+    return lib
+
+
+lib = _load()
+
+
+def _check(status):
+    if status != ZDS_OK:
+        raise ZdsError(status, lib.zds_last_error().decode())
+
+
+def _i64arr(xs):
+    return (ctypes.c_int64 * max(1, len(xs)))(*[int(x) for x in xs])
+
+
+_DT = {torch.float16: ZDS_FP16, torch.bfloat16: ZDS_BF16, torch.float32: ZDS_FP32}
+
+
+def dtype_code(t):
+    try:
+        return _DT[t.dtype]
+    except KeyError:
+        raise ZdsError(ZDS_EINVAL, "unsupported dtype %s" % t.dtype)
+
+
+def _dev_ptr(t, what):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
+        raise ZdsError(ZDS_EINVAL, "%s must be a device tensor" % what)
+    if not t.is_contiguous():
+        raise ZdsError(ZDS_EINVAL, "%s must be contiguous" % what)
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+def hparams(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01):
+    return AdamWHparams(lr, beta1, beta2, eps, weight_decay)
+
+
+def scaler_config(dynamic=True, initial_scale_power=16, window=1000, hysteresis=1,
+                  min_scale=1.0, static_scale=1.0):
+    return ScalerConfig(int(bool(dynamic)), initial_scale_power, window, hysteresis, min_scale,
+                        static_scale)
+
+
+# ------------------------------------------------------------------ geometry
+
+def zds_flat_layout(numels, flat_align):
+    offs = (ctypes.c_int64 * max(1, len(numels)))()
+    total = ctypes.c_int64()
+    _check(lib.zds_flat_layout(_i64arr(numels), len(numels), flat_align, offs, ctypes.byref(total)))
+    return list(offs)[:len(numels)], total.value
+
+
+def zds_shard_range(flat_total, world, rank, flat_align):
+    lo, hi = ctypes.c_int64(), ctypes.c_int64()
+    _check(lib.zds_shard_range(flat_total, world, rank, flat_align, ctypes.byref(lo), ctypes.byref(hi)))
+    return lo.value, hi.value
+
+
+def zds_shard_entries(numels, flat_align, lo, hi):
+    cnt = ctypes.c_int32()
+    st = lib.zds_shard_entries(_i64arr(numels), len(numels), flat_align, lo, hi, None, 0,
+                               ctypes.byref(cnt))
+    if st != ZDS_OK and cnt.value == 0:
+        _check(st)
+    out = (ctypes.c_int64 * (4 * max(1, cnt.value)))()
+    _check(lib.zds_shard_entries(_i64arr(numels), len(numels), flat_align, lo, hi, out, cnt.value,
+                                 ctypes.byref(cnt)))
+    v = list(out)
+    return [tuple(v[4 * i:4 * i + 4]) for i in range(cnt.value)]
+
+
+# ------------------------------------------------------------------ plans
+
+class Plan:
+    """Owning handle of a zds_plan (tensor table of one flat range)."""
+
+    def __init__(self, handle, num_tensors):
+        self.handle = handle
+        self.num_tensors = num_tensors
+
+    @property
+    def num_entries(self):
+        return lib.zds_plan_num_entries(self.handle)
+
+    def entries(self):
+        out = []
+        buf = (ctypes.c_int64 * 4)()
+        for e in range(self.num_entries):
+            _check(lib.zds_plan_entry(self.handle, e, buf))
+            out.append(tuple(buf))
+        return out
+
+    def close(self):
+        if self.handle:
+            lib.zds_plan_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def zds_plan_create(numels, flat_align, lo, hi):
+    h = ctypes.c_void_p()
+    _check(lib.zds_plan_create(ctypes.byref(h), _i64arr(numels), len(numels), flat_align, lo, hi))
+    return Plan(h, len(numels))
+
+
+# ------------------------------------------------------------------ hot calls
+
+def zds_grad_accumulate(plan, srcs, dst, mode, stream=None):
+    """srcs: one device tensor per tensor of the plan's layout (None where the
+    plan has no entry); dst: the flat device buffer of the plan's range."""
+    if len(srcs) != plan.num_tensors:
+        raise ZdsError(ZDS_EINVAL, "need %d source tensors" % plan.num_tensors)
+    sdt = None
+    ptrs = (ctypes.c_void_p * max(1, len(srcs)))()
+    for i, t in enumerate(srcs):
+        if t is None:
+            continue
+        c = dtype_code(t)
+        if sdt is None:
+            sdt = c
+        elif c != sdt:
+            raise ZdsError(ZDS_EINVAL, "source tensors must share one dtype")
+        ptrs[i] = _dev_ptr(t, "source %d" % i)
+    if sdt is None:
+        sdt = ZDS_FP16
+    _check(lib.zds_grad_accumulate(plan.handle, ptrs, sdt, _dev_ptr(dst, "dst"), dtype_code(dst),
+                                   mode, _stream(stream)))
+
+
+def zds_workspace_bytes(n):
+    return lib.zds_workspace_bytes(n)
+
+
+def zds_overflow_and_norm(grads, accum_steps, max_norm, state, scalars, ws, stream=None, n=None):
+    n = grads.numel() if n is None else n
+    _check(lib.zds_overflow_and_norm(_dev_ptr(grads, "grads"), dtype_code(grads), n, accum_steps,
+                                     max_norm, _dev_ptr(state, "state"), _dev_ptr(scalars, "scalars"),
+                                     _dev_ptr(ws, "workspace"), ws.numel() * ws.element_size(),
+                                     _stream(stream)))
+
+
+def zds_adam_step(hp, grads, master, exp_avg, exp_avg_sq, params_out, scalars, state, stream=None,
+                  n=None):
+    n = master.numel() if n is None else n
+    for name, t in (("grads", grads), ("exp_avg", exp_avg), ("exp_avg_sq", exp_avg_sq)):
+        if t.numel() < n:
+            raise ZdsError(ZDS_EINVAL, "%s shorter than master" % name)
+    if params_out is not None and params_out.numel() < n:
+        raise ZdsError(ZDS_EINVAL, "params_out shorter than master")
+    pdt = dtype_code(params_out) if params_out is not None else ZDS_FP16
+    _check(lib.zds_adam_step(ctypes.byref(hp), _dev_ptr(grads, "grads"), dtype_code(grads),
+                             _dev_ptr(master, "master"), _dev_ptr(exp_avg, "exp_avg"),
+                             _dev_ptr(exp_avg_sq, "exp_avg_sq"), _dev_ptr(params_out, "params_out"),
+                             pdt, n, _dev_ptr(scalars, "scalars"), _dev_ptr(state, "state"),
+                             _stream(stream)))
+
+
+def zds_step_state_init(state, cfg, t0=0, beta1_pow0=1.0, beta2_pow0=1.0, stream=None):
+    _check(lib.zds_step_state_init(_dev_ptr(state, "state"), ctypes.byref(cfg), t0, beta1_pow0,
+                                   beta2_pow0, _stream(stream)))
+
+
+def zds_loss_scaler_update(state, scalars, hp, stream=None):
+    _check(lib.zds_loss_scaler_update(_dev_ptr(state, "state"), _dev_ptr(scalars, "scalars"),
+                                      ctypes.byref(hp), _stream(stream)))
+
+
+# ------------------------------------------------------------------ host twins
+
+def zds_step_state_init_host(cfg, t0=0, beta1_pow0=1.0, beta2_pow0=1.0):
+    s = StepState()
+    _check(lib.zds_step_state_init_host(ctypes.byref(s), ctypes.byref(cfg), t0, beta1_pow0, beta2_pow0))
+    return s
+
+
+def zds_loss_scaler_update_host(state, overflow, hp):
+    _check(lib.zds_loss_scaler_update_host(ctypes.byref(state), int(overflow), ctypes.byref(hp)))
+    return state
+
+
+def zds_adam_constants_host(hp, state):
+    out = (ctypes.c_float * 5)()
+    _check(lib.zds_adam_constants_host(ctypes.byref(hp), ctypes.byref(state), out))
+    return dict(zip(("step_size", "bc2_sqrt", "decay", "omb1", "omb2"), list(out)))
+
+
+def zds_clip_scalars_host(sumsq, scale, accum_steps, max_norm):
+    s = StepScalars()
+    _check(lib.zds_clip_scalars_host(sumsq, scale, accum_steps, max_norm, ctypes.byref(s)))
+    return s
+
+
+def zds_last_error():
+    return lib.zds_last_error().decode()
+
+
+def zds_abi_version():
+    return lib.zds_abi_version()
+
+
+# ------------------------------------------------------------------ device structs
+
+def new_state(device="cuda"):
+    return torch.zeros(STATE_BYTES, dtype=torch.uint8, device=device)
+
+
+def new_scalars(device="cuda"):
+    return torch.zeros(SCALARS_BYTES, dtype=torch.uint8, device=device)
+
+
+def new_workspace(n, device="cuda"):
+    return torch.empty((zds_workspace_bytes(n) + 7) // 8, dtype=torch.float64, device=device)
+
+
+def read_state(t):
+    return StepState.from_buffer_copy(bytes(t.cpu().numpy().tobytes()))
+
+
+def read_scalars(t):
+    return StepScalars.from_buffer_copy(bytes(t.cpu().numpy().tobytes()))
+
+
+def write_scalars(t, scalars):
+    """Host -> device copy of a StepScalars (tests force flags this way)."""
+    import numpy as np
+    buf = np.frombuffer(bytes(scalars), dtype=np.uint8).copy()
+    t.copy_(torch.from_numpy(buf).to(t.device))
