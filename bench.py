@@ -35,7 +35,10 @@ def _parse():
                     choices=["llama7b_s1", "llama7b_s1_accum16", "llama7b_whole_1024", "llama65b_s1", "tiny"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=1 << 24, help="oracle sample size (params)")
-    ap.add_argument("--cpu-repeats", type=int, default=8, help="oracle passes over the sample")
+    ap.add_argument("--cpu-repeats", type=int, default=2, help="minimum oracle passes over the sample")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run torch's device copy of a known size (1 GiB read + 1 GiB write) "
+                         "5 times, to calibrate HBM byte counters")
     return ap.parse_args()
 
 
@@ -182,11 +185,11 @@ def run_gpu(args, w):
 
 # ------------------------------------------------------------------ CPU oracle part
 
-def run_cpu_baseline(w, sample, repeats):
+def run_cpu_baseline(w, sample, repeats, min_seconds=10.0):
     """Time the oracle's step (flatten copy, overflow + norm, AdamW + cast,
-    scaler update) `repeats` times on the first `sample` params of the same
-    workload, with inputs generated before timing. Single process: NumPy's
-    elementwise kernels use one thread."""
+    scaler update) on the first `sample` params of the same workload, at least
+    `repeats` times and for at least `min_seconds`, with inputs generated before
+    timing. Single process: NumPy's elementwise kernels use one thread."""
     import numpy as np
     import oracle as O
     from workloads import draw_grads, draw_master, draw_prior_moments
@@ -207,12 +210,14 @@ def run_cpu_baseline(w, sample, repeats):
     ent = [(0, 0, n, 0)]
     bucket = np.zeros(n, np.uint16)
     t0 = time.perf_counter()
-    for _ in range(repeats):
+    done = 0
+    while done < repeats or time.perf_counter() - t0 < min_seconds:
         O.flatten_copy([g], ent, bucket)
         r = O.optimizer_step(bucket, w["gdt"], master, m, v, st, O.AdamW(), 1.0, 1, w["pdt"])
         assert r[3] is not None
+        done += 1
     dt = time.perf_counter() - t0
-    return dict(value=n * repeats / dt, seconds=dt, n=n, repeats=repeats)
+    return dict(value=n * done / dt, seconds=dt, n=n, repeats=done)
 
 
 def main():
@@ -263,6 +268,14 @@ def main():
             "traffic": None,
         },
     }
+    if args.copy_calibration:
+        import torch
+        a = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+        b = torch.empty_like(a)
+        for _ in range(5):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        out["copy_calibration"] = {"bytes_read": 1 << 30, "bytes_written": 1 << 30, "launches": 5}
     if not args.no_cpu_baseline:
         c = run_cpu_baseline(w, args.cpu_sample, args.cpu_repeats)
         out["cpu_baseline"] = {

@@ -105,8 +105,10 @@ typedef struct zds_step_state {
   uint32_t steps_skipped;
 } zds_step_state;
 
-/* Device-resident per-step scalars, 32 bytes, written by
- * zds_overflow_and_norm and read by zds_adam_step / zds_loss_scaler_update. */
+/* Device-resident per-step scalars, 64 bytes. The first 32 bytes are written
+ * by zds_overflow_and_norm; zds_adam_step fills the step constants of its
+ * update (from its hyperparameters and the step state) before its main
+ * kernel runs; zds_loss_scaler_update reads the overflow flag. */
 typedef struct zds_step_scalars {
   uint32_t overflow;   /* 1 if any gradient element is inf or NaN           */
   int32_t accum_steps; /* K used for the mean over micro-batches            */
@@ -115,6 +117,13 @@ typedef struct zds_step_scalars {
   float clip_coef;     /* max_norm / (norm + 1e-6) if norm > max_norm, else 1 */
   float grad_scale;    /* clip_coef / (S * K), the factor Adam applies      */
   float scale_used;    /* S read from the step state                        */
+  /* written by zds_adam_step: */
+  float step_size;     /* lr / (1 - beta1^t)                                */
+  float bc2_sqrt;      /* sqrt(1 - beta2^t)                                 */
+  float decay;         /* 1 - lr * weight_decay                             */
+  float one_minus_beta1;
+  float one_minus_beta2;
+  uint32_t reserved[3];
 } zds_step_scalars;
 
 /* ---------------------------------------------------------------------------
@@ -211,6 +220,9 @@ zds_status zds_overflow_and_norm(const void *grads, zds_dtype dtype, int64_t n,
  * with t = state.t + 1 and the step scalars derived in float64, each rounded
  * once to fp32. If scalars_dev->overflow is set every element is left
  * untouched (the step is skipped on the device; no host sync).
+ * The step constants are derived once per call by a single-wave kernel and
+ * stored in scalars_dev (step_size .. one_minus_beta2); the update kernel
+ * reads them from there.
  *   grads       device, n elements of grad_dtype (16-bit, or the fp32 accumulator)
  *   master, exp_avg, exp_avg_sq   device fp32, n elements, updated in place
  *   params_out  device, n elements of param_dtype (FP16/BF16), write-only;
@@ -218,7 +230,7 @@ zds_status zds_overflow_and_norm(const void *grads, zds_dtype dtype, int64_t n,
  * The state is read, not advanced: zds_loss_scaler_update commits t. */
 zds_status zds_adam_step(const zds_adamw_hparams *hp, const void *grads, zds_dtype grad_dtype,
                          float *master, float *exp_avg, float *exp_avg_sq, void *params_out,
-                         zds_dtype param_dtype, int64_t n, const zds_step_scalars *scalars_dev,
+                         zds_dtype param_dtype, int64_t n, zds_step_scalars *scalars_dev,
                          const zds_step_state *state_dev, void *stream);
 
 /* Row a3. Initialise the device step state from cfg with Adam step count t0

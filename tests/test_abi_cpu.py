@@ -36,7 +36,8 @@ def test_exports_every_declared_function():
 def test_struct_layouts():
     assert ctypes.sizeof(zds.StepState) == 64
     assert zds.StepState.t.offset == 32 and zds.StepState.beta1_pow.offset == 40
-    assert ctypes.sizeof(zds.StepScalars) == 32 and zds.StepScalars.sumsq.offset == 8
+    assert ctypes.sizeof(zds.StepScalars) == 64 and zds.StepScalars.sumsq.offset == 8
+    assert zds.StepScalars.step_size.offset == 32
 
 
 @pytest.mark.parametrize("seed", range(20))

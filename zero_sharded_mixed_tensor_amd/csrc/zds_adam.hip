@@ -7,22 +7,40 @@
 //
 // Memory-bound stream, no MFMA: per element it reads the grad (2 or 4 B) and
 // master/m/v (12 B) and writes master/m/v (12 B) and the 16-bit param (2 B):
-// 28 B (16-bit grads) or 30 B (fp32 accumulator). Each thread owns groups of
-// 8 consecutive elements, so every access is a 16-byte global load/store
-// (two per fp32 group); UNROLL groups are loaded before any is computed to
-// keep enough bytes in flight per CU. The grid is a fixed multiple of the CU
-// count and strides over the groups.
+// 28 B (16-bit grads) or 30 B (fp32 accumulator).
+//
+// Access pattern. A lane owns a quad of 4 consecutive elements: one 16-byte
+// access per fp32 array and one 8-byte access per 16-bit array. Lane l of a
+// wave takes quad base + l, so every load or store instruction of a wave
+// covers one contiguous range (1 KiB of fp32, 512 B of 16-bit) and every
+// 128-byte line is requested by exactly one instruction. (Two 16-byte pieces
+// per lane at stride 32 B would make two instructions each touch every line
+// half, which measured far slower with the non-temporal hint.) A block takes
+// QUADS consecutive tiles of BLOCK quads, issues all loads, then computes and
+// stores. By default the grid has one block per tile, so the hardware keeps
+// replacing finished waves with new ones, and block ids are remapped so that
+// each of the 8 XCDs (which receive blocks round-robin) streams through one
+// contiguous eighth of the arrays.
+//
+// The step constants (lr / (1 - beta1^t), sqrt(1 - beta2^t), 1 - lr*wd, the
+// 1 - beta values) are derived once per call by a single-wave prep kernel
+// into the caller's step-scalars struct, so the update kernel only loads them.
 #include "zds_device.h"
 #include "zds_internal.h"
 
-#ifndef ZDS_ADAM_UNROLL
-#define ZDS_ADAM_UNROLL 2
-#endif
 #ifndef ZDS_ADAM_BLOCK
 #define ZDS_ADAM_BLOCK 256
 #endif
-#ifndef ZDS_ADAM_WAVES_PER_CU
-#define ZDS_ADAM_WAVES_PER_CU 32
+#ifndef ZDS_ADAM_QUADS
+#define ZDS_ADAM_QUADS 1
+#endif
+// 0: one block per tile; > 0: at most this many resident waves per CU, the
+// blocks striding over the tiles.
+#ifndef ZDS_ADAM_PERSIST
+#define ZDS_ADAM_PERSIST 0
+#endif
+#ifndef ZDS_ADAM_XCD
+#define ZDS_ADAM_XCD 1
 #endif
 
 namespace zds {
@@ -34,15 +52,31 @@ struct AdamArgs {
   float *v;
   void *out;
   int64_t n;
-  zds_adamw_hparams hp;
-  const zds_step_scalars *scalars;
-  const zds_step_state *state;
+  float beta1, beta2, eps;
+  const zds_step_scalars *sc;
 };
 
+struct ElemConsts {
+  float b1, b2, omb1, omb2, eps, step_size, bc2_sqrt, decay, gs;
+};
+
+__device__ __forceinline__ ElemConsts load_consts(const AdamArgs &a) {
+  ElemConsts c;
+  c.b1 = a.beta1;
+  c.b2 = a.beta2;
+  c.eps = a.eps;
+  c.omb1 = a.sc->one_minus_beta1;
+  c.omb2 = a.sc->one_minus_beta2;
+  c.step_size = a.sc->step_size;
+  c.bc2_sqrt = a.sc->bc2_sqrt;
+  c.decay = a.sc->decay;
+  c.gs = a.sc->grad_scale;
+  return c;
+}
+
 // One element, fp32, one rounding per operation, in this order.
-__device__ __forceinline__ void adam_elem(float x, float gs, const AdamConsts &c, float &p, float &m,
-                                          float &v) {
-  const float g = x * gs;
+__device__ __forceinline__ void adam_elem(float x, const ElemConsts &c, float &p, float &m, float &v) {
+  const float g = x * c.gs;
   m = c.b1 * m + c.omb1 * g;
   v = c.b2 * v + c.omb2 * (g * g);
   const float denom = sqrtf(v) / c.bc2_sqrt + c.eps;
@@ -50,58 +84,81 @@ __device__ __forceinline__ void adam_elem(float x, float gs, const AdamConsts &c
   p = p - c.step_size * (m / denom);
 }
 
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+template <int D>
+__device__ __forceinline__ void load_quad(const void *base, int64_t q, float (&x)[4]) {
+  if (D == ZDS_FP32) {
+    const f32x4 a = ld_stream(static_cast<const f32x4 *>(base) + q);
+    x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+  } else {
+    const u32x2 w = ld_stream(static_cast<const u32x2 *>(base) + q);
+    x[0] = lo_of<D>(w.x); x[1] = hi_of<D>(w.x);
+    x[2] = lo_of<D>(w.y); x[3] = hi_of<D>(w.y);
+  }
+}
+
+__device__ __forceinline__ void store_quad(float *base, int64_t q, const float (&x)[4]) {
+  const f32x4 a = {x[0], x[1], x[2], x[3]};
+  st_stream(reinterpret_cast<f32x4 *>(base) + q, a);
+}
+
+template <int D>
+__device__ __forceinline__ void store_quad16(void *base, int64_t q, const float (&x)[4]) {
+  const u32x2 w = {pack2<D>(x[0], x[1]), pack2<D>(x[2], x[3])};
+  st_stream(static_cast<u32x2 *>(base) + q, w);
+}
+
+// Block id after the XCD remap: with G a multiple of 8, hardware block b
+// runs on XCD b % 8; it is given tile-block (b % 8) * (G / 8) + b / 8.
+__device__ __forceinline__ int64_t remapped_block() {
+  const int64_t b = blockIdx.x;
+  if (!ZDS_ADAM_XCD) return b;
+  const int64_t per = static_cast<int64_t>(gridDim.x) >> 3;
+  return (b & 7) * per + (b >> 3);
+}
+
 template <int GD, int PD, bool WRITE_OUT>
-__global__ void __launch_bounds__(ZDS_ADAM_BLOCK) adam_vec_kernel(AdamArgs a) {
+__global__ void __launch_bounds__(ZDS_ADAM_BLOCK) adam_quad_kernel(AdamArgs a) {
   // Skip on overflow without a host round trip; the flag is uniform.
-  if (a.scalars->overflow) return;
-  const float gs = a.scalars->grad_scale;
-  const AdamConsts c = adam_constants(a.hp, a.state->beta1_pow, a.state->beta2_pow);
-
-  const int64_t groups = a.n >> 3;
-  const int64_t stride = static_cast<int64_t>(gridDim.x) * ZDS_ADAM_BLOCK;
-  int64_t i = static_cast<int64_t>(blockIdx.x) * ZDS_ADAM_BLOCK + threadIdx.x;
-
-  constexpr int U = ZDS_ADAM_UNROLL;
-  for (; i + (U - 1) * stride < groups; i += U * stride) {
-    float x[U][8], p[U][8], m[U][8], v[U][8];
+  if (a.sc->overflow) return;
+  const ElemConsts c = load_consts(a);
+  constexpr int U = ZDS_ADAM_QUADS;
+  constexpr int64_t span = static_cast<int64_t>(ZDS_ADAM_BLOCK) * U;
+  const int64_t quads = a.n >> 2;
+  const int64_t b0 = remapped_block();
+  for (int64_t t = b0; t * span < quads; t += gridDim.x) {
+    const int64_t q0 = t * span + threadIdx.x;
+    float x[U][4], p[U][4], m[U][4], v[U][4];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int64_t gi = i + u * stride;
-      load8<GD>(a.g, gi, x[u]);
-      load8f(a.p, gi, p[u]);
-      load8f(a.m, gi, m[u]);
-      load8f(a.v, gi, v[u]);
+      const int64_t q = q0 + u * ZDS_ADAM_BLOCK;
+      if (q < quads) {
+        load_quad<GD>(a.g, q, x[u]);
+        load_quad<ZDS_FP32>(a.p, q, p[u]);
+        load_quad<ZDS_FP32>(a.m, q, m[u]);
+        load_quad<ZDS_FP32>(a.v, q, v[u]);
+      }
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
+      const int64_t q = q0 + u * ZDS_ADAM_BLOCK;
+      if (q < quads) {
 #pragma unroll
-      for (int k = 0; k < 8; ++k) adam_elem(x[u][k], gs, c, p[u][k], m[u][k], v[u][k]);
-      const int64_t gi = i + u * stride;
-      store8f(a.p, gi, p[u]);
-      store8f(a.m, gi, m[u]);
-      store8f(a.v, gi, v[u]);
-      if (WRITE_OUT) store8h<PD>(a.out, gi, p[u]);
+        for (int k = 0; k < 4; ++k) adam_elem(x[u][k], c, p[u][k], m[u][k], v[u][k]);
+        store_quad(a.p, q, p[u]);
+        store_quad(a.m, q, m[u]);
+        store_quad(a.v, q, v[u]);
+        if (WRITE_OUT) store_quad16<PD>(a.out, q, p[u]);
+      }
     }
   }
-  for (; i < groups; i += stride) {
-    float x[8], p[8], m[8], v[8];
-    load8<GD>(a.g, i, x);
-    load8f(a.p, i, p);
-    load8f(a.m, i, m);
-    load8f(a.v, i, v);
-#pragma unroll
-    for (int k = 0; k < 8; ++k) adam_elem(x[k], gs, c, p[k], m[k], v[k]);
-    store8f(a.p, i, p);
-    store8f(a.m, i, m);
-    store8f(a.v, i, v);
-    if (WRITE_OUT) store8h<PD>(a.out, i, p);
-  }
-  // Ragged tail: the last n % 8 elements, one per thread of block 0.
-  const int64_t tail0 = groups << 3;
-  if (blockIdx.x == 0 && tail0 + threadIdx.x < a.n) {
+  // Ragged tail: the last n % 4 elements, one per lane of tile-block 0.
+  const int64_t tail0 = quads << 2;
+  if (b0 == 0 && tail0 + threadIdx.x < a.n) {
     const int64_t e = tail0 + threadIdx.x;
     float p = a.p[e], m = a.m[e], v = a.v[e];
-    adam_elem(widen1<GD>(a.g, e), gs, c, p, m, v);
+    adam_elem(widen1<GD>(a.g, e), c, p, m, v);
     a.p[e] = p;
     a.m[e] = m;
     a.v[e] = v;
@@ -109,17 +166,16 @@ __global__ void __launch_bounds__(ZDS_ADAM_BLOCK) adam_vec_kernel(AdamArgs a) {
   }
 }
 
-// Element-wise path for buffers that are not 16-byte aligned.
+// Element-wise path for buffers without the vector alignment.
 template <int GD, int PD, bool WRITE_OUT>
 __global__ void __launch_bounds__(ZDS_ADAM_BLOCK) adam_scalar_kernel(AdamArgs a) {
-  if (a.scalars->overflow) return;
-  const float gs = a.scalars->grad_scale;
-  const AdamConsts c = adam_constants(a.hp, a.state->beta1_pow, a.state->beta2_pow);
+  if (a.sc->overflow) return;
+  const ElemConsts c = load_consts(a);
   const int64_t stride = static_cast<int64_t>(gridDim.x) * ZDS_ADAM_BLOCK;
   for (int64_t e = static_cast<int64_t>(blockIdx.x) * ZDS_ADAM_BLOCK + threadIdx.x; e < a.n;
        e += stride) {
     float p = a.p[e], m = a.m[e], v = a.v[e];
-    adam_elem(widen1<GD>(a.g, e), gs, c, p, m, v);
+    adam_elem(widen1<GD>(a.g, e), c, p, m, v);
     a.p[e] = p;
     a.m[e] = m;
     a.v[e] = v;
@@ -127,44 +183,86 @@ __global__ void __launch_bounds__(ZDS_ADAM_BLOCK) adam_scalar_kernel(AdamArgs a)
   }
 }
 
+// Derives the step constants for t = state.t + 1 into the scalars struct.
+__global__ void __launch_bounds__(64) adam_prep_kernel(zds_adamw_hparams hp, const zds_step_state *state,
+                                                       zds_step_scalars *sc) {
+  if (threadIdx.x != 0) return;
+  const AdamConsts c = adam_constants(hp, state->beta1_pow, state->beta2_pow);
+  sc->step_size = c.step_size;
+  sc->bc2_sqrt = c.bc2_sqrt;
+  sc->decay = c.decay;
+  sc->one_minus_beta1 = c.omb1;
+  sc->one_minus_beta2 = c.omb2;
+}
+
+// Blocks of `kernel` that fit on one CU at once (queried once per kernel).
+template <typename K>
+static int resident_blocks_per_cu(K kernel) {
+  static int cached = 0;
+  if (cached == 0) {
+    int nb = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, kernel, ZDS_ADAM_BLOCK, 0) != hipSuccess || nb < 1)
+      nb = 1;
+    cached = nb;
+  }
+  return cached;
+}
+
+static int64_t round8(int64_t g) { return ZDS_ADAM_XCD ? ((g + 7) / 8) * 8 : g; }
+
 template <int GD, int PD, bool WO>
-static void launch_one(bool vec, int grid, hipStream_t s, const AdamArgs &a) {
-  if (vec)
-    hipLaunchKernelGGL((adam_vec_kernel<GD, PD, WO>), dim3(grid), dim3(ZDS_ADAM_BLOCK), 0, s, a);
-  else
-    hipLaunchKernelGGL((adam_scalar_kernel<GD, PD, WO>), dim3(grid), dim3(ZDS_ADAM_BLOCK), 0, s, a);
+static void launch_one(bool vec, hipStream_t s, const AdamArgs &a) {
+  if (vec) {
+    const int64_t span = static_cast<int64_t>(ZDS_ADAM_BLOCK) * ZDS_ADAM_QUADS;
+    int64_t tiles = ((a.n >> 2) + span - 1) / span;
+    if (tiles < 1) tiles = 1;
+    int64_t g = tiles;
+    if (ZDS_ADAM_PERSIST > 0) {
+      int64_t cap = static_cast<int64_t>(device_cu_count()) * ZDS_ADAM_PERSIST * 64 / ZDS_ADAM_BLOCK;
+      const int64_t res = static_cast<int64_t>(device_cu_count()) *
+                          resident_blocks_per_cu(adam_quad_kernel<GD, PD, WO>);
+      if (cap > res) cap = res;
+      if (g > cap) g = cap;
+    }
+    g = round8(g);
+    if (g > 0x7ffffff8) g = 0x7ffffff8;
+    hipLaunchKernelGGL((adam_quad_kernel<GD, PD, WO>), dim3(static_cast<uint32_t>(g)), dim3(ZDS_ADAM_BLOCK),
+                       0, s, a);
+  } else {
+    int64_t g = (a.n + ZDS_ADAM_BLOCK - 1) / ZDS_ADAM_BLOCK;
+    const int64_t cap = static_cast<int64_t>(device_cu_count()) *
+                        resident_blocks_per_cu(adam_scalar_kernel<GD, PD, WO>);
+    if (g > cap) g = cap;
+    if (g < 1) g = 1;
+    hipLaunchKernelGGL((adam_scalar_kernel<GD, PD, WO>), dim3(static_cast<uint32_t>(g)), dim3(ZDS_ADAM_BLOCK),
+                       0, s, a);
+  }
 }
 
 template <int GD>
-static void launch_gd(zds_dtype pdt, bool wo, bool vec, int grid, hipStream_t s, const AdamArgs &a) {
+static void launch_gd(zds_dtype pdt, bool wo, bool vec, hipStream_t s, const AdamArgs &a) {
   if (!wo) {
-    launch_one<GD, ZDS_FP16, false>(vec, grid, s, a);
+    launch_one<GD, ZDS_FP16, false>(vec, s, a);
   } else if (pdt == ZDS_BF16) {
-    launch_one<GD, ZDS_BF16, true>(vec, grid, s, a);
+    launch_one<GD, ZDS_BF16, true>(vec, s, a);
   } else {
-    launch_one<GD, ZDS_FP16, true>(vec, grid, s, a);
+    launch_one<GD, ZDS_FP16, true>(vec, s, a);
   }
 }
 
 zds_status launch_adam(const zds_adamw_hparams &hp, const void *grads, zds_dtype gdt, float *master,
-                       float *m, float *v, void *out, zds_dtype pdt, int64_t n,
-                       const zds_step_scalars *scalars, const zds_step_state *state,
-                       hipStream_t stream) {
-  AdamArgs a{grads, master, m, v, out, n, hp, scalars, state};
-  const bool vec = aligned(grads, 16) && aligned(master, 16) && aligned(m, 16) && aligned(v, 16) &&
-                   (out == nullptr || aligned(out, 16));
-  const int64_t items = vec ? (n >> 3) : n;
-  const int64_t per_block = static_cast<int64_t>(ZDS_ADAM_BLOCK) * (vec ? ZDS_ADAM_UNROLL : 1);
-  int64_t blocks = (items + per_block - 1) / per_block;
-  const int64_t cap = static_cast<int64_t>(device_cu_count()) * ZDS_ADAM_WAVES_PER_CU * 64 / ZDS_ADAM_BLOCK;
-  if (blocks > cap) blocks = cap;
-  if (blocks < 1) blocks = 1;
-  const int grid = static_cast<int>(blocks);
-  const bool wo = out != nullptr;
+                       float *m, float *v, void *out, zds_dtype pdt, int64_t n, zds_step_scalars *scalars,
+                       const zds_step_state *state, hipStream_t stream) {
+  hipLaunchKernelGGL(adam_prep_kernel, dim3(1), dim3(64), 0, stream, hp, state, scalars);
+  zds_status st = check_launch("adam_step constants kernel");
+  if (st != ZDS_OK) return st;
+  AdamArgs a{grads, master, m, v, out, n, hp.beta1, hp.beta2, hp.eps, scalars};
+  const bool vec = aligned(grads, gdt == ZDS_FP32 ? 16 : 8) && aligned(master, 16) && aligned(m, 16) &&
+                   aligned(v, 16) && (out == nullptr || aligned(out, 8));
   switch (gdt) {
-    case ZDS_FP16: launch_gd<ZDS_FP16>(pdt, wo, vec, grid, stream, a); break;
-    case ZDS_BF16: launch_gd<ZDS_BF16>(pdt, wo, vec, grid, stream, a); break;
-    default: launch_gd<ZDS_FP32>(pdt, wo, vec, grid, stream, a); break;
+    case ZDS_FP16: launch_gd<ZDS_FP16>(pdt, out != nullptr, vec, stream, a); break;
+    case ZDS_BF16: launch_gd<ZDS_BF16>(pdt, out != nullptr, vec, stream, a); break;
+    default: launch_gd<ZDS_FP32>(pdt, out != nullptr, vec, stream, a); break;
   }
   return check_launch("adam_step kernel");
 }

@@ -305,7 +305,7 @@ extern "C" zds_status zds_overflow_and_norm(const void *grads, zds_dtype dtype, 
 
 extern "C" zds_status zds_adam_step(const zds_adamw_hparams *hp, const void *grads, zds_dtype grad_dtype,
                                     float *master, float *exp_avg, float *exp_avg_sq, void *params_out,
-                                    zds_dtype param_dtype, int64_t n, const zds_step_scalars *scalars_dev,
+                                    zds_dtype param_dtype, int64_t n, zds_step_scalars *scalars_dev,
                                     const zds_step_state *state_dev, void *stream) {
   clear_error();
   if (!hp) return fail(ZDS_EINVAL, "zds_adam_step: null hparams");
@@ -401,6 +401,7 @@ extern "C" zds_status zds_clip_scalars_host(double sumsq, float scale, int32_t a
   clear_error();
   if (!out) return fail(ZDS_EINVAL, "zds_clip_scalars_host: null output");
   if (accum_steps < 1) return fail(ZDS_EINVAL, "zds_clip_scalars_host: accum_steps must be >= 1");
+  *out = zds_step_scalars{};
   clip_scalars(sumsq, scale, accum_steps, max_norm, *out);
   return ZDS_OK;
 }
@@ -421,4 +422,4 @@ extern "C" const char *zds_status_string(zds_status s) {
 extern "C" int32_t zds_abi_version(void) { return ZDS_ABI_VERSION; }
 
 static_assert(sizeof(zds_step_state) == 64, "zds_step_state is 64 bytes");
-static_assert(sizeof(zds_step_scalars) == 32, "zds_step_scalars is 32 bytes");
+static_assert(sizeof(zds_step_scalars) == 64, "zds_step_scalars is 64 bytes");

@@ -63,14 +63,28 @@ __device__ __forceinline__ uint16_t narrow1(float a) {
 }
 
 // Streaming 16-byte loads and stores: every byte of the hot arrays is touched
-// once per call, so they bypass cache retention.
+// once per call, so by default they carry the non-temporal hint.
+#ifndef ZDS_NT_LOADS
+#define ZDS_NT_LOADS 1
+#endif
+#ifndef ZDS_NT_STORES
+#define ZDS_NT_STORES 1
+#endif
 template <typename T>
 __device__ __forceinline__ T ld_stream(const T *p) {
+#if ZDS_NT_LOADS
   return __builtin_nontemporal_load(p);
+#else
+  return *p;
+#endif
 }
 template <typename T>
 __device__ __forceinline__ void st_stream(T *p, T v) {
+#if ZDS_NT_STORES
   __builtin_nontemporal_store(v, p);
+#else
+  *p = v;
+#endif
 }
 
 // 8 consecutive elements of dtype D at 16-byte aligned address, as fp32.

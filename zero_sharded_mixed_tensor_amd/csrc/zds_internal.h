@@ -149,9 +149,8 @@ zds_status launch_norm(const void *grads, zds_dtype dtype, int64_t n, int32_t ac
                        double *partials, hipStream_t stream);
 
 zds_status launch_adam(const zds_adamw_hparams &hp, const void *grads, zds_dtype gdt, float *master,
-                       float *m, float *v, void *out, zds_dtype pdt, int64_t n,
-                       const zds_step_scalars *scalars, const zds_step_state *state,
-                       hipStream_t stream);
+                       float *m, float *v, void *out, zds_dtype pdt, int64_t n, zds_step_scalars *scalars,
+                       const zds_step_state *state, hipStream_t stream);
 
 zds_status launch_scaler(zds_step_state *state, const zds_step_scalars *scalars, float beta1,
                          float beta2, hipStream_t stream);

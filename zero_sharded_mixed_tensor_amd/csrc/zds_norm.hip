@@ -115,7 +115,7 @@ __global__ void __launch_bounds__(ZDS_NORM_BLOCK) norm_stage2(const double *part
   for (int i = threadIdx.x; i < nparts; i += ZDS_NORM_BLOCK) acc += partials[i];
   const double total = block_sum(acc);
   if (threadIdx.x == 0) {
-    zds_step_scalars s;
+    zds_step_scalars s = {};
     clip_scalars(total, state->scale, accum_steps, max_norm, s);
     *out = s;
   }

@@ -10,7 +10,7 @@ from . import zds
 
 
 class ShardStep:
-    """Device buffers of one rank's step: the 64-byte step state, the 32-byte
+    """Device buffers of one rank's step: the 64-byte step state, the 64-byte
     per-step scalars and the norm workspace, plus the step's settings."""
 
     def __init__(self, n, hp=None, scaler=None, max_norm=1.0, accum_steps=1, t0=0,

@@ -21,7 +21,7 @@ ZDS_FP16, ZDS_BF16, ZDS_FP32 = 0, 1, 2
 ZDS_COPY, ZDS_OVERWRITE, ZDS_ACCUMULATE = 0, 1, 2
 
 STATE_BYTES = 64
-SCALARS_BYTES = 32
+SCALARS_BYTES = 64
 
 
 class ZdsError(RuntimeError):
@@ -55,7 +55,10 @@ class StepScalars(ctypes.Structure):
     _fields_ = [("overflow", ctypes.c_uint32), ("accum_steps", ctypes.c_int32),
                 ("sumsq", ctypes.c_double), ("norm", ctypes.c_float),
                 ("clip_coef", ctypes.c_float), ("grad_scale", ctypes.c_float),
-                ("scale_used", ctypes.c_float)]
+                ("scale_used", ctypes.c_float), ("step_size", ctypes.c_float),
+                ("bc2_sqrt", ctypes.c_float), ("decay", ctypes.c_float),
+                ("one_minus_beta1", ctypes.c_float), ("one_minus_beta2", ctypes.c_float),
+                ("reserved", ctypes.c_uint32 * 3)]
 
 
 assert ctypes.sizeof(StepState) == STATE_BYTES and ctypes.sizeof(StepScalars) == SCALARS_BYTES
