@@ -220,6 +220,17 @@ def run_cpu_baseline(w, sample, repeats, min_seconds=10.0):
     return dict(value=n * done / dt, seconds=dt, n=n, repeats=done)
 
 
+def _traffic(workload, n):
+    """HBM bytes per launch of the Adam kernel from the committed rocprofv3
+    counter summary of this workload (FETCH_SIZE and WRITE_SIZE, each scaled
+    by a copy of known size), or None when there is none or the kernel's
+    sources changed since it was taken."""
+    from zero_sharded_mixed_tensor_amd.profiling import traffic_from_summary
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
+                        "%s_step_hbm_counters.md" % workload)
+    return traffic_from_summary(path, "adam_quad_kernel")
+
+
 def main():
     args = _parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -265,7 +276,7 @@ def main():
             "unit": "GB/s",
             "frac": round(r["adam_gbs"] / HBM_PEAK_GBS, 4),
             "bytes_per_param": r["adam_bytes_per_param"],
-            "traffic": None,
+            "traffic": _traffic(args.workload, r["n"]),
         },
     }
     if args.copy_calibration:
