@@ -228,7 +228,7 @@ def _traffic(workload, n):
     from zero_sharded_mixed_tensor_amd.profiling import traffic_from_summary
     path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
                         "%s_step_hbm_counters.md" % workload)
-    return traffic_from_summary(path, "adam_quad_kernel")
+    return traffic_from_summary(path, "adam_tile_kernel")
 
 
 def main():
