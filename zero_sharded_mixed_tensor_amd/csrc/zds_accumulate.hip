@@ -7,11 +7,13 @@
 // here in one launch over the plan's device-side tensor table.
 //
 // Work is cut into chunks of kAccumChunk elements that never straddle two
-// table entries; chunk c belongs to the entry e with chunk0[e] <= c <
-// chunk0[e+1], found by a binary search on uniform (scalar) loads. Inside a
-// chunk each thread moves groups of 8 elements with 16-byte accesses when the
-// source and destination of the entry are 16-byte aligned, else element by
-// element. Bytes per element: copy 2+2, overwrite 2+4, accumulate 2+4+4.
+// table entries; the plan's table maps every chunk to its entry, so a block
+// finds its piece with a few uniform (scalar) loads. Copy mode moves 8
+// elements per lane (16-byte accesses); the fp32 modes move quads (8-byte
+// 16-bit loads, 16-byte fp32 accesses), lane l on quad l of a wave's range so
+// each wave-level access is contiguous. Unaligned entries fall back to
+// element-wise moves. Bytes per element: copy 2+2, overwrite 2+4,
+// accumulate 2+4+4. One block per chunk by default.
 #include "zds_device.h"
 #include "zds_internal.h"
 
@@ -20,6 +22,11 @@
 #endif
 #ifndef ZDS_ACC_WAVES_PER_CU
 #define ZDS_ACC_WAVES_PER_CU 32
+#endif
+// 1: one block per chunk; 0: at most ZDS_ACC_WAVES_PER_CU waves per CU
+// striding over the chunks.
+#ifndef ZDS_ACC_ONESHOT
+#define ZDS_ACC_ONESHOT 1
 #endif
 
 namespace zds {
@@ -32,15 +39,6 @@ struct AccArgs {
   void *dst;
 };
 
-__device__ __forceinline__ int find_entry(const int64_t *chunk0, int32_t E, int64_t c) {
-  int lo = 0, hi = E;  // chunk0[lo] <= c < chunk0[hi]
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (chunk0[mid] <= c) lo = mid; else hi = mid;
-  }
-  return lo;
-}
-
 // MODE: ZDS_COPY (16-bit -> same 16-bit), ZDS_OVERWRITE / ZDS_ACCUMULATE
 // (SD -> fp32).
 template <int SD, int MODE>
@@ -50,8 +48,9 @@ __global__ void __launch_bounds__(ZDS_ACC_BLOCK) accumulate_kernel(AccArgs a) {
   const int64_t *len = a.table + E;
   const int64_t *dsto = a.table + 2 * E;
   const int64_t *chunk0 = a.table + 3 * E;
+  const int64_t *chunk_entry = a.table + 4 * E + 1;
   for (int64_t c = blockIdx.x; c < a.total_chunks; c += gridDim.x) {
-    const int e = find_entry(chunk0, E, c);
+    const int64_t e = chunk_entry[c];
     const int64_t local = (c - chunk0[e]) * kAccumChunk;
     const int64_t rem = len[e] - local;
     const int64_t cnt = rem < kAccumChunk ? rem : kAccumChunk;
@@ -70,20 +69,20 @@ __global__ void __launch_bounds__(ZDS_ACC_BLOCK) accumulate_kernel(AccArgs a) {
       }
     } else {
       float *dst = static_cast<float *>(a.dst) + d0;
-      if (aligned(src, 16) && aligned(dst, 16)) {
-        const int64_t groups = cnt >> 3;
-        for (int64_t i = threadIdx.x; i < groups; i += ZDS_ACC_BLOCK) {
-          float x[8];
-          load8<SD>(src, i, x);
+      if (aligned(src, SD == ZDS_FP32 ? 16 : 8) && aligned(dst, 16)) {
+        const int64_t quads = cnt >> 2;
+        for (int64_t q = threadIdx.x; q < quads; q += ZDS_ACC_BLOCK) {
+          float x[4];
+          load_quad<SD>(src, q, x);
           if (MODE == ZDS_ACCUMULATE) {
-            float y[8];
-            load8f(dst, i, y);
+            float y[4];
+            load_quad<ZDS_FP32>(dst, q, y);
 #pragma unroll
-            for (int k = 0; k < 8; ++k) x[k] = y[k] + x[k];
+            for (int k = 0; k < 4; ++k) x[k] = y[k] + x[k];
           }
-          store8f(dst, i, x);
+          store_quad(dst, q, x);
         }
-        for (int64_t j = (groups << 3) + threadIdx.x; j < cnt; j += ZDS_ACC_BLOCK) {
+        for (int64_t j = (quads << 2) + threadIdx.x; j < cnt; j += ZDS_ACC_BLOCK) {
           const float x = widen1<SD>(src, j);
           dst[j] = MODE == ZDS_ACCUMULATE ? dst[j] + x : x;
         }
@@ -108,7 +107,8 @@ zds_status launch_accumulate(const PlanDev &p, const void *const *dev_ptrs, zds_
   if (p.num_entries == 0 || p.total_chunks == 0) return ZDS_OK;
   AccArgs a{p.table, p.num_entries, p.total_chunks, dev_ptrs, dst};
   int64_t grid = static_cast<int64_t>(device_cu_count()) * ZDS_ACC_WAVES_PER_CU * 64 / ZDS_ACC_BLOCK;
-  if (grid > p.total_chunks) grid = p.total_chunks;
+  if (ZDS_ACC_ONESHOT || grid > p.total_chunks) grid = p.total_chunks;
+  if (grid > 0x7fffffff) grid = 0x7fffffff;
   if (grid < 1) grid = 1;
   const int g = static_cast<int>(grid);
   if (mode == ZDS_COPY) {

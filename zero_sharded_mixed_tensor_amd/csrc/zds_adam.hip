@@ -91,31 +91,6 @@ __device__ __forceinline__ void adam_elem(float x, const ElemConsts &c, float &p
   p = p - c.step_size * (m / denom);
 }
 
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-
-template <int D>
-__device__ __forceinline__ void load_quad(const void *base, int64_t q, float (&x)[4]) {
-  if (D == ZDS_FP32) {
-    const f32x4 a = ld_stream(static_cast<const f32x4 *>(base) + q);
-    x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
-  } else {
-    const u32x2 w = ld_stream(static_cast<const u32x2 *>(base) + q);
-    x[0] = lo_of<D>(w.x); x[1] = hi_of<D>(w.x);
-    x[2] = lo_of<D>(w.y); x[3] = hi_of<D>(w.y);
-  }
-}
-
-__device__ __forceinline__ void store_quad(float *base, int64_t q, const float (&x)[4]) {
-  const f32x4 a = {x[0], x[1], x[2], x[3]};
-  st_stream(reinterpret_cast<f32x4 *>(base) + q, a);
-}
-
-template <int D>
-__device__ __forceinline__ void store_quad16(void *base, int64_t q, const float (&x)[4]) {
-  const u32x2 w = {pack2<D>(x[0], x[1]), pack2<D>(x[2], x[3])};
-  st_stream(static_cast<u32x2 *>(base) + q, w);
-}
-
 // Block id after the XCD remap: with G a multiple of 8, hardware block b
 // runs on XCD b % 8; it is given tile-block (b % 8) * (G / 8) + b / 8.
 __device__ __forceinline__ int64_t remapped_block() {

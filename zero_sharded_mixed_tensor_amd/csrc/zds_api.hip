@@ -176,14 +176,19 @@ extern "C" zds_status zds_plan_create(zds_plan **out, const int64_t *numel, int3
   p->num_entries = E;
   hipError_t he = hipGetDevice(&p->device);
   if (he != hipSuccess) { plan_free(p); return hip_fail(he, "zds_plan_create: hipGetDevice"); }
-  std::vector<int64_t> table(3 * static_cast<size_t>(E) + E + 1);
+  // device table: [start E][length E][dst E][first chunk E+1][entry of each chunk]
   int64_t chunks = 0;
+  for (int32_t i = 0; i < E; ++i) chunks += (e[4 * i + 2] + kAccumChunk - 1) / kAccumChunk;
+  std::vector<int64_t> table(4 * static_cast<size_t>(E) + 1 + static_cast<size_t>(chunks));
+  int64_t c = 0;
   for (int32_t i = 0; i < E; ++i) {
     table[i] = e[4 * i + 1];
     table[E + i] = e[4 * i + 2];
     table[2 * E + i] = e[4 * i + 3];
-    table[3 * E + i] = chunks;
-    chunks += (e[4 * i + 2] + kAccumChunk - 1) / kAccumChunk;
+    table[3 * E + i] = c;
+    const int64_t k = (e[4 * i + 2] + kAccumChunk - 1) / kAccumChunk;
+    for (int64_t j = 0; j < k; ++j) table[4 * static_cast<size_t>(E) + 1 + c + j] = i;
+    c += k;
   }
   table[4 * E] = chunks;
   p->total_chunks = chunks;

@@ -12,6 +12,7 @@ namespace zds {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 // 16-bit -> fp32, exact.
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
@@ -87,41 +88,42 @@ __device__ __forceinline__ void st_stream(T *p, T v) {
 #endif
 }
 
-// 8 consecutive elements of dtype D at 16-byte aligned address, as fp32.
+// 8 consecutive 16-bit elements (one 16-byte access) at group index `group`,
+// as fp32.
 template <int D>
 __device__ __forceinline__ void load8(const void *base, int64_t group, float (&x)[8]) {
+  static_assert(D != ZDS_FP32, "load8 is for 16-bit data");
+  const u32x4 w = ld_stream(static_cast<const u32x4 *>(base) + group);
+  x[0] = lo_of<D>(w.x); x[1] = hi_of<D>(w.x);
+  x[2] = lo_of<D>(w.y); x[3] = hi_of<D>(w.y);
+  x[4] = lo_of<D>(w.z); x[5] = hi_of<D>(w.z);
+  x[6] = lo_of<D>(w.w); x[7] = hi_of<D>(w.w);
+}
+
+// Quads: 4 consecutive elements per lane, one 16-byte access for fp32 and
+// one 8-byte access for 16-bit data; lane l of a wave takes quad base + l so
+// each wave-level access covers one contiguous range.
+template <int D>
+__device__ __forceinline__ void load_quad(const void *base, int64_t q, float (&x)[4]) {
   if (D == ZDS_FP32) {
-    const f32x4 *p = static_cast<const f32x4 *>(base) + 2 * group;
-    const f32x4 a = ld_stream(p);
-    const f32x4 b = ld_stream(p + 1);
+    const f32x4 a = ld_stream(static_cast<const f32x4 *>(base) + q);
     x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
-    x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
   } else {
-    const u32x4 w = ld_stream(static_cast<const u32x4 *>(base) + group);
+    const u32x2 w = ld_stream(static_cast<const u32x2 *>(base) + q);
     x[0] = lo_of<D>(w.x); x[1] = hi_of<D>(w.x);
     x[2] = lo_of<D>(w.y); x[3] = hi_of<D>(w.y);
-    x[4] = lo_of<D>(w.z); x[5] = hi_of<D>(w.z);
-    x[6] = lo_of<D>(w.w); x[7] = hi_of<D>(w.w);
   }
 }
 
-__device__ __forceinline__ void load8f(const float *base, int64_t group, float (&x)[8]) {
-  load8<ZDS_FP32>(base, group, x);
-}
-
-__device__ __forceinline__ void store8f(float *base, int64_t group, const float (&x)[8]) {
-  f32x4 *p = reinterpret_cast<f32x4 *>(base) + 2 * group;
+__device__ __forceinline__ void store_quad(float *base, int64_t q, const float (&x)[4]) {
   const f32x4 a = {x[0], x[1], x[2], x[3]};
-  const f32x4 b = {x[4], x[5], x[6], x[7]};
-  st_stream(p, a);
-  st_stream(p + 1, b);
+  st_stream(reinterpret_cast<f32x4 *>(base) + q, a);
 }
 
 template <int D>
-__device__ __forceinline__ void store8h(void *base, int64_t group, const float (&x)[8]) {
-  const u32x4 w = {pack2<D>(x[0], x[1]), pack2<D>(x[2], x[3]), pack2<D>(x[4], x[5]),
-                   pack2<D>(x[6], x[7])};
-  st_stream(static_cast<u32x4 *>(base) + group, w);
+__device__ __forceinline__ void store_quad16(void *base, int64_t q, const float (&x)[4]) {
+  const u32x2 w = {pack2<D>(x[0], x[1]), pack2<D>(x[2], x[3])};
+  st_stream(static_cast<u32x2 *>(base) + q, w);
 }
 
 }  // namespace zds

@@ -157,6 +157,9 @@ zds_status launch_scaler(zds_step_state *state, const zds_step_scalars *scalars,
 zds_status launch_state_init(zds_step_state *state, const zds_step_state &init, hipStream_t stream);
 
 // Chunk size (elements) of the accumulate kernel's work items.
-constexpr int64_t kAccumChunk = 16384;
+#ifndef ZDS_ACC_CHUNK
+#define ZDS_ACC_CHUNK 4096
+#endif
+constexpr int64_t kAccumChunk = ZDS_ACC_CHUNK;
 
 }  // namespace zds

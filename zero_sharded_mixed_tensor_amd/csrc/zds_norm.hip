@@ -84,7 +84,21 @@ __global__ void __launch_bounds__(ZDS_NORM_BLOCK) norm_stage1(const void *x, int
   const int64_t stride = static_cast<int64_t>(gridDim.x) * ZDS_NORM_BLOCK;
   const int64_t tid = static_cast<int64_t>(blockIdx.x) * ZDS_NORM_BLOCK + threadIdx.x;
   int64_t done = 0;
-  if (VEC) {
+  if constexpr (VEC && D == ZDS_FP32) {
+    // fp32: one 16-byte quad per lane, lane-contiguous
+    const int64_t quads = n >> 2;
+    for (int64_t i = tid; i < quads; i += stride) {
+      float v[4];
+      load_quad<D>(x, i, v);
+      acc0 = sq_acc<D>(v[0], acc0);
+      acc1 = sq_acc<D>(v[1], acc1);
+      acc0 = sq_acc<D>(v[2], acc0);
+      acc1 = sq_acc<D>(v[3], acc1);
+    }
+    done = quads << 2;
+    if (blockIdx.x == 0 && done + threadIdx.x < n) acc0 = sq_acc<D>(widen1<D>(x, done + threadIdx.x), acc0);
+  } else if constexpr (VEC) {
+    // 16-bit: 8 elements (16 bytes) per lane, lane-contiguous
     const int64_t groups = n >> 3;
     for (int64_t i = tid; i < groups; i += stride) {
       float v[8];
