@@ -108,7 +108,7 @@ zds_status launch_accumulate(const PlanDev &p, const void *const *dev_ptrs, zds_
   AccArgs a{p.table, p.num_entries, p.total_chunks, dev_ptrs, dst};
   int64_t grid = static_cast<int64_t>(device_cu_count()) * ZDS_ACC_WAVES_PER_CU * 64 / ZDS_ACC_BLOCK;
   if (ZDS_ACC_ONESHOT || grid > p.total_chunks) grid = p.total_chunks;
-  if (grid > 0x7fffffff) grid = 0x7fffffff;
+  if (grid > max_blocks(ZDS_ACC_BLOCK)) grid = max_blocks(ZDS_ACC_BLOCK);
   if (grid < 1) grid = 1;
   const int g = static_cast<int>(grid);
   if (mode == ZDS_COPY) {

@@ -156,6 +156,14 @@ zds_status launch_scaler(zds_step_state *state, const zds_step_scalars *scalars,
                          float beta2, hipStream_t stream);
 zds_status launch_state_init(zds_step_state *state, const zds_step_state &init, hipStream_t stream);
 
+// A dispatch packet counts work-items in 32 bits: a launch must stay below
+// 2^32 of them. Grids are capped here and the kernels loop over the rest.
+constexpr int64_t max_blocks(int threads_per_block) {
+  return ((int64_t(1) << 32) - 1) / threads_per_block < (int64_t(1) << 23)
+             ? ((int64_t(1) << 32) - 1) / threads_per_block
+             : (int64_t(1) << 23);
+}
+
 // Chunk size (elements) of the accumulate kernel's work items.
 #ifndef ZDS_ACC_CHUNK
 #define ZDS_ACC_CHUNK 4096
