@@ -2,8 +2,9 @@
 on one MI355X.
 
 A step is one pass of the whole hot path over the rank's shard:
-  zds_grad_accumulate (copy the per-tensor grads into the flat bucket),
-  zds_overflow_and_norm, zds_adam_step, zds_loss_scaler_update.
+  zds_grad_accumulate_norm (copy the per-tensor grads into the flat bucket,
+  with the overflow/norm pass fused in; --unfused runs zds_grad_accumulate
+  and zds_overflow_and_norm instead), zds_adam_step, zds_loss_scaler_update.
 Default workload: the Llama-7B-shaped Stage-1 shard at N = 8 (rank 0: 33
 table entries, 842,301,440 params), bf16 grads N(0, 2e-3), fp32 master
 N(0, 0.02), moments shaped like one prior step, static loss scale 1, clip
@@ -34,6 +35,9 @@ def _parse():
     ap.add_argument("--workload", default="llama7b_s1",
                     choices=["llama7b_s1", "llama7b_s1_accum16", "llama7b_whole_1024", "llama65b_s1", "tiny"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--unfused", action="store_true",
+                    help="separate overflow/norm pass instead of the one fused into the last "
+                         "flatten/accumulate call")
     ap.add_argument("--cpu-sample", type=int, default=1 << 24, help="oracle sample size (params)")
     ap.add_argument("--cpu-repeats", type=int, default=2, help="minimum oracle passes over the sample")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -62,13 +66,15 @@ def _workload(name):
                 accum=1, scale=16, prior=False, mode="copy")
 
 
-def _bytes_per_param(w):
-    """Algorithmic HBM bytes per param of each kernel of one step."""
+def _bytes_per_param(w, fused):
+    """Algorithmic HBM bytes per param of each kernel of one step. Fused, the
+    norm reads nothing extra: it is formed from the values the last
+    flatten/accumulate call stores."""
     g = 2
     if w["mode"] == "accumulate":
         acc = 6 + 10 * (w["accum"] - 1)      # overwrite once, then accumulate
-        return dict(accumulate=acc / w["accum"], accum_total=acc, norm=4, adam=30)
-    return dict(accumulate=2 * g, accum_total=2 * g, norm=g, adam=28)
+        return dict(accum_total=acc, norm=0 if fused else 4, adam=30)
+    return dict(accum_total=2 * g, norm=0 if fused else g, adam=28)
 
 
 # ------------------------------------------------------------------ GPU part
@@ -122,6 +128,8 @@ def run_gpu(args, w):
            else zds.scaler_config(initial_scale_power=w["scale"], window=1000, hysteresis=1))
     st = ShardStep(n, zds.hparams(), cfg, max_norm=1.0, accum_steps=w["accum"], t0=t0,
                    beta1_pow0=b1p, beta2_pow0=b2p)
+    fused = not args.unfused
+    pws = zds.new_plan_workspace(plan)
     torch.cuda.synchronize()
 
     ev = {k: [] for k in ("accumulate", "norm", "adam", "scaler")}
@@ -132,13 +140,16 @@ def run_gpu(args, w):
             e.record()
             return e
         e0 = mark() if record else None
-        if w["mode"] == "accumulate":
-            for k in range(w["accum"]):
-                zds.zds_grad_accumulate(plan, srcs, bucket, zds.ZDS_OVERWRITE if k == 0 else zds.ZDS_ACCUMULATE)
-        else:
-            zds.zds_grad_accumulate(plan, srcs, bucket, zds.ZDS_COPY)
+        modes = ([zds.ZDS_OVERWRITE] + [zds.ZDS_ACCUMULATE] * (w["accum"] - 1)
+                 if w["mode"] == "accumulate" else [zds.ZDS_COPY])
+        for k, md in enumerate(modes):
+            if fused and k == len(modes) - 1:
+                st.accumulate_norm(plan, srcs, bucket, md, pws)
+            else:
+                zds.zds_grad_accumulate(plan, srcs, bucket, md)
         e1 = mark() if record else None
-        st.norm(bucket)
+        if not fused:
+            st.norm(bucket)
         e2 = mark() if record else None
         st.adam(bucket, master, m, v, p16)
         e3 = mark() if record else None
@@ -163,13 +174,17 @@ def run_gpu(args, w):
     if sc.overflow or state.steps_skipped:
         raise SystemExit("unexpected overflow in the benchmark workload")
 
-    bpp = _bytes_per_param(w)
+    bpp = _bytes_per_param(w, fused)
     kern = {}
     for k, pairs in ev.items():
+        if k == "norm" and fused:
+            continue
         ms = sum(a.elapsed_time(b) for a, b in pairs) / len(pairs)
         entry = {"ms_avg": round(ms, 5)}
         if k == "accumulate":
             entry["gbs"] = round(bpp["accum_total"] * n / (ms * 1e-3) / 1e9, 1)
+            if fused:
+                entry["includes"] = "overflow/norm fused into the last call"
         elif k in ("norm", "adam"):
             entry["gbs"] = round(bpp[k] * n / (ms * 1e-3) / 1e9, 1)
         kern[k] = entry
@@ -177,7 +192,7 @@ def run_gpu(args, w):
     achieved = 28.0 * n / (adam_ms * 1e-3) / 1e9 if w["mode"] != "accumulate" else 30.0 * n / (adam_ms * 1e-3) / 1e9
     step_bytes = (bpp["accum_total"] + bpp["norm"] + bpp["adam"]) * n
     ms_per_step = elapsed / args.steps * 1e3
-    return dict(n=n, entries=len(ents), elapsed=elapsed, ms_per_step=ms_per_step, kernels=kern,
+    return dict(n=n, entries=len(ents), elapsed=elapsed, ms_per_step=ms_per_step, kernels=kern, fused=fused,
                 adam_gbs=achieved, step_gbs=step_bytes / (elapsed / args.steps) / 1e9,
                 step_bytes_per_param=bpp["accum_total"] + bpp["norm"] + bpp["adam"],
                 adam_bytes_per_param=28 if w["mode"] != "accumulate" else 30)
@@ -264,6 +279,7 @@ def main():
             "loss_scale": "static 1" if w["scale"] is None else "dynamic 2^%d" % w["scale"],
             "clip": 1.0,
             "step_bytes_per_param": r["step_bytes_per_param"],
+            "norm_fused_into_flatten": r["fused"],
         },
         "step_gbs": round(r["step_gbs"], 1),
         "step_hbm_frac": round(r["step_gbs"] / HBM_PEAK_GBS, 4),

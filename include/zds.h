@@ -188,6 +188,24 @@ zds_status zds_plan_entry(const zds_plan *plan, int32_t e, int64_t *out4);
 zds_status zds_grad_accumulate(zds_plan *plan, const void *const *src_ptrs, zds_dtype src_dtype,
                                void *dst, zds_dtype dst_dtype, zds_accum_mode mode, void *stream);
 
+/* Rows a1 + a2 fused, for the micro-batch that completes the step's grads:
+ * the same as zds_grad_accumulate followed by zds_overflow_and_norm over
+ * dst (dst_dtype, hi - lo elements), except that the sum of squares is
+ * formed from the values as the kernel stores them, so the flat buffer is
+ * not read a second time. Padding elements of dst between tensors are not
+ * visited and must be zero (as they stay when the buffer was zeroed once).
+ * The sum is accumulated in float64 per block in a fixed order, then the
+ * block partials in index order, so it is run-to-run identical for the plan;
+ * it may differ from zds_overflow_and_norm's sum of the same data in the
+ * last bits (another order). Arguments as for the two calls; ws holds at
+ * least zds_plan_norm_workspace_bytes(plan) bytes. */
+size_t zds_plan_norm_workspace_bytes(const zds_plan *plan);
+zds_status zds_grad_accumulate_norm(zds_plan *plan, const void *const *src_ptrs, zds_dtype src_dtype,
+                                    void *dst, zds_dtype dst_dtype, zds_accum_mode mode,
+                                    int32_t accum_steps, float max_norm,
+                                    const zds_step_state *state_dev, zds_step_scalars *out_dev,
+                                    void *ws, size_t ws_bytes, void *stream);
+
 /* Row a2. Size in bytes of the workspace zds_overflow_and_norm needs for n
  * elements. */
 size_t zds_workspace_bytes(int64_t n);

@@ -16,6 +16,8 @@ that hold at any size.
   oracle derives the clip scalars itself and the GPU's grad_scale must equal
   them.
 * Flags, skips and the loss-scale trajectory are compared exactly.
+The Stage-1 shards run the bench's step (the norm fused into the flatten or
+the last accumulate call); the whole-7B run uses the separate norm pass.
 """
 
 import sys
@@ -144,8 +146,10 @@ def test_llama7b_stage1_shard_bf16():
                    t0=1, beta1_pow0=B1, beta2_pow0=B2)
     idx = _sample_index(n, ents)
     P0, M0, V0 = master[idx].cpu().numpy(), m[idx].cpu().numpy(), v[idx].cpu().numpy()
-    zds.zds_grad_accumulate(plan, srcs, bucket, zds.ZDS_COPY)
-    st.step(bucket, master, m, v, out)
+    # the bench's step: flatten with the norm fused in, then Adam and the scaler
+    st.accumulate_norm(plan, srcs, bucket, zds.ZDS_COPY, zds.new_plan_workspace(plan))
+    st.adam(bucket, master, m, v, out)
+    st.scaler()
     torch.cuda.synchronize()
     _check_copy(bucket, srcs, ents)
     g_host = _h16(bucket)
@@ -169,8 +173,11 @@ def test_llama7b_stage1_shard_accumulate16():
     numels, plan, ents, n, srcs, master, m, v = _setup_shard(llama_7b_tensors(), 8, 0, "fp16", 1e-3, True, 31)
     acc = torch.empty(n, dtype=torch.float32, device="cuda")
     out = torch.empty(n, dtype=torch.float16, device="cuda")
+    st = ShardStep(n, zds.hparams(), zds.scaler_config(initial_scale_power=14), max_norm=1.0, accum_steps=16,
+                   t0=1, beta1_pow0=B1, beta2_pow0=B2)
     idx = _sample_index(n, ents)
     idx_h = idx.cpu().numpy()
+    P0, M0, V0 = master[idx].cpu().numpy(), m[idx].cpu().numpy(), v[idx].cpu().numpy()
     # flat index -> (tensor, offset) for gathering the sampled sources
     owner = np.empty(len(idx_h), np.int64)
     off = np.empty(len(idx_h), np.int64)
@@ -186,13 +193,14 @@ def test_llama7b_stage1_shard_accumulate16():
             sel = owner == t
             xs[sel] = _h16(srcs[t][torch.from_numpy(off[sel]).cuda()])
         wacc = wacc + O.widen(xs, "fp16") if k else O.widen(xs, "fp16").copy()
-        zds.zds_grad_accumulate(plan, srcs, acc, zds.ZDS_OVERWRITE if k == 0 else zds.ZDS_ACCUMULATE)
+        if k < 15:
+            zds.zds_grad_accumulate(plan, srcs, acc, zds.ZDS_OVERWRITE if k == 0 else zds.ZDS_ACCUMULATE)
+        else:  # the last micro-batch with the norm fused in, as the bench runs it
+            st.accumulate_norm(plan, srcs, acc, zds.ZDS_ACCUMULATE, zds.new_plan_workspace(plan))
     torch.cuda.synchronize()
     assert (acc[idx].cpu().numpy().view(np.uint32) == wacc.view(np.uint32)).all()
-    P0, M0, V0 = master[idx].cpu().numpy(), m[idx].cpu().numpy(), v[idx].cpu().numpy()
-    st = ShardStep(n, zds.hparams(), zds.scaler_config(initial_scale_power=14), max_norm=1.0, accum_steps=16,
-                   t0=1, beta1_pow0=B1, beta2_pow0=B2)
-    st.step(acc, master, m, v, out)
+    st.adam(acc, master, m, v, out)
+    st.scaler()
     torch.cuda.synchronize()
     acc_h = acc.cpu().numpy()
     osc = _oracle_scalars(O.sum_of_squares(acc_h, "fp32"), 2.0 ** 14, 16, 1.0, O.overflow_flag(acc_h, "fp32"))
@@ -274,8 +282,9 @@ def test_llama65b_stage1_shard_bf16():
                    t0=1, beta1_pow0=B1, beta2_pow0=B2)
     idx = _sample_index(n, ents)
     P0, M0, V0 = master[idx].cpu().numpy(), m[idx].cpu().numpy(), v[idx].cpu().numpy()
-    zds.zds_grad_accumulate(plan, srcs, bucket, zds.ZDS_COPY)
-    st.step(bucket, master, m, v, out)
+    st.accumulate_norm(plan, srcs, bucket, zds.ZDS_COPY, zds.new_plan_workspace(plan))
+    st.adam(bucket, master, m, v, out)
+    st.scaler()
     ssum = _torch_sumsq(bucket)
     torch.cuda.synchronize()
     _check_copy(bucket, srcs, ents)

@@ -347,3 +347,77 @@ def test_cast_all_fp32_exponents():
         assert (P.view(np.uint32) == p.view(np.uint32)).all()
         want = O.narrow(p, pdt)
         assert (OUT == want).all(), pdt
+
+
+@pytest.mark.parametrize("mode", ["copy", "overwrite", "accumulate"])
+@pytest.mark.parametrize("dtype", ["fp16", "bf16"])
+@pytest.mark.parametrize("T,align,world,misalign", [(7, 64, 3, False), (33, 8, 4, True), (200, 64, 8, False)])
+def test_accumulate_norm_fused_parity(mode, dtype, T, align, world, misalign):
+    """zds_grad_accumulate_norm: the stored values equal the oracle's
+    flatten/accumulate, and the scalars equal the oracle's overflow and norm
+    of that flat buffer (padding zero)."""
+    say("fused accumulate+norm mode=%s dtype=%s T=%d" % (mode, dtype, T))
+    rng = np.random.default_rng(T * 7 + align + world)
+    numels, srcs_np, srcs_dev = _make_table(rng, T, dtype, misalign)
+    _, total = O.flat_layout(numels, align)
+    for rank in sorted({0, world - 1}):
+        lo, hi = O.shard_range(total, world, rank, align)
+        ent = O.shard_entries(numels, align, lo, hi)
+        L = hi - lo
+        plan = zds.zds_plan_create(numels, align, lo, hi)
+        st = ShardStep(max(L, 1), zds.hparams(), zds.scaler_config(initial_scale_power=12), max_norm=1.0,
+                       accum_steps=2)
+        ws = zds.new_plan_workspace(plan)
+        if mode == "copy":
+            dst = to_dev(np.zeros(L, np.uint16), dtype)
+            zds.zds_grad_accumulate_norm(plan, srcs_dev, dst, zds.ZDS_COPY, 2, 1.0, st.state, st.scalars, ws)
+            want = O.flatten_copy(srcs_np, ent, np.zeros(L, np.uint16))
+            wdt = dtype
+        else:
+            dst = torch.zeros(L, dtype=torch.float32, device="cuda")
+            want = np.zeros(L, np.float32)
+            if mode == "accumulate":
+                zds.zds_grad_accumulate(plan, srcs_dev, dst, zds.ZDS_OVERWRITE)
+                O.flatten_accumulate(srcs_np, dtype, ent, want, overwrite=True)
+            m = zds.ZDS_OVERWRITE if mode == "overwrite" else zds.ZDS_ACCUMULATE
+            zds.zds_grad_accumulate_norm(plan, srcs_dev, dst, m, 2, 1.0, st.state, st.scalars, ws)
+            O.flatten_accumulate(srcs_np, dtype, ent, want, overwrite=(mode == "overwrite"))
+            wdt = "fp32"
+        torch.cuda.synchronize()
+        got = to_host(dst)
+        assert (got.view(np.uint32 if wdt == "fp32" else np.uint16) ==
+                want.view(np.uint32 if wdt == "fp32" else np.uint16)).all()
+        sc = st.read_scalars()
+        r = O.overflow_and_norm(want, wdt, 2.0 ** 12, 2, 1.0)
+        assert sc.overflow == r["overflow"] == 0
+        if L:
+            assert abs(sc.sumsq - r["sumsq"]) <= 1e-12 * max(r["sumsq"], 1e-300)
+            assert sc.grad_scale == r["grad_scale"]
+        plan.close()
+
+
+@pytest.mark.parametrize("bad", [np.inf, np.nan])
+def test_accumulate_norm_fused_overflow(bad):
+    say("fused accumulate+norm overflow %r" % bad)
+    rng = np.random.default_rng(5)
+    numels, srcs_np, srcs_dev = _make_table(rng, 9, "fp16")
+    t = 4
+    srcs_np[t][numels[t] // 2] = np.array([bad], np.float16).view(np.uint16)[0]
+    srcs_dev[t] = to_dev(srcs_np[t], "fp16")
+    _, total = O.flat_layout(numels, 64)
+    plan = zds.zds_plan_create(numels, 64, 0, total)
+    st = ShardStep(total, zds.hparams(), zds.scaler_config(initial_scale_power=12), max_norm=1.0)
+    ws = zds.new_plan_workspace(plan)
+    dst = torch.zeros(total, dtype=torch.float16, device="cuda")
+    zds.zds_grad_accumulate_norm(plan, srcs_dev, dst, zds.ZDS_COPY, 1, 1.0, st.state, st.scalars, ws)
+    torch.cuda.synchronize()
+    assert st.read_scalars().overflow == 1
+    # an empty range (all padding) still writes the scalars of an empty shard
+    plan0 = zds.zds_plan_create([5], 64, 32, 64)
+    assert plan0.num_entries == 0
+    st0 = ShardStep(32, zds.hparams(), zds.scaler_config(initial_scale_power=0), max_norm=1.0)
+    zds.zds_grad_accumulate_norm(plan0, [srcs_dev[0]], torch.zeros(32, dtype=torch.float16, device="cuda"),
+                                 zds.ZDS_COPY, 1, 1.0, st0.state, st0.scalars, zds.new_plan_workspace(plan0))
+    torch.cuda.synchronize()
+    s0 = st0.read_scalars()
+    assert s0.overflow == 0 and s0.sumsq == 0.0 and s0.grad_scale == 1.0

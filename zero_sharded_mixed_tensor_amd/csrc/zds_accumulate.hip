@@ -37,12 +37,19 @@ struct AccArgs {
   int64_t total_chunks;
   const void *const *ptrs;
   void *dst;
+  double *partials;  // NORM: one sum of squares per block
 };
+
+__device__ __forceinline__ double sq_add(float x, double acc) {
+  const double d = static_cast<double>(x);
+  return fma(d, d, acc);  // x^2 is exact in float64
+}
 
 // MODE: ZDS_COPY (16-bit -> same 16-bit), ZDS_OVERWRITE / ZDS_ACCUMULATE
 // (SD -> fp32).
-template <int SD, int MODE>
+template <int SD, int MODE, bool NORM>
 __global__ void __launch_bounds__(ZDS_ACC_BLOCK) accumulate_kernel(AccArgs a) {
+  double ss = 0.0;
   const int32_t E = a.num_entries;
   const int64_t *start = a.table;
   const int64_t *len = a.table + E;
@@ -61,11 +68,25 @@ __global__ void __launch_bounds__(ZDS_ACC_BLOCK) accumulate_kernel(AccArgs a) {
       const uint16_t *s = reinterpret_cast<const uint16_t *>(src);
       if (aligned(s, 16) && aligned(dst, 16)) {
         const int64_t groups = cnt >> 3;
-        for (int64_t i = threadIdx.x; i < groups; i += ZDS_ACC_BLOCK)
-          st_stream(reinterpret_cast<u32x4 *>(dst) + i, ld_stream(reinterpret_cast<const u32x4 *>(s) + i));
-        for (int64_t j = (groups << 3) + threadIdx.x; j < cnt; j += ZDS_ACC_BLOCK) dst[j] = s[j];
+        for (int64_t i = threadIdx.x; i < groups; i += ZDS_ACC_BLOCK) {
+          const u32x4 w = ld_stream(reinterpret_cast<const u32x4 *>(s) + i);
+          st_stream(reinterpret_cast<u32x4 *>(dst) + i, w);
+          if (NORM) {
+            ss = sq_add(lo_of<SD>(w.x), ss); ss = sq_add(hi_of<SD>(w.x), ss);
+            ss = sq_add(lo_of<SD>(w.y), ss); ss = sq_add(hi_of<SD>(w.y), ss);
+            ss = sq_add(lo_of<SD>(w.z), ss); ss = sq_add(hi_of<SD>(w.z), ss);
+            ss = sq_add(lo_of<SD>(w.w), ss); ss = sq_add(hi_of<SD>(w.w), ss);
+          }
+        }
+        for (int64_t j = (groups << 3) + threadIdx.x; j < cnt; j += ZDS_ACC_BLOCK) {
+          dst[j] = s[j];
+          if (NORM) ss = sq_add(widen1<SD>(s, j), ss);
+        }
       } else {
-        for (int64_t j = threadIdx.x; j < cnt; j += ZDS_ACC_BLOCK) dst[j] = s[j];
+        for (int64_t j = threadIdx.x; j < cnt; j += ZDS_ACC_BLOCK) {
+          dst[j] = s[j];
+          if (NORM) ss = sq_add(widen1<SD>(s, j), ss);
+        }
       }
     } else {
       float *dst = static_cast<float *>(a.dst) + d0;
@@ -81,49 +102,79 @@ __global__ void __launch_bounds__(ZDS_ACC_BLOCK) accumulate_kernel(AccArgs a) {
             for (int k = 0; k < 4; ++k) x[k] = y[k] + x[k];
           }
           store_quad(dst, q, x);
+          if (NORM) {
+#pragma unroll
+            for (int k = 0; k < 4; ++k) ss = sq_add(x[k], ss);
+          }
         }
         for (int64_t j = (quads << 2) + threadIdx.x; j < cnt; j += ZDS_ACC_BLOCK) {
           const float x = widen1<SD>(src, j);
-          dst[j] = MODE == ZDS_ACCUMULATE ? dst[j] + x : x;
+          const float r = MODE == ZDS_ACCUMULATE ? dst[j] + x : x;
+          dst[j] = r;
+          if (NORM) ss = sq_add(r, ss);
         }
       } else {
         for (int64_t j = threadIdx.x; j < cnt; j += ZDS_ACC_BLOCK) {
           const float x = widen1<SD>(src, j);
-          dst[j] = MODE == ZDS_ACCUMULATE ? dst[j] + x : x;
+          const float r = MODE == ZDS_ACCUMULATE ? dst[j] + x : x;
+          dst[j] = r;
+          if (NORM) ss = sq_add(r, ss);
         }
       }
     }
   }
+  if (NORM) {
+    const double b = block_sum<ZDS_ACC_BLOCK>(ss);
+    if (threadIdx.x == 0) a.partials[blockIdx.x] = b;
+  }
 }
 
-template <int SD, int MODE>
-static void go(int grid, hipStream_t s, const AccArgs &a) {
-  hipLaunchKernelGGL((accumulate_kernel<SD, MODE>), dim3(grid), dim3(ZDS_ACC_BLOCK), 0, s, a);
+template <int SD, int MODE, bool NORM>
+static void go(int64_t grid, hipStream_t s, const AccArgs &a) {
+  hipLaunchKernelGGL((accumulate_kernel<SD, MODE, NORM>), dim3(static_cast<uint32_t>(grid)), dim3(ZDS_ACC_BLOCK),
+                     0, s, a);
+}
+
+int64_t accumulate_grid(int64_t total_chunks) {
+  int64_t grid = static_cast<int64_t>(device_cu_count()) * ZDS_ACC_WAVES_PER_CU * 64 / ZDS_ACC_BLOCK;
+  if (ZDS_ACC_ONESHOT || grid > total_chunks) grid = total_chunks;
+  if (grid > max_blocks(ZDS_ACC_BLOCK)) grid = max_blocks(ZDS_ACC_BLOCK);
+  if (grid < 1) grid = 1;
+  return grid;
+}
+
+template <bool NORM>
+static zds_status dispatch(const PlanDev &p, const void *const *dev_ptrs, zds_dtype src, void *dst,
+                           zds_accum_mode mode, double *partials, hipStream_t stream) {
+  AccArgs a{p.table, p.num_entries, p.total_chunks, dev_ptrs, dst, partials};
+  const int64_t g = accumulate_grid(p.total_chunks);
+  if (mode == ZDS_COPY) {
+    // fp16 and bf16 copies move the same bits; the squares need the type
+    if (src == ZDS_BF16) go<ZDS_BF16, ZDS_COPY, NORM>(g, stream, a);
+    else go<ZDS_FP16, ZDS_COPY, NORM>(g, stream, a);
+  } else if (mode == ZDS_OVERWRITE) {
+    if (src == ZDS_FP16) go<ZDS_FP16, ZDS_OVERWRITE, NORM>(g, stream, a);
+    else if (src == ZDS_BF16) go<ZDS_BF16, ZDS_OVERWRITE, NORM>(g, stream, a);
+    else go<ZDS_FP32, ZDS_OVERWRITE, NORM>(g, stream, a);
+  } else {
+    if (src == ZDS_FP16) go<ZDS_FP16, ZDS_ACCUMULATE, NORM>(g, stream, a);
+    else if (src == ZDS_BF16) go<ZDS_BF16, ZDS_ACCUMULATE, NORM>(g, stream, a);
+    else go<ZDS_FP32, ZDS_ACCUMULATE, NORM>(g, stream, a);
+  }
+  return check_launch(NORM ? "grad_accumulate_norm kernel" : "grad_accumulate kernel");
 }
 
 zds_status launch_accumulate(const PlanDev &p, const void *const *dev_ptrs, zds_dtype src,
                              void *dst, zds_dtype /*dst_dtype*/, zds_accum_mode mode,
                              hipStream_t stream) {
   if (p.num_entries == 0 || p.total_chunks == 0) return ZDS_OK;
-  AccArgs a{p.table, p.num_entries, p.total_chunks, dev_ptrs, dst};
-  int64_t grid = static_cast<int64_t>(device_cu_count()) * ZDS_ACC_WAVES_PER_CU * 64 / ZDS_ACC_BLOCK;
-  if (ZDS_ACC_ONESHOT || grid > p.total_chunks) grid = p.total_chunks;
-  if (grid > max_blocks(ZDS_ACC_BLOCK)) grid = max_blocks(ZDS_ACC_BLOCK);
-  if (grid < 1) grid = 1;
-  const int g = static_cast<int>(grid);
-  if (mode == ZDS_COPY) {
-    // fp16 and bf16 copies move the same bits
-    go<ZDS_FP16, ZDS_COPY>(g, stream, a);
-  } else if (mode == ZDS_OVERWRITE) {
-    if (src == ZDS_FP16) go<ZDS_FP16, ZDS_OVERWRITE>(g, stream, a);
-    else if (src == ZDS_BF16) go<ZDS_BF16, ZDS_OVERWRITE>(g, stream, a);
-    else go<ZDS_FP32, ZDS_OVERWRITE>(g, stream, a);
-  } else {
-    if (src == ZDS_FP16) go<ZDS_FP16, ZDS_ACCUMULATE>(g, stream, a);
-    else if (src == ZDS_BF16) go<ZDS_BF16, ZDS_ACCUMULATE>(g, stream, a);
-    else go<ZDS_FP32, ZDS_ACCUMULATE>(g, stream, a);
-  }
-  return check_launch("grad_accumulate kernel");
+  return dispatch<false>(p, dev_ptrs, src, dst, mode, nullptr, stream);
+}
+
+zds_status launch_accumulate_norm(const PlanDev &p, const void *const *dev_ptrs, zds_dtype src,
+                                  void *dst, zds_dtype /*dst_dtype*/, zds_accum_mode mode,
+                                  double *partials, hipStream_t stream) {
+  return dispatch<true>(p, dev_ptrs, src, dst, mode, partials, stream);
 }
 
 }  // namespace zds

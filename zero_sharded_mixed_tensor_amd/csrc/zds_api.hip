@@ -231,60 +231,100 @@ extern "C" zds_status zds_plan_entry(const zds_plan *plan, int32_t e, int64_t *o
 // Hot calls
 // ---------------------------------------------------------------------------
 
-extern "C" zds_status zds_grad_accumulate(zds_plan *plan, const void *const *src_ptrs,
-                                          zds_dtype src_dtype, void *dst, zds_dtype dst_dtype,
-                                          zds_accum_mode mode, void *stream) {
-  clear_error();
-  if (!plan) return fail(ZDS_EINVAL, "zds_grad_accumulate: null plan");
-  if (!valid_dtype(src_dtype) || !valid_dtype(dst_dtype))
-    return fail(ZDS_EINVAL, "zds_grad_accumulate: bad dtype");
+// Checks, staging of the per-call source pointers, and the launch shared by
+// zds_grad_accumulate and zds_grad_accumulate_norm. With partials != null the
+// kernel also writes one sum of squares per block.
+static zds_status accumulate_impl(const char *fn, zds_plan *plan, const void *const *src_ptrs,
+                                  zds_dtype src_dtype, void *dst, zds_dtype dst_dtype, zds_accum_mode mode,
+                                  double *partials, void *stream) {
+  if (!plan) return fail(ZDS_EINVAL, "%s: null plan", fn);
+  if (!valid_dtype(src_dtype) || !valid_dtype(dst_dtype)) return fail(ZDS_EINVAL, "%s: bad dtype", fn);
   if (mode == ZDS_COPY) {
     if (src_dtype == ZDS_FP32 || dst_dtype != src_dtype)
-      return fail(ZDS_EINVAL, "zds_grad_accumulate: copy mode needs the same 16-bit dtype on both sides");
+      return fail(ZDS_EINVAL, "%s: copy mode needs the same 16-bit dtype on both sides", fn);
   } else if (mode == ZDS_OVERWRITE || mode == ZDS_ACCUMULATE) {
-    if (dst_dtype != ZDS_FP32) return fail(ZDS_EINVAL, "zds_grad_accumulate: accumulator must be fp32");
+    if (dst_dtype != ZDS_FP32) return fail(ZDS_EINVAL, "%s: accumulator must be fp32", fn);
   } else {
-    return fail(ZDS_EINVAL, "zds_grad_accumulate: bad mode %d", static_cast<int>(mode));
+    return fail(ZDS_EINVAL, "%s: bad mode %d", fn, static_cast<int>(mode));
   }
   const int32_t E = plan->num_entries;
-  if (E == 0) return ZDS_OK;
-  if (!src_ptrs || !dst) return fail(ZDS_EINVAL, "zds_grad_accumulate: null src_ptrs or dst");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  PlanDev pd{plan->d_table, E, plan->total_chunks};
+  if (E == 0) {
+    if (!partials) return ZDS_OK;
+    return launch_accumulate_norm(pd, plan->d_ptrs, src_dtype, dst, dst_dtype, mode, partials, s);
+  }
+  if (!src_ptrs || !dst) return fail(ZDS_EINVAL, "%s: null src_ptrs or dst", fn);
   const uintptr_t es = static_cast<uintptr_t>(dtype_size(src_dtype));
   if (!aligned(dst, static_cast<uintptr_t>(dtype_size(dst_dtype))))
-    return fail(ZDS_EALIGN, "zds_grad_accumulate: dst not aligned to its element size");
+    return fail(ZDS_EALIGN, "%s: dst not aligned to its element size", fn);
   int dev = 0;
   hipError_t he = hipGetDevice(&dev);
-  if (he != hipSuccess) return hip_fail(he, "zds_grad_accumulate: hipGetDevice");
-  if (dev != plan->device) return fail(ZDS_EINVAL, "zds_grad_accumulate: plan belongs to device %d, current is %d", plan->device, dev);
+  if (he != hipSuccess) return hip_fail(he, "hipGetDevice");
+  if (dev != plan->device) return fail(ZDS_EINVAL, "%s: plan belongs to device %d, current is %d", fn, plan->device, dev);
   for (int32_t i = 0; i < E; ++i) {
     const int64_t t = plan->entries[4 * static_cast<size_t>(i)];
     const void *sp = src_ptrs[t];
-    if (!sp) return fail(ZDS_EINVAL, "zds_grad_accumulate: src_ptrs[%lld] is null", static_cast<long long>(t));
-    if (!aligned(sp, es)) return fail(ZDS_EALIGN, "zds_grad_accumulate: src_ptrs[%lld] misaligned", static_cast<long long>(t));
+    if (!sp) return fail(ZDS_EINVAL, "%s: src_ptrs[%lld] is null", fn, static_cast<long long>(t));
+    if (!aligned(sp, es)) return fail(ZDS_EALIGN, "%s: src_ptrs[%lld] misaligned", fn, static_cast<long long>(t));
   }
   const uint32_t slot = plan->next % kRing;
   if (plan->used[slot]) {
     he = hipEventSynchronize(plan->ev[slot]);
-    if (he != hipSuccess) return hip_fail(he, "zds_grad_accumulate: staging slot wait");
+    if (he != hipSuccess) return hip_fail(he, "staging slot wait");
   }
   const void **h = plan->h_ptrs + static_cast<size_t>(slot) * E;
   const void **d = plan->d_ptrs + static_cast<size_t>(slot) * E;
   for (int32_t i = 0; i < E; ++i) h[i] = src_ptrs[plan->entries[4 * static_cast<size_t>(i)]];
-  hipStream_t s = static_cast<hipStream_t>(stream);
   he = hipMemcpyAsync(d, h, sizeof(void *) * E, hipMemcpyHostToDevice, s);
-  if (he != hipSuccess) return hip_fail(he, "zds_grad_accumulate: pointer upload");
-  PlanDev pd{plan->d_table, E, plan->total_chunks};
-  zds_status st = launch_accumulate(pd, d, src_dtype, dst, dst_dtype, mode, s);
+  if (he != hipSuccess) return hip_fail(he, "pointer upload");
+  zds_status st = partials ? launch_accumulate_norm(pd, d, src_dtype, dst, dst_dtype, mode, partials, s)
+                           : launch_accumulate(pd, d, src_dtype, dst, dst_dtype, mode, s);
   if (st != ZDS_OK) return st;
   he = hipEventRecord(plan->ev[slot], s);
-  if (he != hipSuccess) return hip_fail(he, "zds_grad_accumulate: hipEventRecord");
+  if (he != hipSuccess) return hip_fail(he, "hipEventRecord");
   plan->used[slot] = true;
   plan->next += 1;
   return ZDS_OK;
 }
 
+extern "C" zds_status zds_grad_accumulate(zds_plan *plan, const void *const *src_ptrs,
+                                          zds_dtype src_dtype, void *dst, zds_dtype dst_dtype,
+                                          zds_accum_mode mode, void *stream) {
+  clear_error();
+  return accumulate_impl("zds_grad_accumulate", plan, src_ptrs, src_dtype, dst, dst_dtype, mode, nullptr,
+                         stream);
+}
+
+extern "C" size_t zds_plan_norm_workspace_bytes(const zds_plan *plan) {
+  if (!plan) return 0;
+  return static_cast<size_t>(partials_workspace_doubles(accumulate_grid(plan->total_chunks))) * sizeof(double);
+}
+
+extern "C" zds_status zds_grad_accumulate_norm(zds_plan *plan, const void *const *src_ptrs,
+                                               zds_dtype src_dtype, void *dst, zds_dtype dst_dtype,
+                                               zds_accum_mode mode, int32_t accum_steps, float max_norm,
+                                               const zds_step_state *state_dev, zds_step_scalars *out_dev,
+                                               void *ws, size_t ws_bytes, void *stream) {
+  clear_error();
+  const char *fn = "zds_grad_accumulate_norm";
+  if (!plan) return fail(ZDS_EINVAL, "%s: null plan", fn);
+  if (accum_steps < 1) return fail(ZDS_EINVAL, "%s: accum_steps must be >= 1", fn);
+  if (!state_dev || !out_dev) return fail(ZDS_EINVAL, "%s: null state or output", fn);
+  if (!aligned(state_dev, 8) || !aligned(out_dev, 8))
+    return fail(ZDS_EALIGN, "%s: state/output not 8-byte aligned", fn);
+  const size_t need = zds_plan_norm_workspace_bytes(plan);
+  if (!ws || ws_bytes < need || !aligned(ws, 8))
+    return fail(ZDS_EINVAL, "%s: workspace of %zu bytes needed (8-byte aligned)", fn, need);
+  double *partials = static_cast<double *>(ws);
+  zds_status st = accumulate_impl(fn, plan, src_ptrs, src_dtype, dst, dst_dtype, mode, partials, stream);
+  if (st != ZDS_OK) return st;
+  return launch_norm_stage2(partials, accumulate_grid(plan->total_chunks), state_dev, accum_steps, max_norm,
+                            out_dev, static_cast<hipStream_t>(stream));
+}
+
 extern "C" size_t zds_workspace_bytes(int64_t n) {
-  return static_cast<size_t>(norm_grid(n < 0 ? 0 : n)) * sizeof(double);
+  return static_cast<size_t>(partials_workspace_doubles(norm_grid(n < 0 ? 0 : n))) * sizeof(double);
 }
 
 extern "C" zds_status zds_overflow_and_norm(const void *grads, zds_dtype dtype, int64_t n,

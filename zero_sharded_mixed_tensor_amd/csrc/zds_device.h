@@ -126,4 +126,49 @@ __device__ __forceinline__ void store_quad16(void *base, int64_t q, const float 
   st_stream(static_cast<u32x2 *>(base) + q, w);
 }
 
+// fp64 reductions: DPP inside 16-lane rows, readlane across the rows, LDS
+// across waves. Fixed order, so sums are run-to-run identical.
+template <int CTRL>
+__device__ __forceinline__ double dpp_f64(double x) {
+  const uint64_t u = __builtin_bit_cast(uint64_t, x);
+  const int lo = __builtin_amdgcn_update_dpp(0, static_cast<int>(u & 0xffffffffu), CTRL, 0xf, 0xf, false);
+  const int hi = __builtin_amdgcn_update_dpp(0, static_cast<int>(u >> 32), CTRL, 0xf, 0xf, false);
+  return __builtin_bit_cast(double, (static_cast<uint64_t>(static_cast<uint32_t>(hi)) << 32) |
+                                        static_cast<uint32_t>(lo));
+}
+
+__device__ __forceinline__ double readlane_f64(double x, int lane) {
+  const uint64_t u = __builtin_bit_cast(uint64_t, x);
+  const uint32_t lo = __builtin_amdgcn_readlane(static_cast<int>(u & 0xffffffffu), lane);
+  const uint32_t hi = __builtin_amdgcn_readlane(static_cast<int>(u >> 32), lane);
+  return __builtin_bit_cast(double, (static_cast<uint64_t>(hi) << 32) | lo);
+}
+
+// Sum over the 64 lanes of a wave, the same value returned to every lane.
+// Needs all 64 lanes active.
+__device__ __forceinline__ double wave_sum(double x) {
+  x = x + dpp_f64<0xB1>(x);   // quad_perm [1,0,3,2]: pairs
+  x = x + dpp_f64<0x4E>(x);   // quad_perm [2,3,0,1]: quads
+  x = x + dpp_f64<0x124>(x);  // row_ror:4
+  x = x + dpp_f64<0x128>(x);  // row_ror:8 -> every lane holds its row's sum
+  return (readlane_f64(x, 0) + readlane_f64(x, 16)) + (readlane_f64(x, 32) + readlane_f64(x, 48));
+}
+
+// Sum over a block of BLOCK threads (all of them must call it); the result is
+// valid in thread 0. Waves add in lane order, the wave totals in wave order.
+template <int BLOCK>
+__device__ __forceinline__ double block_sum(double x) {
+  static_assert(BLOCK % 64 == 0, "block is whole waves");
+  __shared__ double wsum[BLOCK / 64];
+  x = wave_sum(x);
+  const int w = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) wsum[w] = x;
+  __syncthreads();
+  double t = 0.0;
+  if (threadIdx.x == 0) {
+    for (int k = 0; k < BLOCK / 64; ++k) t += wsum[k];
+  }
+  return t;  // valid in thread 0
+}
+
 }  // namespace zds

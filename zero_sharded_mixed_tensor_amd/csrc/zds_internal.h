@@ -134,7 +134,7 @@ inline void state_from_config(zds_step_state &s, const zds_scaler_config &cfg, i
 // ---------------------------------------------------------------------------
 
 struct PlanDev {
-  const int64_t *table;  // [start E][len E][dst E][chunk0 E+1]
+  const int64_t *table;  // [start E][len E][dst E][chunk0 E+1][entry of each chunk]
   int32_t num_entries;
   int64_t total_chunks;
 };
@@ -147,6 +147,24 @@ int norm_grid(int64_t n);
 zds_status launch_norm(const void *grads, zds_dtype dtype, int64_t n, int32_t accum_steps,
                        float max_norm, const zds_step_state *state, zds_step_scalars *out,
                        double *partials, hipStream_t stream);
+
+// Folds nparts float64 partial sums (more levels for large counts, written
+// into the workspace after them) and derives the step scalars.
+zds_status launch_norm_stage2(double *partials, int64_t nparts, const zds_step_state *state,
+                              int32_t accum_steps, float max_norm, zds_step_scalars *out,
+                              hipStream_t stream);
+// Doubles of workspace launch_norm_stage2 needs for nparts partials.
+int64_t partials_workspace_doubles(int64_t nparts);
+
+// Grid of the accumulate kernel for a plan with `total_chunks` chunks (also
+// the number of partial sums the fused norm writes).
+int64_t accumulate_grid(int64_t total_chunks);
+
+// Same as launch_accumulate, and each block also writes the float64 sum of
+// squares of the values it stored to partials[blockIdx].
+zds_status launch_accumulate_norm(const PlanDev &p, const void *const *dev_ptrs, zds_dtype src,
+                                  void *dst, zds_dtype dst_dtype, zds_accum_mode mode,
+                                  double *partials, hipStream_t stream);
 
 zds_status launch_adam(const zds_adamw_hparams &hp, const void *grads, zds_dtype gdt, float *master,
                        float *m, float *v, void *out, zds_dtype pdt, int64_t n, zds_step_scalars *scalars,

@@ -33,45 +33,6 @@ namespace zds {
 
 static_assert(ZDS_NORM_BLOCK % 64 == 0, "block is whole waves");
 
-template <int CTRL>
-__device__ __forceinline__ double dpp_f64(double x) {
-  const uint64_t u = __builtin_bit_cast(uint64_t, x);
-  const int lo = __builtin_amdgcn_update_dpp(0, static_cast<int>(u & 0xffffffffu), CTRL, 0xf, 0xf, false);
-  const int hi = __builtin_amdgcn_update_dpp(0, static_cast<int>(u >> 32), CTRL, 0xf, 0xf, false);
-  return __builtin_bit_cast(double, (static_cast<uint64_t>(static_cast<uint32_t>(hi)) << 32) |
-                                        static_cast<uint32_t>(lo));
-}
-
-__device__ __forceinline__ double readlane_f64(double x, int lane) {
-  const uint64_t u = __builtin_bit_cast(uint64_t, x);
-  const uint32_t lo = __builtin_amdgcn_readlane(static_cast<int>(u & 0xffffffffu), lane);
-  const uint32_t hi = __builtin_amdgcn_readlane(static_cast<int>(u >> 32), lane);
-  return __builtin_bit_cast(double, (static_cast<uint64_t>(hi) << 32) | lo);
-}
-
-// Sum over the 64 lanes of a wave, the same value returned to every lane.
-// Needs all 64 lanes active.
-__device__ __forceinline__ double wave_sum(double x) {
-  x = x + dpp_f64<0xB1>(x);   // quad_perm [1,0,3,2]: pairs
-  x = x + dpp_f64<0x4E>(x);   // quad_perm [2,3,0,1]: quads
-  x = x + dpp_f64<0x124>(x);  // row_ror:4
-  x = x + dpp_f64<0x128>(x);  // row_ror:8 -> every lane holds its row's sum
-  return (readlane_f64(x, 0) + readlane_f64(x, 16)) + (readlane_f64(x, 32) + readlane_f64(x, 48));
-}
-
-__device__ __forceinline__ double block_sum(double x) {
-  __shared__ double wsum[ZDS_NORM_BLOCK / 64];
-  x = wave_sum(x);
-  const int w = threadIdx.x >> 6;
-  if ((threadIdx.x & 63) == 0) wsum[w] = x;
-  __syncthreads();
-  double t = 0.0;
-  if (threadIdx.x == 0) {
-    for (int k = 0; k < ZDS_NORM_BLOCK / 64; ++k) t += wsum[k];
-  }
-  return t;  // valid in thread 0
-}
-
 template <int D>
 __device__ __forceinline__ double sq_acc(float x, double acc) {
   const double d = static_cast<double>(x);
@@ -117,17 +78,17 @@ __global__ void __launch_bounds__(ZDS_NORM_BLOCK) norm_stage1(const void *x, int
   } else {
     for (int64_t e = tid; e < n; e += stride) acc0 = sq_acc<D>(widen1<D>(x, e), acc0);
   }
-  const double b = block_sum(acc0 + acc1);
+  const double b = block_sum<ZDS_NORM_BLOCK>(acc0 + acc1);
   if (threadIdx.x == 0) partials[blockIdx.x] = b;
 }
 
-__global__ void __launch_bounds__(ZDS_NORM_BLOCK) norm_stage2(const double *partials, int nparts,
+__global__ void __launch_bounds__(ZDS_NORM_BLOCK) norm_stage2(const double *partials, int64_t nparts,
                                                                const zds_step_state *state,
                                                                int32_t accum_steps, float max_norm,
                                                                zds_step_scalars *out) {
   double acc = 0.0;
-  for (int i = threadIdx.x; i < nparts; i += ZDS_NORM_BLOCK) acc += partials[i];
-  const double total = block_sum(acc);
+  for (int64_t i = threadIdx.x; i < nparts; i += ZDS_NORM_BLOCK) acc += partials[i];
+  const double total = block_sum<ZDS_NORM_BLOCK>(acc);
   if (threadIdx.x == 0) {
     zds_step_scalars s = {};
     clip_scalars(total, state->scale, accum_steps, max_norm, s);
@@ -163,8 +124,52 @@ zds_status launch_norm(const void *grads, zds_dtype dtype, int64_t n, int32_t ac
   }
   zds_status st = check_launch("overflow_and_norm stage 1");
   if (st != ZDS_OK) return st;
-  hipLaunchKernelGGL(norm_stage2, dim3(1), dim3(ZDS_NORM_BLOCK), 0, stream, partials, grid, state,
-                     accum_steps, max_norm, out);
+  return launch_norm_stage2(partials, grid, state, accum_steps, max_norm, out, stream);
+}
+
+// Block b adds partials [b*kReduceSpan, (b+1)*kReduceSpan) in a fixed order.
+constexpr int64_t kReduceSpan = 8 * ZDS_NORM_BLOCK;
+
+__global__ void __launch_bounds__(ZDS_NORM_BLOCK) norm_reduce(const double *in, int64_t n, double *out) {
+  const int64_t base = static_cast<int64_t>(blockIdx.x) * kReduceSpan;
+  double acc = 0.0;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const int64_t i = base + k * ZDS_NORM_BLOCK + threadIdx.x;
+    if (i < n) acc += in[i];
+  }
+  const double b = block_sum<ZDS_NORM_BLOCK>(acc);
+  if (threadIdx.x == 0) out[blockIdx.x] = b;
+}
+
+int64_t partials_workspace_doubles(int64_t nparts) {
+  int64_t total = nparts;
+  for (int64_t k = nparts; k > kReduceSpan; k = (k + kReduceSpan - 1) / kReduceSpan)
+    total += (k + kReduceSpan - 1) / kReduceSpan;
+  return total;
+}
+
+// Many partials (one per block of a one-block-per-chunk kernel) are first
+// folded kReduceSpan at a time by parallel blocks, in index order, into the
+// workspace after them; the last level goes to the single-block stage 2.
+zds_status launch_norm_stage2(double *partials, int64_t nparts, const zds_step_state *state,
+                              int32_t accum_steps, float max_norm, zds_step_scalars *out,
+                              hipStream_t stream) {
+  double *p = partials;
+  double *next = partials + nparts;
+  int64_t k = nparts;
+  while (k > kReduceSpan) {
+    const int64_t blocks = (k + kReduceSpan - 1) / kReduceSpan;
+    hipLaunchKernelGGL(norm_reduce, dim3(static_cast<uint32_t>(blocks)), dim3(ZDS_NORM_BLOCK), 0, stream, p, k,
+                       next);
+    zds_status st = check_launch("overflow_and_norm partial reduction");
+    if (st != ZDS_OK) return st;
+    p = next;
+    next += blocks;
+    k = blocks;
+  }
+  hipLaunchKernelGGL(norm_stage2, dim3(1), dim3(ZDS_NORM_BLOCK), 0, stream, p, k, state, accum_steps, max_norm,
+                     out);
   return check_launch("overflow_and_norm stage 2");
 }
 

@@ -59,13 +59,23 @@ def _csv(d, suffix):
     return fs[0]
 
 
-def trace_summary(d, command):
+def trace_summary(d, command, skip=0):
+    """Per-kernel table from --stats, plus the average over each kernel's
+    launches after the first `skip` (the bench's warm-up steps), taken from
+    the per-dispatch trace."""
     rows = list(csv.DictReader(open(_csv(d, "kernel_stats.csv"))))
+    per = collections.defaultdict(list)
+    for r in csv.DictReader(open(_csv(d, "kernel_trace.csv"))):
+        per[r["Kernel_Name"]].append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
     out = ["# rocprofv3 kernel trace", "", "Command:", "", "    " + command, "",
-           "| kernel | calls | avg us | total us | % |", "|---|---:|---:|---:|---:|"]
+           "| kernel | calls | avg us | avg us after %d warm-up launches | total us | %% |" % skip,
+           "|---|---:|---:|---:|---:|---:|"]
     for r in rows:
-        out.append("| %s | %s | %.2f | %.1f | %s |" % (
+        d_ns = per.get(r["Name"], [])
+        steady = d_ns[skip:] if len(d_ns) > skip else d_ns
+        out.append("| %s | %s | %.2f | %s | %.1f | %s |" % (
             _short(r["Name"]), r["Calls"], float(r["AverageNs"]) / 1e3,
+            ("%.2f" % (sum(steady) / len(steady) / 1e3)) if steady else "-",
             float(r["TotalDurationNs"]) / 1e3, r["Percentage"]))
     return "\n".join(out) + "\n"
 
@@ -149,6 +159,7 @@ def main():
     t.add_argument("--dir", required=True)
     t.add_argument("--command", required=True)
     t.add_argument("--out", required=True)
+    t.add_argument("--skip", type=int, default=0, help="warm-up launches per kernel to leave out")
     c = sub.add_parser("counters")
     c.add_argument("--fetch", required=True)
     c.add_argument("--write", required=True)
@@ -158,7 +169,7 @@ def main():
     c.add_argument("--out", required=True)
     a = ap.parse_args()
     if a.what == "trace":
-        text = trace_summary(a.dir, a.command)
+        text = trace_summary(a.dir, a.command, a.skip)
     else:
         text = counters_summary(a.fetch, a.write, a.command, a.workload, a.params)
     with open(a.out, "w") as f:

@@ -25,6 +25,11 @@ class ShardStep:
         self.ws = zds.new_workspace(n, device)
         zds.zds_step_state_init(self.state, self.cfg, t0, beta1_pow0, beta2_pow0, stream)
 
+    def accumulate_norm(self, plan, srcs, dst, mode, ws, stream=None):
+        """The step's last micro-batch with the overflow/norm pass fused in."""
+        zds.zds_grad_accumulate_norm(plan, srcs, dst, mode, self.accum_steps, self.max_norm, self.state,
+                                     self.scalars, ws, stream)
+
     def norm(self, grads, stream=None):
         zds.zds_overflow_and_norm(grads, self.accum_steps, self.max_norm, self.state, self.scalars,
                                   self.ws, stream, n=self.n)

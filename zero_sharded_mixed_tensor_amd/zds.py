@@ -77,6 +77,9 @@ _SIGS = {
     "zds_plan_entry": (_I32, [_P, _I32, _PI64]),
     "zds_grad_accumulate": (_I32, [_P, ctypes.POINTER(_P), _I32, _P, _I32, _I32, _P]),
     "zds_workspace_bytes": (ctypes.c_size_t, [_I64]),
+    "zds_plan_norm_workspace_bytes": (ctypes.c_size_t, [_P]),
+    "zds_grad_accumulate_norm": (_I32, [_P, ctypes.POINTER(_P), _I32, _P, _I32, _I32, _I32, ctypes.c_float,
+                                        _P, _P, _P, ctypes.c_size_t, _P]),
     "zds_overflow_and_norm": (_I32, [_P, _I32, _I64, _I32, ctypes.c_float, _P, _P, _P,
                                      ctypes.c_size_t, _P]),
     "zds_adam_step": (_I32, [ctypes.POINTER(AdamWHparams), _P, _I32, _P, _P, _P, _P, _I32, _I64,
@@ -232,6 +235,12 @@ def zds_plan_create(numels, flat_align, lo, hi):
 def zds_grad_accumulate(plan, srcs, dst, mode, stream=None):
     """srcs: one device tensor per tensor of the plan's layout (None where the
     plan has no entry); dst: the flat device buffer of the plan's range."""
+    ptrs, sdt = _src_array(plan, srcs)
+    _check(lib.zds_grad_accumulate(plan.handle, ptrs, sdt, _dev_ptr(dst, "dst"), dtype_code(dst),
+                                   mode, _stream(stream)))
+
+
+def _src_array(plan, srcs):
     if len(srcs) != plan.num_tensors:
         raise ZdsError(ZDS_EINVAL, "need %d source tensors" % plan.num_tensors)
     sdt = None
@@ -245,10 +254,21 @@ def zds_grad_accumulate(plan, srcs, dst, mode, stream=None):
         elif c != sdt:
             raise ZdsError(ZDS_EINVAL, "source tensors must share one dtype")
         ptrs[i] = _dev_ptr(t, "source %d" % i)
-    if sdt is None:
-        sdt = ZDS_FP16
-    _check(lib.zds_grad_accumulate(plan.handle, ptrs, sdt, _dev_ptr(dst, "dst"), dtype_code(dst),
-                                   mode, _stream(stream)))
+    return ptrs, (ZDS_FP16 if sdt is None else sdt)
+
+
+def zds_plan_norm_workspace_bytes(plan):
+    return lib.zds_plan_norm_workspace_bytes(plan.handle)
+
+
+def zds_grad_accumulate_norm(plan, srcs, dst, mode, accum_steps, max_norm, state, scalars, ws, stream=None):
+    """zds_grad_accumulate plus the step's overflow flag, norm and clip
+    scalars formed from the stored values (see include/zds.h)."""
+    ptrs, sdt = _src_array(plan, srcs)
+    _check(lib.zds_grad_accumulate_norm(plan.handle, ptrs, sdt, _dev_ptr(dst, "dst"), dtype_code(dst), mode,
+                                        accum_steps, max_norm, _dev_ptr(state, "state"),
+                                        _dev_ptr(scalars, "scalars"), _dev_ptr(ws, "workspace"),
+                                        ws.numel() * ws.element_size(), _stream(stream)))
 
 
 def zds_workspace_bytes(n):
@@ -334,6 +354,11 @@ def new_scalars(device="cuda"):
 
 def new_workspace(n, device="cuda"):
     return torch.empty((zds_workspace_bytes(n) + 7) // 8, dtype=torch.float64, device=device)
+
+
+def new_plan_workspace(plan, device="cuda"):
+    return torch.empty(max(1, (zds_plan_norm_workspace_bytes(plan) + 7) // 8), dtype=torch.float64,
+                       device=device)
 
 
 def read_state(t):
