@@ -22,7 +22,10 @@
 // and raised the pass from about 5.8 to 6.0 TB/s on the 7B shard. Each block
 // then takes 2 consecutive tiles (6.0 -> 6.3 TB/s: half the block launches,
 // same footprint per wave), and the grid has one block per tile pair, so the
-// dispatcher keeps every CU full as blocks finish.
+// dispatcher keeps every CU full as blocks finish. Issuing the second tile's
+// loads before the first tile's update (software pipelining) measured slower
+// (6.0 TB/s): on this memory system more bytes in flight per wave lose to
+// more waves with one access each.
 //
 // The step constants (lr / (1 - beta1^t), sqrt(1 - beta2^t), 1 - lr*wd, the
 // 1 - beta values) are derived once per call by a single-wave prep kernel

@@ -148,6 +148,7 @@ struct zds_plan {
   hipEvent_t ev[kRing] = {};
   bool used[kRing] = {};
   uint32_t next = 0;
+  int last_slot = -1;  // slot holding the most recently uploaded pointer set
 };
 
 static void plan_free(zds_plan *p) {
@@ -268,23 +269,41 @@ static zds_status accumulate_impl(const char *fn, zds_plan *plan, const void *co
     if (!sp) return fail(ZDS_EINVAL, "%s: src_ptrs[%lld] is null", fn, static_cast<long long>(t));
     if (!aligned(sp, es)) return fail(ZDS_EALIGN, "%s: src_ptrs[%lld] misaligned", fn, static_cast<long long>(t));
   }
-  const uint32_t slot = plan->next % kRing;
-  if (plan->used[slot]) {
-    he = hipEventSynchronize(plan->ev[slot]);
-    if (he != hipSuccess) return hip_fail(he, "staging slot wait");
+  // The same source set as the previous call (the usual case: grads live in
+  // fixed buffers) reuses that slot's device copy; otherwise the next ring
+  // slot is refilled once the launch that last used it has finished.
+  bool same = plan->last_slot >= 0;
+  if (same) {
+    const void **prev = plan->h_ptrs + static_cast<size_t>(plan->last_slot) * E;
+    for (int32_t i = 0; i < E && same; ++i) same = prev[i] == src_ptrs[plan->entries[4 * static_cast<size_t>(i)]];
+  }
+  uint32_t slot;
+  if (same) {
+    slot = static_cast<uint32_t>(plan->last_slot);
+  } else {
+    slot = plan->next % kRing;
+    if (plan->used[slot]) {
+      he = hipEventSynchronize(plan->ev[slot]);
+      if (he != hipSuccess) return hip_fail(he, "staging slot wait");
+    }
   }
   const void **h = plan->h_ptrs + static_cast<size_t>(slot) * E;
   const void **d = plan->d_ptrs + static_cast<size_t>(slot) * E;
-  for (int32_t i = 0; i < E; ++i) h[i] = src_ptrs[plan->entries[4 * static_cast<size_t>(i)]];
-  he = hipMemcpyAsync(d, h, sizeof(void *) * E, hipMemcpyHostToDevice, s);
-  if (he != hipSuccess) return hip_fail(he, "pointer upload");
+  if (!same) {
+    for (int32_t i = 0; i < E; ++i) h[i] = src_ptrs[plan->entries[4 * static_cast<size_t>(i)]];
+    he = hipMemcpyAsync(d, h, sizeof(void *) * E, hipMemcpyHostToDevice, s);
+    if (he != hipSuccess) return hip_fail(he, "pointer upload");
+  }
   zds_status st = partials ? launch_accumulate_norm(pd, d, src_dtype, dst, dst_dtype, mode, partials, s)
                            : launch_accumulate(pd, d, src_dtype, dst, dst_dtype, mode, s);
   if (st != ZDS_OK) return st;
   he = hipEventRecord(plan->ev[slot], s);
   if (he != hipSuccess) return hip_fail(he, "hipEventRecord");
   plan->used[slot] = true;
-  plan->next += 1;
+  if (!same) {
+    plan->next += 1;
+    plan->last_slot = static_cast<int>(slot);
+  }
   return ZDS_OK;
 }
 
