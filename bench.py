@@ -33,7 +33,8 @@ def _parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="llama7b_s1",
-                    choices=["llama7b_s1", "llama7b_s1_accum16", "llama7b_whole_1024", "llama65b_s1", "tiny"])
+                    choices=["llama7b_s1", "llama7b_s1_accum16", "llama7b_whole_1024", "llama65b_s1", "tiny",
+                             "llama7b_s2_intake8"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--unfused", action="store_true",
                     help="separate overflow/norm pass instead of the one fused into the last "
@@ -59,6 +60,11 @@ def _workload(name):
     if name == "llama7b_whole_1024":
         return dict(tensors=llama_7b_split_1024(), world=1, rank=0, gdt="fp16", pdt="fp16", sigma=1e-3,
                     accum=1, scale=16, prior=False, mode="copy")
+    if name == "llama7b_s2_intake8":
+        # Stage 2 at N = 8: the rank sums the 8 peers' bf16 copies of its slice
+        # into an fp32 shard gradient, then steps on it (mean over the peers)
+        return dict(tensors=llama_7b_tensors(), world=8, rank=0, gdt="bf16", pdt="bf16", sigma=2e-3,
+                    accum=8, scale=None, prior=True, mode="intake", peers=8)
     if name == "llama65b_s1":
         return dict(tensors=llama_65b_tensors(), world=8, rank=0, gdt="bf16", pdt="bf16", sigma=1e-3,
                     accum=1, scale=None, prior=True, mode="copy")
@@ -71,6 +77,8 @@ def _bytes_per_param(w, fused):
     norm reads nothing extra: it is formed from the values the last
     flatten/accumulate call stores."""
     g = 2
+    if w["mode"] == "intake":
+        return dict(accum_total=2 * w["peers"] + 4, norm=4, adam=30)
     if w["mode"] == "accumulate":
         acc = 6 + 10 * (w["accum"] - 1)      # overwrite once, then accumulate
         return dict(accum_total=acc, norm=0 if fused else 4, adam=30)
@@ -98,7 +106,8 @@ def run_gpu(args, w):
     # per-tensor grads of the tensors this shard touches (whole tensors)
     srcs = [None] * len(numels)
     for t, _, _, _ in ents:
-        srcs[t] = torch.empty(numels[t], dtype=tdt[w["gdt"]], device=dev)
+        if w["mode"] != "intake":
+            srcs[t] = torch.empty(numels[t], dtype=tdt[w["gdt"]], device=dev)
     scale = 1.0 if w["scale"] is None else 2.0 ** w["scale"]
 
     def fill_grads(k):
@@ -120,7 +129,15 @@ def run_gpu(args, w):
         v = torch.zeros(n, dtype=torch.float32, device=dev)
         t0, b1p, b2p = 0, 1.0, 1.0
     p16 = master.to(tdt[w["pdt"]])
-    if w["mode"] == "accumulate":
+    if w["mode"] == "intake":
+        peers = []
+        for k in range(w["peers"]):
+            pk = torch.empty(n, dtype=tdt[w["gdt"]], device=dev)
+            gk = torch.Generator(device=dev)
+            gk.manual_seed(7000 + k)
+            peers.append(pk.normal_(0.0, w["sigma"], generator=gk))
+        bucket = torch.zeros(n, dtype=torch.float32, device=dev)
+    elif w["mode"] == "accumulate":
         bucket = torch.zeros(n, dtype=torch.float32, device=dev)
     else:
         bucket = torch.zeros(n, dtype=tdt[w["gdt"]], device=dev)
@@ -128,7 +145,7 @@ def run_gpu(args, w):
            else zds.scaler_config(initial_scale_power=w["scale"], window=1000, hysteresis=1))
     st = ShardStep(n, zds.hparams(), cfg, max_norm=1.0, accum_steps=w["accum"], t0=t0,
                    beta1_pow0=b1p, beta2_pow0=b2p)
-    fused = not args.unfused
+    fused = not args.unfused and w["mode"] != "intake"
     pws = zds.new_plan_workspace(plan)
     torch.cuda.synchronize()
 
@@ -141,7 +158,9 @@ def run_gpu(args, w):
             return e
         e0 = mark() if record else None
         modes = ([zds.ZDS_OVERWRITE] + [zds.ZDS_ACCUMULATE] * (w["accum"] - 1)
-                 if w["mode"] == "accumulate" else [zds.ZDS_COPY])
+                 if w["mode"] == "accumulate" else [] if w["mode"] == "intake" else [zds.ZDS_COPY])
+        if w["mode"] == "intake":
+            zds.zds_reduce_peer_slices(peers, bucket, zds.ZDS_OVERWRITE)
         for k, md in enumerate(modes):
             if fused and k == len(modes) - 1:
                 st.accumulate_norm(plan, srcs, bucket, md, pws)
@@ -189,13 +208,15 @@ def run_gpu(args, w):
             entry["gbs"] = round(bpp[k] * n / (ms * 1e-3) / 1e9, 1)
         kern[k] = entry
     adam_ms = kern["adam"]["ms_avg"]
-    achieved = 28.0 * n / (adam_ms * 1e-3) / 1e9 if w["mode"] != "accumulate" else 30.0 * n / (adam_ms * 1e-3) / 1e9
+    achieved = bpp["adam"] * n / (adam_ms * 1e-3) / 1e9
+    if w["mode"] == "intake":
+        kern["intake"] = kern.pop("accumulate")
     step_bytes = (bpp["accum_total"] + bpp["norm"] + bpp["adam"]) * n
     ms_per_step = elapsed / args.steps * 1e3
     return dict(n=n, entries=len(ents), elapsed=elapsed, ms_per_step=ms_per_step, kernels=kern, fused=fused,
                 adam_gbs=achieved, step_gbs=step_bytes / (elapsed / args.steps) / 1e9,
                 step_bytes_per_param=bpp["accum_total"] + bpp["norm"] + bpp["adam"],
-                adam_bytes_per_param=28 if w["mode"] != "accumulate" else 30)
+                adam_bytes_per_param=bpp["adam"])
 
 
 # ------------------------------------------------------------------ CPU oracle part

@@ -253,6 +253,24 @@ zds_status zds_adam_step(const zds_adamw_hparams *hp, const void *grads, zds_dty
                          zds_dtype param_dtype, int64_t n, zds_step_scalars *scalars_dev,
                          const zds_step_state *state_dev, void *stream);
 
+/* Stage-2 reduce-scatter intake (a next row). Under Stage 2 the grads are
+ * reduce-scattered rather than all-reduced ([aidhplus] ZeRO-2 section; [ch01]
+ * §1.2 table): each rank sums the N peers' copies of its own slice. This call
+ * is that sum on one rank:
+ *   dst  = sum_k fp32(peer_ptrs[k][j])        (ZDS_OVERWRITE)
+ *   dst += sum_k fp32(peer_ptrs[k][j])        (ZDS_ACCUMULATE)
+ * for j < n, the sum formed in fp32 in peer order 0..N-1 (one round-to-
+ * nearest add per peer), the previous destination added last, a 16-bit
+ * destination rounded once at the end.
+ *   peer_ptrs  host array of num_peers (1..16) device pointers, n fp16/bf16
+ *              elements each (the slices received from the peers)
+ *   dst        device, n elements of fp32 or of the peers' dtype
+ * No mean is taken: to average over peers, give the step accum_steps = K * N.
+ * 2N + 4 (fp32 out) bytes of HBM traffic per element, +4 when accumulating. */
+zds_status zds_reduce_peer_slices(const void *const *peer_ptrs, int32_t num_peers, zds_dtype src_dtype,
+                                  int64_t n, void *dst, zds_dtype dst_dtype, zds_accum_mode mode,
+                                  void *stream);
+
 /* Row a3. Initialise the device step state from cfg with Adam step count t0
  * and powers beta1^t0, beta2^t0 (1, 1 for a fresh optimizer). */
 zds_status zds_step_state_init(zds_step_state *state_dev, const zds_scaler_config *cfg, int64_t t0,

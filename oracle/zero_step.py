@@ -371,3 +371,28 @@ def optimizer_step(x, gdtype, master, m, v, state, hp, max_norm, accum_steps, pd
     master, m, v = adamw_update(x, gdtype, sc["grad_scale"], master, m, v, c)
     p16 = narrow(master, pdtype)
     return master, m, v, p16, scaler_update(state, 0, hp.beta1, hp.beta2), sc
+
+
+# ---------------------------------------------------------------------------
+# Next row: Stage-2 reduce-scatter intake on one rank.
+# [aidhplus] ZeRO-2 section and [ch01] §1.2 table: under Stage 2 the grads are
+# reduce-scattered instead of all-reduced, each rank keeping only the grads of
+# its own slice. The rank's part of that collective is the sum, over the N
+# peers, of the peers' copies of its slice. Reading: the sum is formed in fp32
+# in peer order (one round-to-nearest add per peer), then stored in the
+# destination dtype (16-bit: one rounding at the end). The mean over peers is
+# not taken here: the step divides by accum_steps, so passing K * N there
+# averages over micro-batches and peers at once.
+# ---------------------------------------------------------------------------
+
+def reduce_peer_slices(slices, src_dtype, dst, dst_dtype, accumulate):
+    """dst (+)= sum over peers k = 0..N-1 of fp32(slices[k]), in that order.
+    dst is an fp32 array or 16-bit bit patterns; returned updated."""
+    acc = widen(slices[0], src_dtype).copy()
+    for sl in slices[1:]:
+        acc = acc + widen(sl, src_dtype)
+    if dst_dtype == FP32:
+        return dst + acc if accumulate else acc
+    if accumulate:
+        acc = widen(dst, dst_dtype) + acc
+    return narrow(acc, dst_dtype)

@@ -295,3 +295,34 @@ def test_llama65b_stage1_shard_bf16():
     want = _oracle_update(_h16(bucket[idx]), "bf16", osc, ost, P0, M0, V0, "bf16")
     _compare_samples("65B shard", idx, master, m, v, out, want)
     plan.close()
+
+
+def test_llama7b_stage2_intake_eight_peers():
+    """Stage 2 at N = 8 on the 7B shard: the rank sums 8 peers' bf16 copies of
+    its 842M-element slice into an fp32 shard gradient, then steps on it with
+    the mean over the peers (accum_steps = 8)."""
+    say("full size: Llama-7B Stage-2 intake, 8 peers")
+    numels, plan, ents, n, srcs, master, m, v = _setup_shard(llama_7b_tensors(), 8, 0, "bf16", 2e-3, True, 61)
+    del srcs
+    peers = [torch.empty(n, dtype=torch.bfloat16, device="cuda") for _ in range(8)]
+    draw_sources_(peers, 2e-3, 1.0, 61, 0)
+    acc = torch.empty(n, dtype=torch.float32, device="cuda")
+    out = torch.empty(n, dtype=torch.bfloat16, device="cuda")
+    st = ShardStep(n, zds.hparams(), zds.scaler_config(dynamic=False, static_scale=1.0), max_norm=1.0,
+                   accum_steps=8, t0=1, beta1_pow0=B1, beta2_pow0=B2)
+    idx = _sample_index(n, ents)
+    P0, M0, V0 = master[idx].cpu().numpy(), m[idx].cpu().numpy(), v[idx].cpu().numpy()
+    zds.zds_reduce_peer_slices(peers, acc, zds.ZDS_OVERWRITE)
+    st.step(acc, master, m, v, out)
+    torch.cuda.synchronize()
+    psamp = [_h16(pk[idx]) for pk in peers]
+    want_acc = O.reduce_peer_slices(psamp, "bf16", None, "fp32", accumulate=False)
+    assert (acc[idx].cpu().numpy().view(np.uint32) == want_acc.view(np.uint32)).all()
+    acc_h = acc.cpu().numpy()
+    osc = _oracle_scalars(O.sum_of_squares(acc_h, "fp32"), 1.0, 8, 1.0, O.overflow_flag(acc_h, "fp32"))
+    del acc_h
+    _compare_scalars(st.read_scalars(), osc)
+    ost = O.scaler_init(dynamic=False, static_scale=1.0, t=1, beta1_pow=B1, beta2_pow=B2)
+    want = _oracle_update(want_acc, "fp32", osc, ost, P0, M0, V0, "bf16")
+    _compare_samples("7B stage-2 intake", idx, master, m, v, out, want)
+    plan.close()

@@ -421,3 +421,27 @@ def test_accumulate_norm_fused_overflow(bad):
     torch.cuda.synchronize()
     s0 = st0.read_scalars()
     assert s0.overflow == 0 and s0.sumsq == 0.0 and s0.grad_scale == 1.0
+
+
+@pytest.mark.parametrize("N", [1, 2, 3, 5, 8, 16])
+@pytest.mark.parametrize("sdt,ddt", [("bf16", "fp32"), ("fp16", "fp32"), ("bf16", "bf16"), ("fp16", "fp16")])
+def test_reduce_peer_slices_parity(N, sdt, ddt):
+    say("reduce peers N=%d %s -> %s" % (N, sdt, ddt))
+    for n, offset in ((1, 0), (7, 0), (513, 0), (512 * 37 + 13, 0), (100003, 0), (4099, 1)):
+        peers = [draw_grads(n, sdt, 1e-2, 1.0, 40 + k, 94, n) for k in range(N)]
+        dpeers = [to_dev(np.concatenate([np.zeros(offset, np.uint16), p]), sdt)[offset:] for p in peers]
+        for acc in (False, True):
+            if ddt == "fp32":
+                base = draw_master(n, 0.5, 7, 95)
+                dst = to_dev(np.concatenate([np.zeros(offset, np.float32), base]), "fp32")[offset:]
+            else:
+                base = draw_grads(n, ddt, 0.5, 1.0, 8, 95, 0)
+                dst = to_dev(np.concatenate([np.zeros(offset, np.uint16), base]), ddt)[offset:]
+            zds.zds_reduce_peer_slices(dpeers, dst, zds.ZDS_ACCUMULATE if acc else zds.ZDS_OVERWRITE)
+            torch.cuda.synchronize()
+            want = O.reduce_peer_slices(peers, sdt, base.copy(), ddt, accumulate=acc)
+            got = to_host(dst)
+            if ddt == "fp32":
+                assert (got.view(np.uint32) == want.view(np.uint32)).all(), (n, acc)
+            else:
+                assert (got == want).all(), (n, acc)

@@ -32,6 +32,8 @@ MUTANTS = {
  "ovf_mask": ("return (bits & m) == m", "return (bits & m) == m - 1"),
  "widen_bf16": ("return (x.astype(np.uint32) << np.uint32(16)).view(np.float32)", "return (x.astype(np.uint32) << np.uint32(15)).view(np.float32)"),
  "decay_sign": ("c[\"decay\"] = np.float32(1.0 - float(lr) * float(wd))", "c[\"decay\"] = np.float32(1.0 + float(lr) * float(wd))"),
+ "reduce_drop_last": ("    for sl in slices[1:]:", "    for sl in slices[1:-1]:"),
+ "reduce_ignore_dst": ("        return dst + acc if accumulate else acc", "        return acc"),
  "beta_pow_skip": ("st = replace(st, t=st.t + 1, beta1_pow=st.beta1_pow * b1, beta2_pow=st.beta2_pow * b2,", "st = replace(st, t=st.t + 1, beta1_pow=st.beta1_pow * b2, beta2_pow=st.beta2_pow * b1,"),
 }
 

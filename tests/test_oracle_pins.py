@@ -619,3 +619,43 @@ def test_overflow_step_leaves_state():
     assert (r[0] == master).all() and (r[1] == m).all() and (r[2] == v).all()
     assert r[4].scale == st.scale / 2 and r[4].t == 5 and r[4].last_skip == 1
     assert r[4].beta1_pow == st.beta1_pow
+
+
+# ---------------------------------------------------------------- Stage-2 intake
+
+def test_reduce_peers_single_and_identical():
+    rng = np.random.default_rng(30)
+    x = (rng.standard_normal(5000) * 3).astype(np.float16).view(np.uint16)
+    one = O.reduce_peer_slices([x], O.FP16, None, O.FP32, accumulate=False)
+    assert (one.view(np.uint32) == O.widen(x, O.FP16).view(np.uint32)).all()
+    for N in (2, 3, 7, 8, 16):
+        s = O.reduce_peer_slices([x] * N, O.FP16, None, O.FP32, accumulate=False)
+        # k * x needs at most 11 + log2(k) significand bits: every partial sum is exact
+        assert (s == O.widen(x, O.FP16) * np.float32(N)).all()
+
+
+def test_reduce_peers_exact_rational_bound():
+    rng = np.random.default_rng(31)
+    for N in (2, 5, 8):
+        sl = [(rng.standard_normal(400) * 10.0 ** rng.integers(-3, 3, 400)).astype(np.float16).view(np.uint16)
+              for _ in range(N)]
+        got = O.reduce_peer_slices(sl, O.FP16, None, O.FP32, accumulate=False)
+        for j in range(400):
+            vals = [Fraction(float(O.widen(s[j:j + 1], O.FP16)[0])) for s in sl]
+            exact = sum(vals, Fraction(0))
+            mag = sum(abs(v) for v in vals)
+            assert abs(Fraction(float(got[j])) - exact) <= mag * Fraction(N, 2 ** 24)
+
+
+def test_reduce_peers_accumulate_and_16bit_destination():
+    rng = np.random.default_rng(32)
+    sl = [(rng.standard_normal(3000)).astype(np.float32) for _ in range(4)]
+    bits = [(s.view(np.uint32) >> 16).astype(np.uint16) for s in sl]
+    base = rng.standard_normal(3000).astype(np.float32)
+    acc = O.reduce_peer_slices(bits, O.BF16, base.copy(), O.FP32, accumulate=True)
+    plain = O.reduce_peer_slices(bits, O.BF16, None, O.FP32, accumulate=False)
+    assert (acc == base + plain).all()
+    # 16-bit destination: the fp32 sum rounded once, to nearest even
+    out16 = O.reduce_peer_slices(bits, O.BF16, None, O.BF16, accumulate=False)
+    for j in range(0, 3000, 7):
+        assert int(out16[j]) == _bf16_rne_exact(int(plain[j:j + 1].view(np.uint32)[0]))

@@ -342,6 +342,28 @@ extern "C" zds_status zds_grad_accumulate_norm(zds_plan *plan, const void *const
                             out_dev, static_cast<hipStream_t>(stream));
 }
 
+extern "C" zds_status zds_reduce_peer_slices(const void *const *peer_ptrs, int32_t num_peers, zds_dtype src_dtype,
+                                             int64_t n, void *dst, zds_dtype dst_dtype, zds_accum_mode mode,
+                                             void *stream) {
+  clear_error();
+  const char *fn = "zds_reduce_peer_slices";
+  if (num_peers < 1 || num_peers > kMaxPeers) return fail(ZDS_EINVAL, "%s: num_peers must be in [1, %d]", fn, kMaxPeers);
+  if (src_dtype != ZDS_FP16 && src_dtype != ZDS_BF16) return fail(ZDS_EINVAL, "%s: peers must be fp16 or bf16", fn);
+  if (dst_dtype != ZDS_FP32 && dst_dtype != src_dtype)
+    return fail(ZDS_EINVAL, "%s: destination must be fp32 or the peers' dtype", fn);
+  if (mode != ZDS_OVERWRITE && mode != ZDS_ACCUMULATE) return fail(ZDS_EINVAL, "%s: mode must be overwrite or accumulate", fn);
+  if (n < 0) return fail(ZDS_EINVAL, "%s: n < 0", fn);
+  if (n == 0) return ZDS_OK;
+  if (!peer_ptrs || !dst) return fail(ZDS_EINVAL, "%s: null pointer", fn);
+  for (int k = 0; k < num_peers; ++k) {
+    if (!peer_ptrs[k]) return fail(ZDS_EINVAL, "%s: peer %d is null", fn, k);
+    if (!aligned(peer_ptrs[k], 2)) return fail(ZDS_EALIGN, "%s: peer %d misaligned", fn, k);
+  }
+  if (!aligned(dst, static_cast<uintptr_t>(dtype_size(dst_dtype)))) return fail(ZDS_EALIGN, "%s: dst misaligned", fn);
+  return launch_reduce_peers(peer_ptrs, num_peers, src_dtype, n, dst, dst_dtype, mode == ZDS_ACCUMULATE,
+                             static_cast<hipStream_t>(stream));
+}
+
 extern "C" size_t zds_workspace_bytes(int64_t n) {
   return static_cast<size_t>(partials_workspace_doubles(norm_grid(n < 0 ? 0 : n))) * sizeof(double);
 }

@@ -166,6 +166,11 @@ zds_status launch_accumulate_norm(const PlanDev &p, const void *const *dev_ptrs,
                                   void *dst, zds_dtype dst_dtype, zds_accum_mode mode,
                                   double *partials, hipStream_t stream);
 
+// Most peers zds_reduce_peer_slices sums in one call.
+constexpr int kMaxPeers = 16;
+zds_status launch_reduce_peers(const void *const *peers, int32_t npeers, zds_dtype src, int64_t n, void *dst,
+                               zds_dtype dst_dtype, bool accumulate, hipStream_t stream);
+
 zds_status launch_adam(const zds_adamw_hparams &hp, const void *grads, zds_dtype gdt, float *master,
                        float *m, float *v, void *out, zds_dtype pdt, int64_t n, zds_step_scalars *scalars,
                        const zds_step_state *state, hipStream_t stream);

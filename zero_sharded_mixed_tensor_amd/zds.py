@@ -77,6 +77,7 @@ _SIGS = {
     "zds_plan_entry": (_I32, [_P, _I32, _PI64]),
     "zds_grad_accumulate": (_I32, [_P, ctypes.POINTER(_P), _I32, _P, _I32, _I32, _P]),
     "zds_workspace_bytes": (ctypes.c_size_t, [_I64]),
+    "zds_reduce_peer_slices": (_I32, [ctypes.POINTER(_P), _I32, _I32, _I64, _P, _I32, _I32, _P]),
     "zds_plan_norm_workspace_bytes": (ctypes.c_size_t, [_P]),
     "zds_grad_accumulate_norm": (_I32, [_P, ctypes.POINTER(_P), _I32, _P, _I32, _I32, _I32, ctypes.c_float,
                                         _P, _P, _P, ctypes.c_size_t, _P]),
@@ -269,6 +270,22 @@ def zds_grad_accumulate_norm(plan, srcs, dst, mode, accum_steps, max_norm, state
                                         accum_steps, max_norm, _dev_ptr(state, "state"),
                                         _dev_ptr(scalars, "scalars"), _dev_ptr(ws, "workspace"),
                                         ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def zds_reduce_peer_slices(peers, dst, mode, stream=None, n=None):
+    """dst (+)= sum over the peer slices (device tensors of one 16-bit dtype),
+    in peer order, in fp32 (see include/zds.h)."""
+    if not peers:
+        raise ZdsError(ZDS_EINVAL, "need at least one peer slice")
+    n = dst.numel() if n is None else n
+    sdt = dtype_code(peers[0])
+    arr = (ctypes.c_void_p * len(peers))()
+    for k, t in enumerate(peers):
+        if dtype_code(t) != sdt or t.numel() < n:
+            raise ZdsError(ZDS_EINVAL, "peer %d: wrong dtype or too short" % k)
+        arr[k] = _dev_ptr(t, "peer %d" % k)
+    _check(lib.zds_reduce_peer_slices(arr, len(peers), sdt, n, _dev_ptr(dst, "dst"), dtype_code(dst), mode,
+                                      _stream(stream)))
 
 
 def zds_workspace_bytes(n):
