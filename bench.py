@@ -34,7 +34,9 @@ def _parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="llama7b_s1",
                     choices=["llama7b_s1", "llama7b_s1_accum16", "llama7b_whole_1024", "llama65b_s1", "tiny",
-                             "llama7b_s2_intake8"])
+                             "llama7b_s2_intake8", "llama7b_s1_offload"])
+    ap.add_argument("--offload-threads", type=int, default=0,
+                    help="host threads for the offloaded optimizer (0: all available)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--unfused", action="store_true",
                     help="separate overflow/norm pass instead of the one fused into the last "
@@ -65,6 +67,10 @@ def _workload(name):
         # into an fp32 shard gradient, then steps on it (mean over the peers)
         return dict(tensors=llama_7b_tensors(), world=8, rank=0, gdt="bf16", pdt="bf16", sigma=2e-3,
                     accum=8, scale=None, prior=True, mode="intake", peers=8)
+    if name == "llama7b_s1_offload":
+        # the C2 shard with its fp32 optimizer state in pinned host memory
+        return dict(tensors=llama_7b_tensors(), world=8, rank=0, gdt="bf16", pdt="bf16", sigma=2e-3,
+                    accum=1, scale=None, prior=True, mode="copy", offload=True)
     if name == "llama65b_s1":
         return dict(tensors=llama_65b_tensors(), world=8, rank=0, gdt="bf16", pdt="bf16", sigma=1e-3,
                     accum=1, scale=None, prior=True, mode="copy")
@@ -219,6 +225,69 @@ def run_gpu(args, w):
                 adam_bytes_per_param=bpp["adam"])
 
 
+def run_offload(args, w):
+    """The shard's fp32 optimizer state in pinned host memory: flatten on the
+    device, then OffloadStep (device norm, chunked download, host AdamW on
+    all host threads, upload of the 16-bit params, device scaler). Timed by
+    wall clock per step (the host update is synchronous)."""
+    import torch
+    from zero_sharded_mixed_tensor_amd import zds
+    from zero_sharded_mixed_tensor_amd.step import OffloadStep
+
+    tdt = {"fp16": torch.float16, "bf16": torch.bfloat16}
+    numels = [n for _, n in w["tensors"]]
+    _, total = zds.zds_flat_layout(numels, 64)
+    lo, hi = zds.zds_shard_range(total, w["world"], w["rank"], 64)
+    n = hi - lo
+    plan = zds.zds_plan_create(numels, 64, lo, hi)
+    dev = torch.device("cuda", 0)
+    srcs = [None] * len(numels)
+    for t, _, _, _ in plan.entries():
+        g = torch.Generator(device=dev)
+        g.manual_seed(5000 + t)
+        srcs[t] = torch.empty(numels[t], dtype=tdt[w["gdt"]], device=dev).normal_(0.0, w["sigma"], generator=g)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(1234)
+    host = []
+    for sig in (0.02, 0.1 * w["sigma"], w["sigma"]):
+        d = torch.empty(n, dtype=torch.float32, device=dev).normal_(0.0, sig, generator=gen)
+        h = torch.empty(n, dtype=torch.float32, pin_memory=True)
+        h.copy_(d)
+        host.append(h)
+        del d
+    host[2].mul_(host[2]).mul_(0.001)
+    b1p, b2p = float(torch.tensor(0.9, dtype=torch.float32)), float(torch.tensor(0.999, dtype=torch.float32))
+    off = OffloadStep(n, host[0], host[1], host[2], tdt[w["gdt"]], tdt[w["pdt"]], zds.hparams(),
+                      zds.scaler_config(dynamic=False, static_scale=1.0), max_norm=1.0, t0=1, beta1_pow0=b1p,
+                      beta2_pow0=b2p, threads=args.offload_threads)
+    bucket = torch.empty(n, dtype=tdt[w["gdt"]], device=dev)
+    p16 = torch.empty(n, dtype=tdt[w["pdt"]], device=dev)
+
+    def one():
+        zds.zds_grad_accumulate(plan, srcs, bucket, zds.ZDS_COPY)
+        off.step(bucket, p16)
+
+    for _ in range(args.warmup):
+        one()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        one()
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t0
+    import os as _os
+    threads = args.offload_threads or len(_os.sched_getaffinity(0))
+    return {
+        "metric": METRIC, "value": round(n * args.steps / el, 1), "unit": "params/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(el / args.steps * 1e3, 3),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": args.workload, "params": n, "grad_dtype": w["gdt"], "param_dtype": w["pdt"],
+                   "optimizer_state": "pinned host memory", "host_threads": threads,
+                   "host_bytes_per_param": 28, "pcie_bytes_per_param": 4},
+        "host_update_gbs": round(28 * n * args.steps / el / 1e9, 1),
+    }
+
+
 # ------------------------------------------------------------------ CPU oracle part
 
 def run_cpu_baseline(w, sample, repeats, min_seconds=10.0):
@@ -275,6 +344,9 @@ def main():
               "slice); run with --gpus 1.", file=sys.stderr)
         return 2
     w = _workload(args.workload)
+    if w.get("offload"):
+        print(json.dumps(run_offload(args, w)), flush=True)
+        return 0
     r = run_gpu(args, w)
     out = {
         "metric": METRIC,

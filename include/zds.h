@@ -271,6 +271,24 @@ zds_status zds_reduce_peer_slices(const void *const *peer_ptrs, int32_t num_peer
                                   int64_t n, void *dst, zds_dtype dst_dtype, zds_accum_mode mode,
                                   void *stream);
 
+/* Offloaded optimizer shard (a next row). ZeRO-Offload keeps the optimizer
+ * state, and runs its update, in host memory ([aiqz] 卸载策略; [csdn] §4.3):
+ * this is zds_adam_step on host buffers, bit-identical to the device kernel
+ * (same constants from hp and state, same fp32 operation order, IEEE divide
+ * and square root, round-to-nearest-even casts).
+ *   grads, master, exp_avg, exp_avg_sq, params_out   HOST pointers, n elements
+ *              (params_out may be NULL); pinned memory lets the caller overlap
+ *              the grad download and param upload with the update
+ *   scalars, state   HOST copies of the step scalars / state (the norm pass
+ *              runs on the device; copy the 64-byte structs down first); an
+ *              overflow flag skips the update
+ *   num_threads      host threads (0: all the process may use)
+ * Returns when the update is done. Host-memory bound, 28 B/param. */
+zds_status zds_cpu_adam_step(const zds_adamw_hparams *hp, const void *grads, zds_dtype grad_dtype,
+                             float *master, float *exp_avg, float *exp_avg_sq, void *params_out,
+                             zds_dtype param_dtype, int64_t n, const zds_step_scalars *scalars,
+                             const zds_step_state *state, int32_t num_threads);
+
 /* Row a3. Initialise the device step state from cfg with Adam step count t0
  * and powers beta1^t0, beta2^t0 (1, 1 for a fresh optimizer). */
 zds_status zds_step_state_init(zds_step_state *state_dev, const zds_scaler_config *cfg, int64_t t0,

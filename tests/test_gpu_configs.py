@@ -229,3 +229,40 @@ def test_bf16_stage1_shard_prior_moments():
     assert osc["coef"] < 1.0
     _compare("bf16 shard", (to_host(dP), to_host(dM), to_host(dV), to_host(dOUT)), (oP, oM, oV, oOUT),
              st.read_scalars(), osc, ost, st.read_state())
+
+
+def test_offloaded_optimizer_shard_steps():
+    """Optimizer shard in pinned host memory: device norm, chunked download,
+    host AdamW, upload of the 16-bit params, device scaler; 4 steps with an
+    overflow at step 2, against the oracle."""
+    say("offload: 4 steps, overflow at step 2")
+    from zero_sharded_mixed_tensor_amd.step import OffloadStep
+    n = 300_001
+    master = draw_master(n, 0.02, 8, 9)
+    hm = torch.from_numpy(master.copy()).pin_memory()
+    hmm = torch.zeros(n, dtype=torch.float32).pin_memory()
+    hv = torch.zeros(n, dtype=torch.float32).pin_memory()
+    off = OffloadStep(n, hm, hmm, hv, torch.float16, torch.float16, zds.hparams(),
+                      zds.scaler_config(initial_scale_power=12), max_norm=1.0, chunk=65536, threads=3)
+    out = torch.zeros(n, dtype=torch.float16, device="cuda")
+    oP, oM, oV = master.copy(), np.zeros(n, np.float32), np.zeros(n, np.float32)
+    o16 = np.zeros(n, np.uint16)
+    ost = O.scaler_init(initial_scale_power=12)
+    for k in range(1, 5):
+        g = draw_grads(n, "fp16", 1e-3, ost.scale, 8, 9, k)
+        if k == 2:
+            g[n // 3] = 0x7C00
+        sc = off.step(to_dev(g, "fp16"), out)
+        torch.cuda.synchronize()
+        oP, oM, oV, r16, ost, osc = O.optimizer_step(g, "fp16", oP, oM, oV, ost, O.AdamW(), 1.0, 1, "fp16")
+        if r16 is not None:
+            o16 = r16
+        assert sc.overflow == osc["overflow"]
+        if not sc.overflow:
+            assert sc.grad_scale == osc["grad_scale"]
+        assert (hm.numpy().view(np.uint32) == oP.view(np.uint32)).all(), k
+        assert (hmm.numpy().view(np.uint32) == oM.view(np.uint32)).all(), k
+        assert (hv.numpy().view(np.uint32) == oV.view(np.uint32)).all(), k
+        assert (to_host(out) == o16).all(), k
+        s = off.dev.read_state()
+        assert (s.scale, s.t) == (np.float32(ost.scale), ost.t), k

@@ -15,6 +15,7 @@ class ShardStep:
 
     def __init__(self, n, hp=None, scaler=None, max_norm=1.0, accum_steps=1, t0=0,
                  beta1_pow0=1.0, beta2_pow0=1.0, device="cuda", stream=None):
+        # (positional order is relied on by OffloadStep)
         self.n = n
         self.hp = hp if hp is not None else zds.hparams()
         self.cfg = scaler if scaler is not None else zds.scaler_config()
@@ -51,3 +52,75 @@ class ShardStep:
 
     def read_scalars(self):
         return zds.read_scalars(self.scalars)
+
+
+class OffloadStep:
+    """A rank whose fp32 optimizer shard lives in pinned host memory
+    (ZeRO-Offload): the grads' overflow/norm pass runs on the device, the
+    grads stream to the host in chunks, the host updates each chunk as soon
+    as it has arrived (zds_cpu_adam_step) and streams its 16-bit params
+    back, so downloads, the host update and uploads overlap; the loss scaler
+    then runs on the device state.
+
+    master, exp_avg, exp_avg_sq: pinned host fp32 tensors (n elements)."""
+
+    def __init__(self, n, master, exp_avg, exp_avg_sq, grad_dtype, param_dtype, hp=None, scaler=None,
+                 max_norm=1.0, accum_steps=1, t0=0, beta1_pow0=1.0, beta2_pow0=1.0, chunk=1 << 25,
+                 threads=0, device="cuda"):
+        import torch
+        self.torch = torch
+        self.dev = ShardStep(n, hp, scaler, max_norm, accum_steps, t0, beta1_pow0, beta2_pow0, device)
+        self.n = n
+        self.master, self.m, self.v = master, exp_avg, exp_avg_sq
+        self.gh = torch.empty(n, dtype=grad_dtype, pin_memory=True)
+        self.ph = torch.empty(n, dtype=param_dtype, pin_memory=True)
+        self.sc_h = torch.empty(zds.SCALARS_BYTES, dtype=torch.uint8, pin_memory=True)
+        self.st_h = torch.empty(zds.STATE_BYTES, dtype=torch.uint8, pin_memory=True)
+        self.chunk = chunk
+        self.threads = threads
+        self.down = torch.cuda.Stream(device)
+        self.up = torch.cuda.Stream(device)
+
+    def step(self, grads, params_out):
+        """grads: device gradient shard (n elements); params_out: device
+        16-bit params (n elements), written."""
+        torch = self.torch
+        d = self.dev
+        cur = torch.cuda.current_stream()
+        self.up.wait_stream(cur)  # earlier readers of params_out come first
+        d.norm(grads)
+        ready = torch.cuda.Event()
+        ready.record(cur)
+        # downloads: the scalars/state first, then the grads chunk by chunk
+        self.down.wait_event(ready)
+        evs = []
+        with torch.cuda.stream(self.down):
+            self.sc_h.copy_(d.scalars, non_blocking=True)
+            self.st_h.copy_(d.state, non_blocking=True)
+            for a in range(0, self.n, self.chunk):
+                b = min(self.n, a + self.chunk)
+                self.gh[a:b].copy_(grads[a:b], non_blocking=True)
+                e = torch.cuda.Event()
+                e.record(self.down)
+                evs.append((a, b, e))
+        if evs:
+            evs[0][2].synchronize()
+        else:
+            self.down.synchronize()
+        sc = zds.StepScalars.from_buffer_copy(self.sc_h.numpy().tobytes())
+        st = zds.StepState.from_buffer_copy(self.st_h.numpy().tobytes())
+        last_up = None
+        for a, b, e in evs:
+            e.synchronize()
+            zds.zds_cpu_adam_step(d.hp, self.gh[a:b], self.master[a:b], self.m[a:b], self.v[a:b],
+                                  self.ph[a:b], sc, st, num_threads=self.threads)
+            if sc.overflow:
+                continue
+            with torch.cuda.stream(self.up):
+                params_out[a:b].copy_(self.ph[a:b], non_blocking=True)
+                last_up = torch.cuda.Event()
+                last_up.record(self.up)
+        if last_up is not None:
+            cur.wait_event(last_up)
+        d.scaler()
+        return sc

@@ -85,6 +85,8 @@ _SIGS = {
                                      ctypes.c_size_t, _P]),
     "zds_adam_step": (_I32, [ctypes.POINTER(AdamWHparams), _P, _I32, _P, _P, _P, _P, _I32, _I64,
                              _P, _P, _P]),
+    "zds_cpu_adam_step": (_I32, [ctypes.POINTER(AdamWHparams), _P, _I32, _P, _P, _P, _P, _I32, _I64,
+                                 ctypes.POINTER(StepScalars), ctypes.POINTER(StepState), _I32]),
     "zds_step_state_init": (_I32, [_P, ctypes.POINTER(ScalerConfig), _I64, ctypes.c_double,
                                    ctypes.c_double, _P]),
     "zds_loss_scaler_update": (_I32, [_P, _P, ctypes.POINTER(AdamWHparams), _P]),
@@ -314,6 +316,46 @@ def zds_adam_step(hp, grads, master, exp_avg, exp_avg_sq, params_out, scalars, s
                              _dev_ptr(exp_avg_sq, "exp_avg_sq"), _dev_ptr(params_out, "params_out"),
                              pdt, n, _dev_ptr(scalars, "scalars"), _dev_ptr(state, "state"),
                              _stream(stream)))
+
+
+def _host_ptr(x, what):
+    """Host buffer address: a CPU torch tensor or a C-contiguous numpy array."""
+    if x is None:
+        return None
+    if isinstance(x, torch.Tensor):
+        if x.device.type != "cpu" or not x.is_contiguous():
+            raise ZdsError(ZDS_EINVAL, "%s must be a contiguous host tensor" % what)
+        return x.data_ptr()
+    import numpy as np
+    if not isinstance(x, np.ndarray) or not x.flags["C_CONTIGUOUS"]:
+        raise ZdsError(ZDS_EINVAL, "%s must be a contiguous host array" % what)
+    return x.ctypes.data
+
+
+_NP_DT = {"float16": ZDS_FP16, "float32": ZDS_FP32}
+
+
+def _host_dtype(x, declared=None):
+    if declared is not None:
+        return declared
+    if isinstance(x, torch.Tensor):
+        return dtype_code(x)
+    return _NP_DT[str(x.dtype)]
+
+
+def zds_cpu_adam_step(hp, grads, master, exp_avg, exp_avg_sq, params_out, scalars, state, num_threads=0,
+                      grad_dtype=None, param_dtype=None, n=None):
+    """AdamW on host buffers (see include/zds.h). Buffers are CPU torch
+    tensors or numpy arrays; 16-bit numpy data given as uint16 needs
+    grad_dtype / param_dtype (ZDS_FP16 or ZDS_BF16). scalars and state are
+    StepScalars / StepState host structs."""
+    n = (master.numel() if isinstance(master, torch.Tensor) else master.size) if n is None else n
+    gdt = _host_dtype(grads, grad_dtype)
+    pdt = ZDS_FP16 if params_out is None else _host_dtype(params_out, param_dtype)
+    _check(lib.zds_cpu_adam_step(ctypes.byref(hp), _host_ptr(grads, "grads"), gdt, _host_ptr(master, "master"),
+                                 _host_ptr(exp_avg, "exp_avg"), _host_ptr(exp_avg_sq, "exp_avg_sq"),
+                                 _host_ptr(params_out, "params_out"), pdt, n, ctypes.byref(scalars),
+                                 ctypes.byref(state), num_threads))
 
 
 def zds_step_state_init(state, cfg, t0=0, beta1_pow0=1.0, beta2_pow0=1.0, stream=None):
