@@ -396,3 +396,31 @@ def reduce_peer_slices(slices, src_dtype, dst, dst_dtype, accumulate):
     if accumulate:
         acc = widen(dst, dst_dtype) + acc
     return narrow(acc, dst_dtype)
+
+
+# ---------------------------------------------------------------------------
+# Checkpoint consolidation. [algomooc] 训练与恢复边界 and the checkpoint
+# paragraph of its spoken answer: every rank saves its own shard, and a
+# separate export step merges the ZeRO shards into one full fp32 state dict.
+# Reading: the rank shards, put side by side in rank order, are the flat
+# buffer; the full state of tensor t is the flat range [offset_t,
+# offset_t + numel_t) of it, and the padding between and after tensors is
+# dropped.
+# ---------------------------------------------------------------------------
+
+def consolidate(shards, numels, align):
+    """shards: (lo, hi, fp32 array of hi - lo elements) per rank, in any
+    order, together covering [0, padded total) without gaps or overlaps.
+    Returns the list of full per-tensor fp32 arrays."""
+    shards = sorted(shards, key=lambda s: s[0])
+    pos = 0
+    for lo, hi, a in shards:
+        if lo != pos or hi < lo or len(a) != hi - lo:
+            raise ValueError("shards do not tile the flat buffer at %d" % pos)
+        pos = hi
+    offsets, total = flat_layout(numels, align)
+    if pos < total:
+        raise ValueError("shards end at %d, the layout needs %d" % (pos, total))
+    flat = np.concatenate([np.asarray(a, dtype=np.float32) for _, _, a in shards]) if shards else \
+        np.zeros(0, np.float32)
+    return [flat[o:o + n].copy() for o, n in zip(offsets, numels)]

@@ -34,6 +34,8 @@ MUTANTS = {
  "decay_sign": ("c[\"decay\"] = np.float32(1.0 - float(lr) * float(wd))", "c[\"decay\"] = np.float32(1.0 + float(lr) * float(wd))"),
  "reduce_drop_last": ("    for sl in slices[1:]:", "    for sl in slices[1:-1]:"),
  "reduce_ignore_dst": ("        return dst + acc if accumulate else acc", "        return acc"),
+ "consolidate_unsorted": ("    shards = sorted(shards, key=lambda s: s[0])\n    pos = 0", "    pos = shards[0][0] if shards else 0"),
+ "consolidate_keep_pad": ("return [flat[o:o + n].copy() for o, n in zip(offsets, numels)]", "return [flat[i * n:(i + 1) * n].copy() for i, n in enumerate(numels)]"),
  "beta_pow_skip": ("st = replace(st, t=st.t + 1, beta1_pow=st.beta1_pow * b1, beta2_pow=st.beta2_pow * b2,", "st = replace(st, t=st.t + 1, beta1_pow=st.beta1_pow * b2, beta2_pow=st.beta2_pow * b1,"),
 }
 

@@ -659,3 +659,55 @@ def test_reduce_peers_accumulate_and_16bit_destination():
     out16 = O.reduce_peer_slices(bits, O.BF16, None, O.BF16, accumulate=False)
     for j in range(0, 3000, 7):
         assert int(out16[j]) == _bf16_rne_exact(int(plain[j:j + 1].view(np.uint32)[0]))
+
+
+# ---------------------------------------------------------------- consolidation
+
+def test_consolidate_hand_example():
+    # tensors of 3 and 2 elements, align 4: t0 at 0, t1 at 4, total 8; two
+    # ranks of 4 elements each (rank 0 = t0 + 1 pad, rank 1 = t1 + 2 pad)
+    r0 = np.array([1, 2, 3, -7], np.float32)
+    r1 = np.array([4, 5, -8, -9], np.float32)
+    t = O.consolidate([(4, 8, r1), (0, 4, r0)], [3, 2], 4)
+    assert [list(x) for x in t] == [[1, 2, 3], [4, 5]]
+    # one rank per element, align 1
+    t = O.consolidate([(i, i + 1, np.array([10 + i], np.float32)) for i in range(5)], [2, 0, 3], 1)
+    assert [list(x) for x in t] == [[10, 11], [], [12, 13, 14]]
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_consolidate_inverts_the_partition(seed):
+    # Brute force: place every tensor element at its flat index by hand, cut
+    # the buffer into the world's equal slices, shuffle them, merge back.
+    rng = np.random.default_rng(400 + seed)
+    numels = [int(x) for x in rng.integers(0, 300, int(rng.integers(1, 12)))]
+    align = int(rng.choice([1, 4, 16, 64]))
+    world = int(rng.integers(1, 9))
+    tensors = [rng.standard_normal(n).astype(np.float32) for n in numels]
+    pos, flat_index = 0, []
+    for n in numels:
+        flat_index.append(list(range(pos, pos + n)))
+        pos = -(-(pos + n) // align) * align
+    padded = -(-pos // (world * align)) * (world * align)
+    flat = np.full(padded, np.nan, np.float32)  # padding must never reach the output
+    for t, idx in zip(tensors, flat_index):
+        for v, i in zip(t, idx):
+            flat[i] = v
+    per = padded // world
+    shards = [(r * per, (r + 1) * per, flat[r * per:(r + 1) * per]) for r in range(world)]
+    assert all(O.shard_range(pos, world, r, align) == shards[r][:2] for r in range(world))
+    order = rng.permutation(world)
+    got = O.consolidate([shards[i] for i in order], numels, align)
+    assert len(got) == len(tensors)
+    for a, b in zip(got, tensors):
+        assert a.dtype == np.float32 and (a.view(np.uint32) == b.view(np.uint32)).all()
+
+
+def test_consolidate_rejects_gaps_and_overlaps():
+    a = np.zeros(4, np.float32)
+    with pytest.raises(ValueError):
+        O.consolidate([(0, 4, a), (5, 9, a)], [8], 1)      # gap
+    with pytest.raises(ValueError):
+        O.consolidate([(0, 4, a), (3, 7, a)], [7], 1)      # overlap
+    with pytest.raises(ValueError):
+        O.consolidate([(0, 4, a)], [6], 1)                 # too short
