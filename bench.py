@@ -34,9 +34,11 @@ def _parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="llama7b_s1",
                     choices=["llama7b_s1", "llama7b_s1_accum16", "llama7b_whole_1024", "llama65b_s1", "tiny",
-                             "llama7b_s2_intake8", "llama7b_s1_offload"])
+                             "llama7b_s2_intake8", "llama7b_s1_offload", "llama7b_s1_checkpoint"])
     ap.add_argument("--offload-threads", type=int, default=0,
                     help="host threads for the offloaded optimizer (0: all available)")
+    ap.add_argument("--ckpt-dir", default=None,
+                    help="directory for the checkpoint workload's shard file (default: a new one under $TMPDIR)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--unfused", action="store_true",
                     help="separate overflow/norm pass instead of the one fused into the last "
@@ -71,6 +73,10 @@ def _workload(name):
         # the C2 shard with its fp32 optimizer state in pinned host memory
         return dict(tensors=llama_7b_tensors(), world=8, rank=0, gdt="bf16", pdt="bf16", sigma=2e-3,
                     accum=1, scale=None, prior=True, mode="copy", offload=True)
+    if name == "llama7b_s1_checkpoint":
+        # save and reload the C2 shard's optimizer state (master, m, v, state)
+        return dict(tensors=llama_7b_tensors(), world=8, rank=0, gdt="bf16", pdt="bf16", sigma=2e-3,
+                    accum=1, scale=None, prior=True, mode="copy", checkpoint=True)
     if name == "llama65b_s1":
         return dict(tensors=llama_65b_tensors(), world=8, rank=0, gdt="bf16", pdt="bf16", sigma=1e-3,
                     accum=1, scale=None, prior=True, mode="copy")
@@ -288,6 +294,75 @@ def run_offload(args, w):
     }
 
 
+def run_checkpoint(args, w):
+    """Save the rank's device shard (fp32 master, exp_avg, exp_avg_sq and the
+    step state) to one file and load it back into fresh device buffers, timed
+    by wall clock; the reload is checked bit for bit against what was saved.
+    The file goes through the page cache (no fsync), so a reload right after
+    a save reads host memory, not the disk."""
+    import shutil
+    import tempfile
+    import torch
+    from zero_sharded_mixed_tensor_amd import zds
+    from zero_sharded_mixed_tensor_amd.step import ShardStep
+
+    numels = [n for _, n in w["tensors"]]
+    _, total = zds.zds_flat_layout(numels, 64)
+    lo, hi = zds.zds_shard_range(total, w["world"], w["rank"], 64)
+    n = hi - lo
+    dev = torch.device("cuda", 0)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(4321)
+    src = [torch.empty(n, dtype=torch.float32, device=dev).normal_(0.0, s, generator=gen)
+           for s in (0.02, 0.1 * w["sigma"], w["sigma"])]
+    src[2].mul_(src[2]).mul_(0.001)
+    st = ShardStep(n, zds.hparams(), zds.scaler_config(dynamic=False, static_scale=1.0), t0=1,
+                   beta1_pow0=0.9, beta2_pow0=0.999)
+    dst = [torch.empty_like(x) for x in src]
+    state2 = zds.new_state()
+    meta = zds.checkpoint_meta(numels, w["world"], w["rank"], 64, stage=1)
+    made = args.ckpt_dir is None
+    d = tempfile.mkdtemp(prefix="zds_ckpt_", dir=os.environ.get("TMPDIR", "/tmp")) if made else args.ckpt_dir
+    path = os.path.join(d, "zero_rank%d.zckpt" % w["rank"])
+    reps = max(1, min(args.steps, 3))
+    file_bytes = 256 + 8 * len(numels) + 12 * n
+    try:
+        torch.cuda.synchronize()
+        saves, loads = [], []
+        for _ in range(reps):
+            t0 = time.perf_counter()
+            zds.zds_checkpoint_save(path, meta, numels, *src, st.state)
+            saves.append(time.perf_counter() - t0)
+            for x in dst:
+                x.fill_(float("nan"))
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            zds.zds_checkpoint_load(path, meta, numels, *dst, state2)
+            loads.append(time.perf_counter() - t0)
+            exact = all(torch.equal(a.view(torch.int32), b.view(torch.int32)) for a, b in zip(src, dst))
+            exact = exact and torch.equal(st.state, state2)
+            if not exact:
+                raise RuntimeError("the reloaded shard differs from the saved one")
+        assert os.path.getsize(path) == file_bytes
+    finally:
+        if made:
+            shutil.rmtree(d, ignore_errors=True)
+        elif os.path.exists(path):
+            os.remove(path)
+    save_s, load_s = min(saves), min(loads)
+    return {
+        "metric": "rank shard checkpoint save + reload throughput", "value": round(2 * file_bytes / (save_s + load_s) / 1e9, 2),
+        "unit": "GB/s", "n_gpus": 1, "steps": reps, "warmup": 0,
+        "ms_per_step": round((save_s + load_s) * 1e3, 1), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": args.workload, "params": n, "file_bytes": file_bytes,
+                   "sections": "master, exp_avg, exp_avg_sq (fp32) + 64-byte step state", "fsync": False},
+        "save_gbs": round(file_bytes / save_s / 1e9, 2), "load_gbs": round(file_bytes / load_s / 1e9, 2),
+        "save_ms": [round(x * 1e3, 1) for x in saves], "load_ms": [round(x * 1e3, 1) for x in loads],
+        "bit_exact_reload": True,
+    }
+
+
 # ------------------------------------------------------------------ CPU oracle part
 
 def run_cpu_baseline(w, sample, repeats, min_seconds=10.0):
@@ -346,6 +421,9 @@ def main():
     w = _workload(args.workload)
     if w.get("offload"):
         print(json.dumps(run_offload(args, w)), flush=True)
+        return 0
+    if w.get("checkpoint"):
+        print(json.dumps(run_checkpoint(args, w)), flush=True)
         return 0
     r = run_gpu(args, w)
     out = {

@@ -53,7 +53,9 @@ typedef enum zds_status {
   ZDS_EINVAL = 1, /* bad argument: null pointer, bad enum, size, range */
   ZDS_EALIGN = 2, /* a pointer is not aligned to its element size */
   ZDS_ENOMEM = 3, /* the library could not allocate its own memory */
-  ZDS_EHIP = 4    /* a HIP runtime call or kernel launch failed */
+  ZDS_EHIP = 4,   /* a HIP runtime call or kernel launch failed */
+  ZDS_EIO = 5     /* a file could not be opened, read or written, or is not a
+                     valid, intact checkpoint of this library */
 } zds_status;
 
 typedef enum zds_dtype { ZDS_FP16 = 0, ZDS_BF16 = 1, ZDS_FP32 = 2 } zds_dtype;
@@ -288,6 +290,76 @@ zds_status zds_cpu_adam_step(const zds_adamw_hparams *hp, const void *grads, zds
                              float *master, float *exp_avg, float *exp_avg_sq, void *params_out,
                              zds_dtype param_dtype, int64_t n, const zds_step_scalars *scalars,
                              const zds_step_state *state, int32_t num_threads);
+
+/* ---------------------------------------------------------------------------
+ * Sharded checkpoint / resume and consolidation (a next row). The engine saves
+ * and loads per-rank shard checkpoints to resume training when the library
+ * version, the topology and the configuration (world size, ZeRO stage,
+ * offload, format) match; merging the shards into one full fp32 state is a
+ * separate export step that resuming does not need ([algomooc] 训练与恢复边界
+ * and the checkpoint paragraph of the spoken answer).
+ * A rank's file holds its fp32 master / exp_avg / exp_avg_sq shard, its step
+ * state, the tensor table and a 64-bit hash per section; a save goes to
+ * "<path>.tmp" and is renamed over <path> only once complete.
+ * ------------------------------------------------------------------------- */
+
+#define ZDS_CHECKPOINT_FORMAT 1
+
+/* Where the arrays and the step state of a save / load live. */
+typedef enum zds_location { ZDS_ON_DEVICE = 0, ZDS_ON_HOST = 1 } zds_location;
+
+/* The partition a shard belongs to. lo, hi and flat_total must be what
+ * zds_flat_layout and zds_shard_range give for the tensor table, world,
+ * rank and flat_align; stage (1..3) and offload (0/1) record the run's
+ * configuration and must match on load. 48 bytes. */
+typedef struct zds_checkpoint_meta {
+  int32_t world;
+  int32_t rank;
+  int32_t flat_align;
+  int32_t stage;
+  int32_t offload;
+  int32_t num_tensors;
+  int64_t flat_total;
+  int64_t lo, hi;
+} zds_checkpoint_meta;
+
+/* Writes rank meta->rank's shard to `path`.
+ *   numel      host, meta->num_tensors entries: the tensor table
+ *   master, exp_avg, exp_avg_sq   hi - lo fp32 elements each, device or host
+ *              memory as `loc` says (with the state)
+ *   state      the 64-byte step state (device or host as `loc` says)
+ *   stream     ZDS_ON_DEVICE: the save first waits for the work already
+ *              enqueued on it, so it records the state that work leaves
+ * Synchronous: returns once the file is complete. EINVAL if meta does not
+ * match the tensor table's partition, EIO on a file error. */
+zds_status zds_checkpoint_save(const char *path, const zds_checkpoint_meta *meta, const int64_t *numel,
+                               const float *master, const float *exp_avg, const float *exp_avg_sq,
+                               const zds_step_state *state, zds_location loc, void *stream);
+
+/* Reads a file's meta and step state (host; state may be NULL) and, when
+ * numel_out is not NULL, up to max_tensors entries of its tensor table
+ * (EINVAL when the table has more). EIO for a file that is not an intact
+ * checkpoint of this format. */
+zds_status zds_checkpoint_read_meta(const char *path, zds_checkpoint_meta *meta, zds_step_state *state,
+                                    int64_t *numel_out, int32_t max_tensors);
+
+/* Restores rank expect->rank's shard from `path` into master / exp_avg /
+ * exp_avg_sq and the step state, in device or host memory as `loc` says. The
+ * file's meta must equal *expect field by field and its tensor table must
+ * equal numel (EINVAL otherwise: a different world size, rank, stage,
+ * offload setting or model); every section is checked against its hash (EIO
+ * on a mismatch). Synchronous. */
+zds_status zds_checkpoint_load(const char *path, const zds_checkpoint_meta *expect, const int64_t *numel,
+                               float *master, float *exp_avg, float *exp_avg_sq, zds_step_state *state,
+                               zds_location loc, void *stream);
+
+/* Consolidation: the world's num_files shard files (any order; ranks 0 ..
+ * world-1 of one run at one step) merged into full per-tensor fp32 state:
+ * out (host, out_numel = sum of the tensor table) receives the tensors one
+ * after another, unpadded, in table order. section 0 = master weights (the
+ * full fp32 state dict), 1 = exp_avg, 2 = exp_avg_sq. */
+zds_status zds_consolidate_fp32(const char *const *paths, int32_t num_files, int32_t section, float *out,
+                                int64_t out_numel);
 
 /* Row a3. Initialise the device step state from cfg with Adam step count t0
  * and powers beta1^t0, beta2^t0 (1, 1 for a fresh optimizer). */

@@ -501,6 +501,7 @@ extern "C" const char *zds_status_string(zds_status s) {
     case ZDS_EALIGN: return "misaligned pointer";
     case ZDS_ENOMEM: return "out of memory";
     case ZDS_EHIP: return "HIP error";
+    case ZDS_EIO: return "file error";
   }
   return "unknown status";
 }
@@ -509,3 +510,4 @@ extern "C" int32_t zds_abi_version(void) { return ZDS_ABI_VERSION; }
 
 static_assert(sizeof(zds_step_state) == 64, "zds_step_state is 64 bytes");
 static_assert(sizeof(zds_step_scalars) == 64, "zds_step_scalars is 64 bytes");
+static_assert(sizeof(zds_checkpoint_meta) == 48, "zds_checkpoint_meta is 48 bytes");

@@ -16,9 +16,10 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libzds.so")
 
-ZDS_OK, ZDS_EINVAL, ZDS_EALIGN, ZDS_ENOMEM, ZDS_EHIP = 0, 1, 2, 3, 4
+ZDS_OK, ZDS_EINVAL, ZDS_EALIGN, ZDS_ENOMEM, ZDS_EHIP, ZDS_EIO = 0, 1, 2, 3, 4, 5
 ZDS_FP16, ZDS_BF16, ZDS_FP32 = 0, 1, 2
 ZDS_COPY, ZDS_OVERWRITE, ZDS_ACCUMULATE = 0, 1, 2
+ZDS_ON_DEVICE, ZDS_ON_HOST = 0, 1
 
 STATE_BYTES = 64
 SCALARS_BYTES = 64
@@ -61,7 +62,17 @@ class StepScalars(ctypes.Structure):
                 ("reserved", ctypes.c_uint32 * 3)]
 
 
+class CheckpointMeta(ctypes.Structure):
+    _fields_ = [("world", ctypes.c_int32), ("rank", ctypes.c_int32), ("flat_align", ctypes.c_int32),
+                ("stage", ctypes.c_int32), ("offload", ctypes.c_int32), ("num_tensors", ctypes.c_int32),
+                ("flat_total", ctypes.c_int64), ("lo", ctypes.c_int64), ("hi", ctypes.c_int64)]
+
+    def as_tuple(self):
+        return tuple(getattr(self, f) for f, _ in self._fields_)
+
+
 assert ctypes.sizeof(StepState) == STATE_BYTES and ctypes.sizeof(StepScalars) == SCALARS_BYTES
+assert ctypes.sizeof(CheckpointMeta) == 48
 
 _P = ctypes.c_void_p
 _I32, _I64, _U32 = ctypes.c_int32, ctypes.c_int64, ctypes.c_uint32
@@ -87,6 +98,13 @@ _SIGS = {
                              _P, _P, _P]),
     "zds_cpu_adam_step": (_I32, [ctypes.POINTER(AdamWHparams), _P, _I32, _P, _P, _P, _P, _I32, _I64,
                                  ctypes.POINTER(StepScalars), ctypes.POINTER(StepState), _I32]),
+    "zds_checkpoint_save": (_I32, [ctypes.c_char_p, ctypes.POINTER(CheckpointMeta), _PI64, _P, _P, _P, _P,
+                                   _I32, _P]),
+    "zds_checkpoint_read_meta": (_I32, [ctypes.c_char_p, ctypes.POINTER(CheckpointMeta),
+                                        ctypes.POINTER(StepState), _PI64, _I32]),
+    "zds_checkpoint_load": (_I32, [ctypes.c_char_p, ctypes.POINTER(CheckpointMeta), _PI64, _P, _P, _P, _P,
+                                   _I32, _P]),
+    "zds_consolidate_fp32": (_I32, [ctypes.POINTER(ctypes.c_char_p), _I32, _I32, _P, _I64]),
     "zds_step_state_init": (_I32, [_P, ctypes.POINTER(ScalerConfig), _I64, ctypes.c_double,
                                    ctypes.c_double, _P]),
     "zds_loss_scaler_update": (_I32, [_P, _P, ctypes.POINTER(AdamWHparams), _P]),
@@ -356,6 +374,78 @@ def zds_cpu_adam_step(hp, grads, master, exp_avg, exp_avg_sq, params_out, scalar
                                  _host_ptr(exp_avg, "exp_avg"), _host_ptr(exp_avg_sq, "exp_avg_sq"),
                                  _host_ptr(params_out, "params_out"), pdt, n, ctypes.byref(scalars),
                                  ctypes.byref(state), num_threads))
+
+
+# ------------------------------------------------------------------ checkpoints
+
+def checkpoint_meta(numels, world, rank, flat_align, stage=1, offload=0):
+    """The CheckpointMeta of rank's shard of the layout of numels."""
+    _, total = zds_flat_layout(numels, flat_align)
+    lo, hi = zds_shard_range(total, world, rank, flat_align)
+    return CheckpointMeta(world, rank, flat_align, stage, int(offload), len(numels), total, lo, hi)
+
+
+def _is_device(x):
+    return isinstance(x, torch.Tensor) and x.device.type == "cuda"
+
+
+def _ckpt_buffers(master, exp_avg, exp_avg_sq, state):
+    """Location and addresses of a shard: all device tensors (state: the
+    64-byte device state), or all host buffers (state: a StepState)."""
+    if _is_device(master):
+        ptrs = [_dev_ptr(master, "master"), _dev_ptr(exp_avg, "exp_avg"), _dev_ptr(exp_avg_sq, "exp_avg_sq"),
+                _dev_ptr(state, "state")]
+        return ZDS_ON_DEVICE, ptrs
+    if not isinstance(state, StepState):
+        raise ZdsError(ZDS_EINVAL, "a host shard takes its state as a StepState")
+    ptrs = [_host_ptr(master, "master"), _host_ptr(exp_avg, "exp_avg"), _host_ptr(exp_avg_sq, "exp_avg_sq"),
+            ctypes.addressof(state)]
+    return ZDS_ON_HOST, ptrs
+
+
+def zds_checkpoint_save(path, meta, numels, master, exp_avg, exp_avg_sq, state, stream=None):
+    loc, p = _ckpt_buffers(master, exp_avg, exp_avg_sq, state)
+    _check(lib.zds_checkpoint_save(os.fsencode(path), ctypes.byref(meta), _i64arr(numels), p[0], p[1], p[2],
+                                   p[3], loc, _stream(stream) if loc == ZDS_ON_DEVICE else None))
+
+
+def zds_checkpoint_read_meta(path, max_tensors=1 << 20):
+    """(CheckpointMeta, StepState, tensor table) of a checkpoint file."""
+    meta, st = CheckpointMeta(), StepState()
+    _check(lib.zds_checkpoint_read_meta(os.fsencode(path), ctypes.byref(meta), ctypes.byref(st), None, 0))
+    table = (ctypes.c_int64 * max(1, meta.num_tensors))()
+    _check(lib.zds_checkpoint_read_meta(os.fsencode(path), ctypes.byref(meta), None, table,
+                                        min(meta.num_tensors, max_tensors)))
+    return meta, st, [int(x) for x in table[:meta.num_tensors]]
+
+
+def zds_checkpoint_load(path, meta, numels, master, exp_avg, exp_avg_sq, state, stream=None):
+    loc, p = _ckpt_buffers(master, exp_avg, exp_avg_sq, state)
+    _check(lib.zds_checkpoint_load(os.fsencode(path), ctypes.byref(meta), _i64arr(numels), p[0], p[1], p[2],
+                                   p[3], loc, _stream(stream) if loc == ZDS_ON_DEVICE else None))
+
+
+def zds_consolidate_fp32(paths, section=0, out=None):
+    """Merged fp32 tensors of a world's shard files: a flat float32 numpy
+    array, tensors one after another in table order (see
+    split_consolidated)."""
+    import numpy as np
+    _, _, numels = zds_checkpoint_read_meta(paths[0])
+    total = int(sum(numels))
+    if out is None:
+        out = np.empty(total, dtype=np.float32)
+    arr = (ctypes.c_char_p * len(paths))(*[os.fsencode(x) for x in paths])
+    n = out.numel() if isinstance(out, torch.Tensor) else out.size
+    _check(lib.zds_consolidate_fp32(arr, len(paths), section, _host_ptr(out, "out") if total else None, n))
+    return out
+
+
+def split_consolidated(flat, numels):
+    outs, a = [], 0
+    for n in numels:
+        outs.append(flat[a:a + n])
+        a += n
+    return outs
 
 
 def zds_step_state_init(state, cfg, t0=0, beta1_pow0=1.0, beta2_pow0=1.0, stream=None):
