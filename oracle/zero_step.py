@@ -424,3 +424,66 @@ def consolidate(shards, numels, align):
     flat = np.concatenate([np.asarray(a, dtype=np.float32) for _, _, a in shards]) if shards else \
         np.zeros(0, np.float32)
     return [flat[o:o + n].copy() for o, n in zip(offsets, numels)]
+
+
+# ---------------------------------------------------------------------------
+# 1-bit compression with error compensation (a next row). [csdn] §4.2
+# 通信压缩: 1-bit Adam sends only the sign of each gradient element and
+# compensates the compression error afterwards, on the receiving side.
+# Readings (the page gives no more detail):
+#  - the magnitude travels as one fp32 scale per chunk of `chunk` consecutive
+#    elements (the last chunk may be shorter): the chunk's root mean square,
+#    so that the decoded chunk keeps the L2 norm of what was encoded;
+#  - error compensation is error feedback: whatever the encoding lost is kept
+#    in an fp32 error buffer and added to the next input before it is
+#    encoded. Every end that encodes (the sender, and the receiver when it
+#    sends the combined result on) keeps its own buffer;
+#  - a sign bit is 1 for c >= 0 (so -0 encodes as +) and 0 otherwise (NaN
+#    included); bit b of 32-bit word w is element 32w + b, bits past the end
+#    are 0;
+#  - the receiver's decode of N peers' payloads is their sum, formed in fp32
+#    in peer order; the mean over peers is left to the caller (as for the
+#    Stage-2 intake above).
+# ---------------------------------------------------------------------------
+
+def onebit_compress(x, err, chunk):
+    """Encode c = x + err (fp32). Returns (words uint32[ceil(n/32)],
+    scales float32[ceil(n/chunk)], new_err float32[n]) with, per chunk j,
+    s_j = fp32(sqrt(sum(c_i^2) / len_j)) (exact squares, correctly rounded sum,
+    float64 divide and sqrt) and new_err_i = c_i - s_j * sign_i (one fp32
+    rounding)."""
+    x = np.asarray(x, np.float32)
+    c = x + np.asarray(err, np.float32)
+    n = c.size
+    pos = c >= np.float32(0.0)
+    scales = np.zeros(-(-n // chunk), np.float32)
+    new_err = np.empty(n, np.float32)
+    for j in range(scales.size):
+        a, b = j * chunk, min(n, (j + 1) * chunk)
+        sumsq = math.fsum(float(v) * float(v) for v in c[a:b])
+        s = np.float32(math.sqrt(sumsq / (b - a)))
+        scales[j] = s
+        new_err[a:b] = np.where(pos[a:b], c[a:b] - s, c[a:b] + s)
+    words = np.zeros(-(-n // 32), np.uint32)
+    for i in np.nonzero(pos)[0]:
+        words[i >> 5] |= np.uint32(1) << np.uint32(i & 31)
+    return words, scales, new_err
+
+
+def onebit_signs(words, n):
+    """+1 / -1 (fp32) of elements 0 .. n-1 of a packed sign stream."""
+    i = np.arange(n)
+    bit = (words[i >> 5] >> (i & 31).astype(np.uint32)) & np.uint32(1)
+    return np.where(bit == 1, np.float32(1.0), np.float32(-1.0))
+
+
+def onebit_decompress(payloads, n, chunk, dst, accumulate):
+    """payloads: [(words, scales)] of N peers. Returns the fp32 sum over
+    peers k = 0..N-1, in that order, of s_{k, chunk(i)} * sign_{k, i}; with
+    accumulate, dst + that sum."""
+    j = np.arange(n) // chunk
+    acc = None
+    for words, scales in payloads:
+        d = np.asarray(scales, np.float32)[j] * onebit_signs(words, n)
+        acc = d if acc is None else acc + d
+    return dst + acc if accumulate else acc

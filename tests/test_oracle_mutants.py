@@ -36,6 +36,13 @@ MUTANTS = {
  "reduce_ignore_dst": ("        return dst + acc if accumulate else acc", "        return acc"),
  "consolidate_unsorted": ("    shards = sorted(shards, key=lambda s: s[0])\n    pos = 0", "    pos = shards[0][0] if shards else 0"),
  "consolidate_keep_pad": ("return [flat[o:o + n].copy() for o, n in zip(offsets, numels)]", "return [flat[i * n:(i + 1) * n].copy() for i, n in enumerate(numels)]"),
+ "onebit_no_err": ("    c = x + np.asarray(err, np.float32)\n", "    c = x.copy()\n"),
+ "onebit_msb_first": ("words[i >> 5] |= np.uint32(1) << np.uint32(i & 31)", "words[i >> 5] |= np.uint32(1) << np.uint32(31 - (i & 31))"),
+ "onebit_mean_abs": ("s = np.float32(math.sqrt(sumsq / (b - a)))", "s = np.float32(math.fsum(abs(float(v)) for v in c[a:b]) / (b - a))"),
+ "onebit_full_len": ("s = np.float32(math.sqrt(sumsq / (b - a)))", "s = np.float32(math.sqrt(sumsq / chunk))"),
+ "onebit_err_sign": ("np.where(pos[a:b], c[a:b] - s, c[a:b] + s)", "np.where(pos[a:b], c[a:b] + s, c[a:b] - s)"),
+ "onebit_neg_zero": ("    pos = c >= np.float32(0.0)\n", "    pos = ~np.signbit(c)\n"),
+ "onebit_dec_sign": ("return np.where(bit == 1, np.float32(1.0), np.float32(-1.0))", "return np.where(bit == 1, np.float32(-1.0), np.float32(1.0))"),
  "beta_pow_skip": ("st = replace(st, t=st.t + 1, beta1_pow=st.beta1_pow * b1, beta2_pow=st.beta2_pow * b2,", "st = replace(st, t=st.t + 1, beta1_pow=st.beta1_pow * b2, beta2_pow=st.beta2_pow * b1,"),
 }
 

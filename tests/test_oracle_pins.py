@@ -711,3 +711,124 @@ def test_consolidate_rejects_gaps_and_overlaps():
         O.consolidate([(0, 4, a), (3, 7, a)], [7], 1)      # overlap
     with pytest.raises(ValueError):
         O.consolidate([(0, 4, a)], [6], 1)                 # too short
+
+
+# ---------------------------------------------------------------- 1-bit codec
+
+def _f32_sqrt_of_fraction(q):
+    """fp32 nearest to sqrt(q) for a rational q, from 60-digit decimal
+    arithmetic (far from any rounding tie for the values used here)."""
+    with decimal.localcontext() as ctx:
+        ctx.prec = 60
+        r = (decimal.Decimal(q.numerator) / decimal.Decimal(q.denominator)).sqrt()
+    return np.float32(float(r))
+
+
+def test_onebit_hand_example():
+    x = np.array([1, -2, 3, -4, 0, -0.0], np.float32)
+    words, scales, err = O.onebit_compress(x, np.zeros(6, np.float32), 4)
+    # signs + - + - (+0) (-0 counts as +): bits 0, 2, 4, 5
+    assert words.tolist() == [0b110101]
+    s = _f32_sqrt_of_fraction(Fraction(1 + 4 + 9 + 16, 4))
+    assert scales[0] == s and scales[1] == 0.0
+    assert err[:4].tolist() == [np.float32(1) - s, np.float32(-2) + s, np.float32(3) - s, np.float32(-4) + s]
+    assert err[4] == 0.0 and err[5] == 0.0
+    d = O.onebit_decompress([(words, scales)], 6, 4, None, accumulate=False)
+    assert d.tolist() == [s, -s, s, -s, 0.0, 0.0]
+
+
+def test_onebit_bit_layout():
+    n = 100
+    for i in (0, 1, 31, 32, 63, 64, 99):
+        x = -np.ones(n, np.float32)
+        x[i] = 1.0
+        words, _, _ = O.onebit_compress(x, np.zeros(n, np.float32), 64)
+        want = np.zeros(4, np.uint32)
+        want[i // 32] = np.uint32(1) << np.uint32(i % 32)
+        assert (words == want).all(), i
+    # NaN encodes as 0, and bits past the end stay 0
+    x = np.ones(40, np.float32)
+    x[3] = np.nan
+    words, scales, err = O.onebit_compress(x, np.zeros(40, np.float32), 64)
+    assert words.tolist() == [0xFFFFFFF7, 0xFF] and np.isnan(scales[0]) and np.isnan(err).all()
+
+
+@pytest.mark.parametrize("k", [-20, -3, 0, 5])
+def test_onebit_equal_magnitudes_are_exact(k):
+    rng = np.random.default_rng(50 + k)
+    a = np.float32(2.0 ** k * 1.375)
+    n = 3 * 256 + 17
+    c = np.where(rng.random(n) < 0.5, a, -a).astype(np.float32)
+    words, scales, err = O.onebit_compress(c, np.zeros(n, np.float32), 256)
+    assert (scales == a).all() and (err == 0).all()
+    assert (O.onebit_decompress([(words, scales)], n, 256, None, False) == c).all()
+    # the error buffer is added before encoding: x + err with err = -x encodes zeros
+    _, s0, e0 = O.onebit_compress(c, -c, 256)
+    assert (s0 == 0).all() and (e0 == 0).all()
+
+
+def test_onebit_partial_last_chunk_uses_its_length():
+    n = 1024 + 3
+    x = np.full(n, 0.5, np.float32)
+    x[-3:] = np.float32(-3.0)
+    _, scales, _ = O.onebit_compress(x, np.zeros(n, np.float32), 1024)
+    assert scales.tolist() == [0.5, 3.0]
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_onebit_keeps_norm_and_loses_only_rounding(seed):
+    rng = np.random.default_rng(60 + seed)
+    n, chunk = 5000, 512
+    x = (rng.standard_normal(n) * 10.0 ** rng.integers(-4, 2, n)).astype(np.float32)
+    e = (rng.standard_normal(n) * 1e-2).astype(np.float32)
+    words, scales, err = O.onebit_compress(x, e, chunk)
+    c = x + e
+    for j in range(scales.size):
+        a, b = j * chunk, min(n, (j + 1) * chunk)
+        exact = sum((Fraction(float(v)) ** 2 for v in c[a:b]), Fraction(0))
+        got = Fraction(float(scales[j])) ** 2 * (b - a)
+        assert abs(got - exact) <= exact * Fraction(1, 2 ** 22)        # one fp32 rounding of the RMS
+    d = O.onebit_decompress([(words, scales)], n, chunk, None, False)
+    assert ((d > 0) == (c >= 0)).all()
+    # decoded + new error == encoded input, up to the one rounding of the error
+    resid = np.abs(d.astype(np.float64) + err.astype(np.float64) - c.astype(np.float64))
+    assert (resid <= np.spacing(np.abs(err)).astype(np.float64) / 2 + 0.0).all()
+
+
+def test_onebit_error_feedback_telescopes():
+    # sum over T steps of what was sent + the final error == T * x + e0: the
+    # compression loses nothing over time but rounding
+    rng = np.random.default_rng(70)
+    n, chunk, T = 3000, 256, 40
+    x = rng.standard_normal(n).astype(np.float32)
+    e = np.zeros(n, np.float32)
+    sent = np.zeros(n, np.float64)
+    bound = np.zeros(n, np.float64)
+    for _ in range(T):
+        words, scales, e_new = O.onebit_compress(x, e, chunk)
+        sent += O.onebit_decompress([(words, scales)], n, chunk, None, False)
+        bound += np.spacing(np.abs(x + e)).astype(np.float64) + np.spacing(np.abs(e_new)).astype(np.float64)
+        e = e_new
+    assert (np.abs(sent + e - T * x.astype(np.float64)) <= bound).all()
+    assert np.abs(sent / T - x).max() < np.abs(e).max() / T + 1e-5
+
+
+def test_onebit_decompress_sums_peers_exactly():
+    # power-of-two magnitudes: every partial sum is exact, so the peer sum is
+    # the integer sum of the signed scales
+    rng = np.random.default_rng(80)
+    n, chunk, N = 2000, 128, 6
+    payloads, ints = [], []
+    for k in range(N):
+        exps = rng.integers(-3, 4, -(-n // chunk))
+        sgn = np.where(rng.random(n) < 0.5, 1, -1)
+        mag = (2.0 ** exps[np.arange(n) // chunk]).astype(np.float32)
+        words, scales, _ = O.onebit_compress((sgn * mag).astype(np.float32), np.zeros(n, np.float32), chunk)
+        assert (scales == 2.0 ** exps).all()
+        payloads.append((words, scales))
+        ints.append(sgn * (2.0 ** (exps[np.arange(n) // chunk] + 3)))  # scaled by 8: integers
+    want = np.sum(ints, axis=0) / 8.0
+    got = O.onebit_decompress(payloads, n, chunk, None, False)
+    assert (got == want).all()
+    base = rng.standard_normal(n).astype(np.float32)
+    assert (O.onebit_decompress(payloads, n, chunk, base.copy(), True) == base + got).all()
