@@ -439,15 +439,17 @@ def consolidate(shards, numels, align):
 #    encoded. Every end that encodes (the sender, and the receiver when it
 #    sends the combined result on) keeps its own buffer;
 #  - a sign bit is 1 for c >= 0 (so -0 encodes as +) and 0 otherwise (NaN
-#    included); bit b of 32-bit word w is element 32w + b, bits past the end
-#    are 0;
+#    included). The signs travel in 64-bit words, four per group of 256
+#    elements: bit l of word 4g + i is element 256g + 4l + i, so that word i
+#    of a group holds the i-th element of each of 64 consecutive quads; bits
+#    past the end are 0;
 #  - the receiver's decode of N peers' payloads is their sum, formed in fp32
 #    in peer order; the mean over peers is left to the caller (as for the
 #    Stage-2 intake above).
 # ---------------------------------------------------------------------------
 
 def onebit_compress(x, err, chunk):
-    """Encode c = x + err (fp32). Returns (words uint32[ceil(n/32)],
+    """Encode c = x + err (fp32). Returns (words uint64[4 * ceil(n/256)],
     scales float32[ceil(n/chunk)], new_err float32[n]) with, per chunk j,
     s_j = fp32(sqrt(sum(c_i^2) / len_j)) (exact squares, correctly rounded sum,
     float64 divide and sqrt) and new_err_i = c_i - s_j * sign_i (one fp32
@@ -464,16 +466,20 @@ def onebit_compress(x, err, chunk):
         s = np.float32(math.sqrt(sumsq / (b - a)))
         scales[j] = s
         new_err[a:b] = np.where(pos[a:b], c[a:b] - s, c[a:b] + s)
-    words = np.zeros(-(-n // 32), np.uint32)
+    words = np.zeros(4 * -(-n // 256), np.uint64)
     for i in np.nonzero(pos)[0]:
-        words[i >> 5] |= np.uint32(1) << np.uint32(i & 31)
+        g, r = divmod(int(i), 256)
+        lane, k = divmod(r, 4)
+        words[4 * g + k] |= np.uint64(1) << np.uint64(lane)
     return words, scales, new_err
 
 
 def onebit_signs(words, n):
     """+1 / -1 (fp32) of elements 0 .. n-1 of a packed sign stream."""
     i = np.arange(n)
-    bit = (words[i >> 5] >> (i & 31).astype(np.uint32)) & np.uint32(1)
+    word = 4 * (i // 256) + i % 4
+    lane = (i % 256) // 4
+    bit = (words[word] >> lane.astype(np.uint64)) & np.uint64(1)
     return np.where(bit == 1, np.float32(1.0), np.float32(-1.0))
 
 
