@@ -34,7 +34,8 @@ def _parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="llama7b_s1",
                     choices=["llama7b_s1", "llama7b_s1_accum16", "llama7b_whole_1024", "llama65b_s1", "tiny",
-                             "llama7b_s2_intake8", "llama7b_s1_offload", "llama7b_s1_checkpoint"])
+                             "llama7b_s2_intake8", "llama7b_s1_offload", "llama7b_s1_checkpoint",
+                             "llama7b_s1_onebit8"])
     ap.add_argument("--offload-threads", type=int, default=0,
                     help="host threads for the offloaded optimizer (0: all available)")
     ap.add_argument("--ckpt-dir", default=None,
@@ -77,6 +78,11 @@ def _workload(name):
         # save and reload the C2 shard's optimizer state (master, m, v, state)
         return dict(tensors=llama_7b_tensors(), world=8, rank=0, gdt="bf16", pdt="bf16", sigma=2e-3,
                     accum=1, scale=None, prior=True, mode="copy", checkpoint=True)
+    if name == "llama7b_s1_onebit8":
+        # 1-bit codec on the C2 shard: encode with error feedback, then the
+        # decode-sum of 8 peers' messages, chunk 2048
+        return dict(tensors=llama_7b_tensors(), world=8, rank=0, gdt="bf16", pdt="bf16", sigma=2e-3,
+                    accum=1, scale=None, prior=False, mode="copy", onebit=True, peers=8, chunk=2048)
     if name == "llama65b_s1":
         return dict(tensors=llama_65b_tensors(), world=8, rank=0, gdt="bf16", pdt="bf16", sigma=1e-3,
                     accum=1, scale=None, prior=True, mode="copy")
@@ -294,6 +300,70 @@ def run_offload(args, w):
     }
 
 
+def run_onebit(args, w):
+    """One rank's codec work per exchange on its shard: zds_onebit_compress of
+    an fp32 buffer with its error buffer, then zds_onebit_decompress of the
+    8 peers' messages into an fp32 buffer. Each kernel is timed with HIP
+    events on the stream it runs on."""
+    import torch
+    from zero_sharded_mixed_tensor_amd import zds
+    from workloads.device import draw_payload_, fill_normal_
+
+    numels = [n for _, n in w["tensors"]]
+    _, total = zds.zds_flat_layout(numels, 64)
+    lo, hi = zds.zds_shard_range(total, w["world"], w["rank"], 64)
+    n, chunk, N = hi - lo, w["chunk"], w["peers"]
+    x = fill_normal_(torch.empty(n, dtype=torch.float32, device="cuda"), w["sigma"], 91)
+    err = fill_normal_(torch.empty(n, dtype=torch.float32, device="cuda"), 1e-2 * w["sigma"], 92)
+    mine = zds.onebit_payload(n, chunk)
+    peers = [draw_payload_(*zds.onebit_payload(n, chunk), w["sigma"], 93 + k) for k in range(N)]
+    out = torch.empty(n, dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    enc_ms, dec_ms = [], []
+
+    def one(record):
+        if record:
+            ev[0].record(stream)
+        zds.zds_onebit_compress(x, err, chunk, *mine)
+        if record:
+            ev[1].record(stream)
+        zds.zds_onebit_decompress(peers, chunk, out)
+        if record:
+            ev[2].record(stream)
+
+    for _ in range(args.warmup):
+        one(False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        one(True)
+        torch.cuda.synchronize()
+        enc_ms.append(ev[0].elapsed_time(ev[1]))
+        dec_ms.append(ev[1].elapsed_time(ev[2]))
+    el = time.perf_counter() - t0
+    payload_b = (n + 255) // 256 * 32 + (n + chunk - 1) // chunk * 4  # sign words + scales
+    enc_b = 12 * n + payload_b
+    dec_b = N * payload_b + 4 * n
+    e_ms, d_ms = sum(enc_ms) / len(enc_ms), sum(dec_ms) / len(dec_ms)
+    enc_gbs = enc_b / (e_ms * 1e-3) / 1e9
+    return {
+        "metric": "1-bit codec elements/s (encode + 8-peer decode) and achieved HBM GB/s",
+        "value": round(n / ((e_ms + d_ms) * 1e-3), 1), "unit": "elements/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(e_ms + d_ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": args.workload, "elements": n, "chunk": chunk, "peers": N,
+                   "encode_bytes": enc_b, "decode_bytes": dec_b},
+        "kernels": {"encode": {"ms_avg": round(e_ms, 5), "gbs": round(enc_gbs, 1)},
+                    "decode": {"ms_avg": round(d_ms, 5), "gbs": round(dec_b / (d_ms * 1e-3) / 1e9, 1)}},
+        "roofline": {"kernel": "zds_onebit_compress", "bound": "hbm", "achieved": round(enc_gbs, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(enc_gbs / HBM_PEAK_GBS, 4),
+                     "bytes_per_element": round(enc_b / n, 4),
+                     "traffic": _traffic(args.workload, n, "onebit_encode_kernel")},
+        "wall_s": round(el, 3),
+    }
+
+
 def run_checkpoint(args, w):
     """Save the rank's device shard (fp32 master, exp_avg, exp_avg_sq and the
     step state) to one file and load it back into fresh device buffers, timed
@@ -400,15 +470,27 @@ def run_cpu_baseline(w, sample, repeats, min_seconds=10.0):
     return dict(value=n * done / dt, seconds=dt, n=n, repeats=done)
 
 
-def _traffic(workload, n):
-    """HBM bytes per launch of the Adam kernel from the committed rocprofv3
-    counter summary of this workload (FETCH_SIZE and WRITE_SIZE, each scaled
-    by a copy of known size), or None when there is none or the kernel's
-    sources changed since it was taken."""
+def _traffic(workload, n, kernel="adam_tile_kernel"):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
+    summary of this workload (FETCH_SIZE and WRITE_SIZE, each scaled by a
+    copy of known size), or None when there is none or the kernel's sources
+    changed since it was taken."""
     from zero_sharded_mixed_tensor_amd.profiling import traffic_from_summary
     path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
                         "%s_step_hbm_counters.md" % workload)
-    return traffic_from_summary(path, "adam_tile_kernel")
+    return traffic_from_summary(path, kernel)
+
+
+def _copy_calibration():
+    """torch's device copy of 1 GiB, 5 times: a kernel of known traffic for
+    scaling HBM byte counters."""
+    import torch
+    a = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(5):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    return {"bytes_read": 1 << 30, "bytes_written": 1 << 30, "launches": 5}
 
 
 def main():
@@ -421,6 +503,12 @@ def main():
     w = _workload(args.workload)
     if w.get("offload"):
         print(json.dumps(run_offload(args, w)), flush=True)
+        return 0
+    if w.get("onebit"):
+        out = run_onebit(args, w)
+        if args.copy_calibration:
+            out["copy_calibration"] = _copy_calibration()
+        print(json.dumps(out), flush=True)
         return 0
     if w.get("checkpoint"):
         print(json.dumps(run_checkpoint(args, w)), flush=True)
@@ -467,13 +555,7 @@ def main():
         },
     }
     if args.copy_calibration:
-        import torch
-        a = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
-        b = torch.empty_like(a)
-        for _ in range(5):
-            b.copy_(a)
-        torch.cuda.synchronize()
-        out["copy_calibration"] = {"bytes_read": 1 << 30, "bytes_written": 1 << 30, "launches": 5}
+        out["copy_calibration"] = _copy_calibration()
     if not args.no_cpu_baseline:
         c = run_cpu_baseline(w, args.cpu_sample, args.cpu_repeats)
         out["cpu_baseline"] = {

@@ -273,6 +273,42 @@ zds_status zds_reduce_peer_slices(const void *const *peer_ptrs, int32_t num_peer
                                   int64_t n, void *dst, zds_dtype dst_dtype, zds_accum_mode mode,
                                   void *stream);
 
+/* 1-bit compression with error compensation (a next row): the rank-local
+ * encode / decode of a sign-compressed exchange. 1-bit Adam sends only the
+ * sign of each element and compensates the compression error afterwards
+ * ([csdn] §4.2 通信压缩). The page gives no more; readings: a chunk of `chunk`
+ * consecutive elements (the last one may be shorter) sends one fp32 scale,
+ * its root mean square, with its signs; the error is fed back, i.e. added to
+ * the next input before it is encoded.
+ *
+ * zds_onebit_compress, all device pointers, enqueued on stream:
+ *   x        n fp32 values to encode (16-byte aligned)
+ *   error    n fp32, read and updated in place, or NULL (no error feedback:
+ *            encode x alone). With c = x + error: bit = c >= 0 (-0 is +),
+ *            s = fp32(sqrt(sum over the chunk of c^2 / its length)), squares
+ *            summed in float64; the new error is c - s (bit 1) or c + s.
+ *   chunk    1024, 2048, 4096, 8192 or 16384
+ *   words    4 * ceil(n / 256) uint64, 16-byte aligned: bit l of word
+ *            4g + i is element 256g + 4l + i (the lane mask of a wave whose
+ *            lane l holds quad l of group g); bits past n are 0
+ *   scales   ceil(n / chunk) fp32
+ * Non-finite inputs give non-finite scales (check for overflow first).
+ * HBM-bound: 12 B/element + the payload (1/8 B + 4/chunk B). */
+zds_status zds_onebit_compress(const float *x, float *error, int64_t n, int32_t chunk, uint64_t *words,
+                               float *scales, void *stream);
+
+/* Decode of num_peers (1..16) payloads of n elements each, all made with the
+ * same chunk: dst[i] (+)= sum over peers k = 0.. in that order of
+ * +-scales_k[i / chunk] (fp32, one rounding per add; with ZDS_ACCUMULATE the
+ * previous dst is added last). The mean over peers is left to the caller
+ * (pass K * N as accum_steps to the step). Words 8-byte aligned; dst: n
+ * fp32, 16-byte aligned, not overlapping any payload.
+ * Moves N/8 + 4N/chunk B of payload + 4 B (8 B accumulating) per element;
+ * with many peers the per-element select-and-add work, not HBM, bounds it. */
+zds_status zds_onebit_decompress(const uint64_t *const *peer_words, const float *const *peer_scales,
+                                 int32_t num_peers, int64_t n, int32_t chunk, float *dst, zds_accum_mode mode,
+                                 void *stream);
+
 /* Offloaded optimizer shard (a next row). ZeRO-Offload keeps the optimizer
  * state, and runs its update, in host memory ([aiqz] 卸载策略; [csdn] §4.3):
  * this is zds_adam_step on host buffers, bit-identical to the device kernel

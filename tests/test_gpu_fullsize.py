@@ -326,3 +326,49 @@ def test_llama7b_stage2_intake_eight_peers():
     want = _oracle_update(want_acc, "fp32", osc, ost, P0, M0, V0, "bf16")
     _compare_samples("7B stage-2 intake", idx, master, m, v, out, want)
     plan.close()
+
+
+def test_llama7b_onebit_codec_shard():
+    """1-bit codec at the 7B Stage-1 shard size (842,301,440 fp32 elements,
+    chunk 2048): the encode with error feedback checked against the oracle on
+    64 sampled chunks and the last one, and the 8-peer decode of random
+    payloads on the same chunks (the codec is chunk-local, so each sampled
+    chunk is an independent oracle case)."""
+    from workloads.device import draw_payload_, fill_normal_
+    say("full size: 1-bit codec on the Llama-7B shard")
+    numels = [n for _, n in llama_7b_tensors()]
+    _, total = O.flat_layout(numels, 64)
+    lo, hi = O.shard_range(total, 8, 0, 64)
+    n, chunk = hi - lo, 2048
+    nch = -(-n // chunk)
+    x = fill_normal_(torch.empty(n, dtype=torch.float32, device="cuda"), 2e-3, 71)
+    e = fill_normal_(torch.empty(n, dtype=torch.float32, device="cuda"), 2e-5, 72)
+    pick = np.unique(np.append(np.random.default_rng(73).integers(0, nch, 64), nch - 1))
+    spans = [(int(j) * chunk, min(n, (int(j) + 1) * chunk)) for j in pick]
+    before = [(x[a:b].cpu().numpy(), e[a:b].cpu().numpy()) for a, b in spans]
+    words, scales = zds.onebit_payload(n, chunk)
+    zds.zds_onebit_compress(x, e, chunk, words, scales)
+    torch.cuda.synchronize()
+    differ = 0
+    for (a, b), j, (xs, es) in zip(spans, pick, before):
+        ow, osc, oe = O.onebit_compress(xs, es, chunk)
+        assert (words[a // 64:4 * ((b + 255) // 256)].cpu().numpy().view(np.uint64) == ow).all(), j
+        s = scales[int(j):int(j) + 1].cpu().numpy()
+        ge = e[a:b].cpu().numpy()
+        if s[0] == osc[0]:
+            assert (ge.view(np.uint32) == oe.view(np.uint32)).all(), j
+        else:
+            differ += 1
+            assert abs(int(s.view(np.int32)[0]) - int(osc.view(np.int32)[0])) == 1, j
+            assert (np.abs(ge - oe) <= np.spacing(max(abs(s[0]), abs(osc[0])))).all(), j
+    assert differ <= 1
+    del x, e
+    peers = [draw_payload_(*zds.onebit_payload(n, chunk), 1e-3, 80 + k) for k in range(8)]
+    out = torch.empty(n, dtype=torch.float32, device="cuda")
+    zds.zds_onebit_decompress(peers, chunk, out)
+    torch.cuda.synchronize()
+    for (a, b), j in zip(spans, pick):
+        pay = [(pw[a // 64:4 * ((b + 255) // 256)].cpu().numpy().view(np.uint64), ps[int(j):int(j) + 1].cpu().numpy())
+               for pw, ps in peers]
+        want = O.onebit_decompress(pay, b - a, chunk, None, False)
+        assert (out[a:b].cpu().numpy().view(np.uint32) == want.view(np.uint32)).all(), j

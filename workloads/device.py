@@ -35,3 +35,14 @@ def draw_sources_(srcs, sigma, scale, seed, step):
         if s is not None:
             fill_normal_(s, sigma * scale, (int(seed) * 1_000_003 + int(step) * 4099 + t) & 0x7FFFFFFFFFFF)
     return srcs
+
+
+def draw_payload_(words, scales, sigma, seed):
+    """A random 1-bit message: uniformly random sign words (any integer
+    storage; filled as 32-bit halves) and per-chunk scales |N(0, sigma)|,
+    from torch's device generator."""
+    g = torch.Generator(device=words.device)
+    g.manual_seed(int(seed))
+    words.view(torch.int32).random_(-(1 << 31), 1 << 31, generator=g)
+    scales.normal_(0.0, float(sigma), generator=g).abs_()
+    return words, scales

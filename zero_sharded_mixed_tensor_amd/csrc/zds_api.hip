@@ -8,6 +8,7 @@
 #include <vector>
 
 #include "zds_internal.h"
+#include "zds_onebit.h"
 
 namespace zds {
 
@@ -362,6 +363,45 @@ extern "C" zds_status zds_reduce_peer_slices(const void *const *peer_ptrs, int32
   if (!aligned(dst, static_cast<uintptr_t>(dtype_size(dst_dtype)))) return fail(ZDS_EALIGN, "%s: dst misaligned", fn);
   return launch_reduce_peers(peer_ptrs, num_peers, src_dtype, n, dst, dst_dtype, mode == ZDS_ACCUMULATE,
                              static_cast<hipStream_t>(stream));
+}
+
+static bool onebit_chunk_ok(int32_t c) {
+  return c == 1024 || c == 2048 || c == 4096 || c == 8192 || c == 16384;
+}
+
+extern "C" zds_status zds_onebit_compress(const float *x, float *error, int64_t n, int32_t chunk, uint64_t *words,
+                                          float *scales, void *stream) {
+  clear_error();
+  const char *fn = "zds_onebit_compress";
+  if (!onebit_chunk_ok(chunk)) return fail(ZDS_EINVAL, "%s: chunk must be 1024, 2048, 4096, 8192 or 16384", fn);
+  if (n < 0) return fail(ZDS_EINVAL, "%s: n < 0", fn);
+  if (n == 0) return ZDS_OK;
+  if (!x || !words || !scales) return fail(ZDS_EINVAL, "%s: null pointer", fn);
+  if (!aligned(x, 16) || (error && !aligned(error, 16)))
+    return fail(ZDS_EALIGN, "%s: x and error must be 16-byte aligned", fn);
+  if (!aligned(words, 16) || !aligned(scales, 4))
+    return fail(ZDS_EALIGN, "%s: words must be 16-byte and scales 4-byte aligned", fn);
+  return launch_onebit_encode(x, error, n, chunk, words, scales, static_cast<hipStream_t>(stream));
+}
+
+extern "C" zds_status zds_onebit_decompress(const uint64_t *const *peer_words, const float *const *peer_scales,
+                                            int32_t num_peers, int64_t n, int32_t chunk, float *dst,
+                                            zds_accum_mode mode, void *stream) {
+  clear_error();
+  const char *fn = "zds_onebit_decompress";
+  if (num_peers < 1 || num_peers > kMaxPeers) return fail(ZDS_EINVAL, "%s: num_peers must be in [1, %d]", fn, kMaxPeers);
+  if (!onebit_chunk_ok(chunk)) return fail(ZDS_EINVAL, "%s: chunk must be 1024, 2048, 4096, 8192 or 16384", fn);
+  if (mode != ZDS_OVERWRITE && mode != ZDS_ACCUMULATE) return fail(ZDS_EINVAL, "%s: mode must be overwrite or accumulate", fn);
+  if (n < 0) return fail(ZDS_EINVAL, "%s: n < 0", fn);
+  if (n == 0) return ZDS_OK;
+  if (!peer_words || !peer_scales || !dst) return fail(ZDS_EINVAL, "%s: null pointer", fn);
+  for (int k = 0; k < num_peers; ++k) {
+    if (!peer_words[k] || !peer_scales[k]) return fail(ZDS_EINVAL, "%s: peer %d is null", fn, k);
+    if (!aligned(peer_words[k], 8) || !aligned(peer_scales[k], 4)) return fail(ZDS_EALIGN, "%s: peer %d misaligned", fn, k);
+  }
+  if (!aligned(dst, 16)) return fail(ZDS_EALIGN, "%s: dst must be 16-byte aligned", fn);
+  return launch_onebit_decode(peer_words, peer_scales, num_peers, n, chunk, dst, mode == ZDS_ACCUMULATE,
+                              static_cast<hipStream_t>(stream));
 }
 
 extern "C" size_t zds_workspace_bytes(int64_t n) {

@@ -98,6 +98,8 @@ _SIGS = {
                              _P, _P, _P]),
     "zds_cpu_adam_step": (_I32, [ctypes.POINTER(AdamWHparams), _P, _I32, _P, _P, _P, _P, _I32, _I64,
                                  ctypes.POINTER(StepScalars), ctypes.POINTER(StepState), _I32]),
+    "zds_onebit_compress": (_I32, [_P, _P, _I64, _I32, _P, _P, _P]),
+    "zds_onebit_decompress": (_I32, [ctypes.POINTER(_P), ctypes.POINTER(_P), _I32, _I64, _I32, _P, _I32, _P]),
     "zds_checkpoint_save": (_I32, [ctypes.c_char_p, ctypes.POINTER(CheckpointMeta), _PI64, _P, _P, _P, _P,
                                    _I32, _P]),
     "zds_checkpoint_read_meta": (_I32, [ctypes.c_char_p, ctypes.POINTER(CheckpointMeta),
@@ -374,6 +376,32 @@ def zds_cpu_adam_step(hp, grads, master, exp_avg, exp_avg_sq, params_out, scalar
                                  _host_ptr(exp_avg, "exp_avg"), _host_ptr(exp_avg_sq, "exp_avg_sq"),
                                  _host_ptr(params_out, "params_out"), pdt, n, ctypes.byref(scalars),
                                  ctypes.byref(state), num_threads))
+
+
+# ------------------------------------------------------------------ 1-bit codec
+
+def onebit_payload(n, chunk, device="cuda"):
+    """Device buffers of one encoded message: (words, scales)."""
+    return (torch.zeros(4 * ((n + 255) // 256), dtype=torch.int64, device=device),
+            torch.zeros((n + chunk - 1) // chunk, dtype=torch.float32, device=device))
+
+
+def zds_onebit_compress(x, error, chunk, words, scales, stream=None, n=None):
+    n = x.numel() if n is None else n
+    if x.dtype != torch.float32 or (error is not None and error.dtype != torch.float32):
+        raise ZdsError(ZDS_EINVAL, "x and error must be fp32")
+    _check(lib.zds_onebit_compress(_dev_ptr(x, "x"), _dev_ptr(error, "error"), n, chunk, _dev_ptr(words, "words"),
+                                   _dev_ptr(scales, "scales"), _stream(stream)))
+
+
+def zds_onebit_decompress(payloads, chunk, dst, mode=ZDS_OVERWRITE, stream=None, n=None):
+    """payloads: [(words, scales)] of the peers, in sum order."""
+    n = dst.numel() if n is None else n
+    if dst.dtype != torch.float32:
+        raise ZdsError(ZDS_EINVAL, "dst must be fp32")
+    W = (_P * len(payloads))(*[_dev_ptr(w, "words") for w, _ in payloads])
+    S = (_P * len(payloads))(*[_dev_ptr(s, "scales") for _, s in payloads])
+    _check(lib.zds_onebit_decompress(W, S, len(payloads), n, chunk, _dev_ptr(dst, "dst"), mode, _stream(stream)))
 
 
 # ------------------------------------------------------------------ checkpoints
