@@ -13,7 +13,10 @@
 // 16-bit loads, 16-byte fp32 accesses), lane l on quad l of a wave's range so
 // each wave-level access is contiguous. Unaligned entries fall back to
 // element-wise moves. Bytes per element: copy 2+2, overwrite 2+4,
-// accumulate 2+4+4. One block per chunk by default.
+// accumulate 2+4+4. A block takes a whole chunk in copy mode and half a
+// chunk in the fp32 modes, and issues all of its vector loads before its
+// first store, so the two dependent table lookups and the data latency are
+// paid once per block.
 #include "zds_device.h"
 #include "zds_internal.h"
 
@@ -28,6 +31,7 @@
 #ifndef ZDS_ACC_ONESHOT
 #define ZDS_ACC_ONESHOT 1
 #endif
+
 
 namespace zds {
 
@@ -45,81 +49,126 @@ __device__ __forceinline__ double sq_add(float x, double acc) {
   return fma(d, d, acc);  // x^2 is exact in float64
 }
 
+// Chunks a block takes per iteration: copy mode moves little per chunk, so a
+// block takes two and overlaps their table lookups and loads.
+// Work units per chunk: the fp32 modes move more bytes per element, so a
+// block takes half a chunk there and the whole chunk in copy mode; either way
+// a block issues all of its unit's vector loads before its first store and
+// pays the two dependent table lookups once.
+#ifndef ZDS_ACC_FP32_PARTS
+#define ZDS_ACC_FP32_PARTS 2
+#endif
+template <int MODE>
+constexpr int parts_per_chunk() { return MODE == ZDS_COPY ? 1 : ZDS_ACC_FP32_PARTS; }
+static_assert(kAccumChunk % (8 * ZDS_ACC_FP32_PARTS) == 0, "a unit holds whole vector accesses in every mode");
+
+// One work unit: where it reads and writes, and whether the vector path
+// applies (both ends 16-byte aligned, or 8-byte for 16-bit sources of the
+// fp32 modes).
+struct Piece {
+  const char *src;
+  int64_t d0;   // destination element offset
+  int64_t cnt;  // elements (0: nothing to do)
+  bool vec;
+};
+
+// Unit u: part u % P of chunk u / P of its entry.
+template <int SD, int MODE>
+__device__ __forceinline__ Piece unit_piece(const AccArgs &a, int64_t u) {
+  constexpr int P = parts_per_chunk<MODE>();
+  constexpr int64_t span = kAccumChunk / P;
+  const int32_t E = a.num_entries;
+  const int64_t *t = a.table;  // [start E][len E][dst E][chunk0 E+1][entry of each chunk]
+  const int64_t c = u / P;
+  const int64_t e = t[4 * E + 1 + c];
+  const int64_t local = (c - t[3 * E + e]) * kAccumChunk + (u % P) * span;
+  const int64_t rem = t[E + e] - local;
+  Piece pc;
+  pc.cnt = rem < 0 ? 0 : (rem < span ? rem : span);
+  pc.src = static_cast<const char *>(a.ptrs[e]) + (t[e] + local) * (SD == ZDS_FP32 ? 4 : 2);
+  pc.d0 = t[2 * E + e] + local;
+  if (MODE == ZDS_COPY)
+    pc.vec = aligned(pc.src, 16) && aligned(static_cast<uint16_t *>(a.dst) + pc.d0, 16);
+  else
+    pc.vec = aligned(pc.src, SD == ZDS_FP32 ? 16 : 8) && aligned(static_cast<float *>(a.dst) + pc.d0, 16);
+  return pc;
+}
+
 // MODE: ZDS_COPY (16-bit -> same 16-bit), ZDS_OVERWRITE / ZDS_ACCUMULATE
-// (SD -> fp32).
+// (SD -> fp32). Every vector load of a block iteration is issued before its
+// first store.
 template <int SD, int MODE, bool NORM>
 __global__ void __launch_bounds__(ZDS_ACC_BLOCK) accumulate_kernel(AccArgs a) {
+  constexpr int P = parts_per_chunk<MODE>();
+  constexpr int PER = MODE == ZDS_COPY ? 8 : 4;                                     // elements per access
+  constexpr int UPT = (kAccumChunk / P / PER + ZDS_ACC_BLOCK - 1) / ZDS_ACC_BLOCK;  // accesses per thread
+  const int64_t units = a.total_chunks * P;
   double ss = 0.0;
-  const int32_t E = a.num_entries;
-  const int64_t *start = a.table;
-  const int64_t *len = a.table + E;
-  const int64_t *dsto = a.table + 2 * E;
-  const int64_t *chunk0 = a.table + 3 * E;
-  const int64_t *chunk_entry = a.table + 4 * E + 1;
-  for (int64_t c = blockIdx.x; c < a.total_chunks; c += gridDim.x) {
-    const int64_t e = chunk_entry[c];
-    const int64_t local = (c - chunk0[e]) * kAccumChunk;
-    const int64_t rem = len[e] - local;
-    const int64_t cnt = rem < kAccumChunk ? rem : kAccumChunk;
-    const char *src = static_cast<const char *>(a.ptrs[e]) + (start[e] + local) * (SD == ZDS_FP32 ? 4 : 2);
-    const int64_t d0 = dsto[e] + local;
+  for (int64_t u = blockIdx.x; u < units; u += gridDim.x) {  // uniform per block
+    const Piece pc = unit_piece<SD, MODE>(a, u);
     if (MODE == ZDS_COPY) {
-      uint16_t *dst = static_cast<uint16_t *>(a.dst) + d0;
-      const uint16_t *s = reinterpret_cast<const uint16_t *>(src);
-      if (aligned(s, 16) && aligned(dst, 16)) {
-        const int64_t groups = cnt >> 3;
-        for (int64_t i = threadIdx.x; i < groups; i += ZDS_ACC_BLOCK) {
-          const u32x4 w = ld_stream(reinterpret_cast<const u32x4 *>(s) + i);
-          st_stream(reinterpret_cast<u32x4 *>(dst) + i, w);
+      const int64_t groups = pc.vec ? pc.cnt >> 3 : 0;
+      const u32x4 *s4 = reinterpret_cast<const u32x4 *>(pc.src);
+      u32x4 *d4 = reinterpret_cast<u32x4 *>(static_cast<uint16_t *>(a.dst) + pc.d0);
+      u32x4 w[UPT];
+#pragma unroll
+      for (int r = 0; r < UPT; ++r) {
+        const int64_t i = threadIdx.x + r * ZDS_ACC_BLOCK;
+        if (i < groups) w[r] = ld_stream(s4 + i);
+      }
+#pragma unroll
+      for (int r = 0; r < UPT; ++r) {
+        const int64_t i = threadIdx.x + r * ZDS_ACC_BLOCK;
+        if (i < groups) {
+          st_stream(d4 + i, w[r]);
           if (NORM) {
-            ss = sq_add(lo_of<SD>(w.x), ss); ss = sq_add(hi_of<SD>(w.x), ss);
-            ss = sq_add(lo_of<SD>(w.y), ss); ss = sq_add(hi_of<SD>(w.y), ss);
-            ss = sq_add(lo_of<SD>(w.z), ss); ss = sq_add(hi_of<SD>(w.z), ss);
-            ss = sq_add(lo_of<SD>(w.w), ss); ss = sq_add(hi_of<SD>(w.w), ss);
+            ss = sq_add(lo_of<SD>(w[r].x), ss); ss = sq_add(hi_of<SD>(w[r].x), ss);
+            ss = sq_add(lo_of<SD>(w[r].y), ss); ss = sq_add(hi_of<SD>(w[r].y), ss);
+            ss = sq_add(lo_of<SD>(w[r].z), ss); ss = sq_add(hi_of<SD>(w[r].z), ss);
+            ss = sq_add(lo_of<SD>(w[r].w), ss); ss = sq_add(hi_of<SD>(w[r].w), ss);
           }
-        }
-        for (int64_t j = (groups << 3) + threadIdx.x; j < cnt; j += ZDS_ACC_BLOCK) {
-          dst[j] = s[j];
-          if (NORM) ss = sq_add(widen1<SD>(s, j), ss);
-        }
-      } else {
-        for (int64_t j = threadIdx.x; j < cnt; j += ZDS_ACC_BLOCK) {
-          dst[j] = s[j];
-          if (NORM) ss = sq_add(widen1<SD>(s, j), ss);
         }
       }
+      // the tail of a vector piece, or a whole unaligned one
+      const uint16_t *s16 = reinterpret_cast<const uint16_t *>(pc.src);
+      uint16_t *d16 = static_cast<uint16_t *>(a.dst) + pc.d0;
+      for (int64_t j = (groups << 3) + threadIdx.x; j < pc.cnt; j += ZDS_ACC_BLOCK) {
+        d16[j] = s16[j];
+        if (NORM) ss = sq_add(widen1<SD>(s16, j), ss);
+      }
     } else {
-      float *dst = static_cast<float *>(a.dst) + d0;
-      if (aligned(src, SD == ZDS_FP32 ? 16 : 8) && aligned(dst, 16)) {
-        const int64_t quads = cnt >> 2;
-        for (int64_t q = threadIdx.x; q < quads; q += ZDS_ACC_BLOCK) {
-          float x[4];
-          load_quad<SD>(src, q, x);
-          if (MODE == ZDS_ACCUMULATE) {
-            float y[4];
-            load_quad<ZDS_FP32>(dst, q, y);
+      const int64_t quads = pc.vec ? pc.cnt >> 2 : 0;
+      float *d32 = static_cast<float *>(a.dst) + pc.d0;
+      float x[UPT][4], y[UPT][4];
 #pragma unroll
-            for (int k = 0; k < 4; ++k) x[k] = y[k] + x[k];
+      for (int r = 0; r < UPT; ++r) {
+        const int64_t q = threadIdx.x + r * ZDS_ACC_BLOCK;
+        if (q < quads) {
+          load_quad<SD>(pc.src, q, x[r]);
+          if (MODE == ZDS_ACCUMULATE) load_quad<ZDS_FP32>(d32, q, y[r]);
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < UPT; ++r) {
+        const int64_t q = threadIdx.x + r * ZDS_ACC_BLOCK;
+        if (q < quads) {
+          if (MODE == ZDS_ACCUMULATE) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) x[r][i] = y[r][i] + x[r][i];
           }
-          store_quad(dst, q, x);
+          store_quad(d32, q, x[r]);
           if (NORM) {
 #pragma unroll
-            for (int k = 0; k < 4; ++k) ss = sq_add(x[k], ss);
+            for (int i = 0; i < 4; ++i) ss = sq_add(x[r][i], ss);
           }
         }
-        for (int64_t j = (quads << 2) + threadIdx.x; j < cnt; j += ZDS_ACC_BLOCK) {
-          const float x = widen1<SD>(src, j);
-          const float r = MODE == ZDS_ACCUMULATE ? dst[j] + x : x;
-          dst[j] = r;
-          if (NORM) ss = sq_add(r, ss);
-        }
-      } else {
-        for (int64_t j = threadIdx.x; j < cnt; j += ZDS_ACC_BLOCK) {
-          const float x = widen1<SD>(src, j);
-          const float r = MODE == ZDS_ACCUMULATE ? dst[j] + x : x;
-          dst[j] = r;
-          if (NORM) ss = sq_add(r, ss);
-        }
+      }
+      // the tail of a vector piece, or a whole unaligned one
+      for (int64_t j = (quads << 2) + threadIdx.x; j < pc.cnt; j += ZDS_ACC_BLOCK) {
+        const float v = widen1<SD>(pc.src, j);
+        const float r = MODE == ZDS_ACCUMULATE ? d32[j] + v : v;
+        d32[j] = r;
+        if (NORM) ss = sq_add(r, ss);
       }
     }
   }
@@ -135,9 +184,10 @@ static void go(int64_t grid, hipStream_t s, const AccArgs &a) {
                      0, s, a);
 }
 
-int64_t accumulate_grid(int64_t total_chunks) {
+int64_t accumulate_grid(int64_t total_chunks, zds_accum_mode mode) {
+  const int64_t iters = total_chunks * (mode == ZDS_COPY ? parts_per_chunk<ZDS_COPY>() : parts_per_chunk<ZDS_OVERWRITE>());
   int64_t grid = static_cast<int64_t>(device_cu_count()) * ZDS_ACC_WAVES_PER_CU * 64 / ZDS_ACC_BLOCK;
-  if (ZDS_ACC_ONESHOT || grid > total_chunks) grid = total_chunks;
+  if (ZDS_ACC_ONESHOT || grid > iters) grid = iters;
   if (grid > max_blocks(ZDS_ACC_BLOCK)) grid = max_blocks(ZDS_ACC_BLOCK);
   if (grid < 1) grid = 1;
   return grid;
@@ -147,7 +197,7 @@ template <bool NORM>
 static zds_status dispatch(const PlanDev &p, const void *const *dev_ptrs, zds_dtype src, void *dst,
                            zds_accum_mode mode, double *partials, hipStream_t stream) {
   AccArgs a{p.table, p.num_entries, p.total_chunks, dev_ptrs, dst, partials};
-  const int64_t g = accumulate_grid(p.total_chunks);
+  const int64_t g = accumulate_grid(p.total_chunks, mode);
   if (mode == ZDS_COPY) {
     // fp16 and bf16 copies move the same bits; the squares need the type
     if (src == ZDS_BF16) go<ZDS_BF16, ZDS_COPY, NORM>(g, stream, a);

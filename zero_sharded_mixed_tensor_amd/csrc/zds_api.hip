@@ -318,7 +318,9 @@ extern "C" zds_status zds_grad_accumulate(zds_plan *plan, const void *const *src
 
 extern "C" size_t zds_plan_norm_workspace_bytes(const zds_plan *plan) {
   if (!plan) return 0;
-  return static_cast<size_t>(partials_workspace_doubles(accumulate_grid(plan->total_chunks))) * sizeof(double);
+  // the fp32 modes launch the most blocks, hence write the most partials
+  return static_cast<size_t>(partials_workspace_doubles(accumulate_grid(plan->total_chunks, ZDS_OVERWRITE))) *
+         sizeof(double);
 }
 
 extern "C" zds_status zds_grad_accumulate_norm(zds_plan *plan, const void *const *src_ptrs,
@@ -339,7 +341,7 @@ extern "C" zds_status zds_grad_accumulate_norm(zds_plan *plan, const void *const
   double *partials = static_cast<double *>(ws);
   zds_status st = accumulate_impl(fn, plan, src_ptrs, src_dtype, dst, dst_dtype, mode, partials, stream);
   if (st != ZDS_OK) return st;
-  return launch_norm_stage2(partials, accumulate_grid(plan->total_chunks), state_dev, accum_steps, max_norm,
+  return launch_norm_stage2(partials, accumulate_grid(plan->total_chunks, mode), state_dev, accum_steps, max_norm,
                             out_dev, static_cast<hipStream_t>(stream));
 }
 

@@ -50,9 +50,10 @@ zds_status launch_norm_stage2(double *partials, int64_t nparts, const zds_step_s
 // Doubles of workspace launch_norm_stage2 needs for nparts partials.
 int64_t partials_workspace_doubles(int64_t nparts);
 
-// Grid of the accumulate kernel for a plan with `total_chunks` chunks (also
-// the number of partial sums the fused norm writes).
-int64_t accumulate_grid(int64_t total_chunks);
+// Grid of the accumulate kernel in `mode` for a plan with `total_chunks`
+// chunks (also the number of partial sums the fused norm writes; largest in
+// the fp32 modes).
+int64_t accumulate_grid(int64_t total_chunks, zds_accum_mode mode);
 
 // Same as launch_accumulate, and each block also writes the float64 sum of
 // squares of the values it stored to partials[blockIdx].
@@ -83,7 +84,7 @@ constexpr int64_t max_blocks(int threads_per_block) {
 
 // Chunk size (elements) of the accumulate kernel's work items.
 #ifndef ZDS_ACC_CHUNK
-#define ZDS_ACC_CHUNK 4096
+#define ZDS_ACC_CHUNK 8192
 #endif
 constexpr int64_t kAccumChunk = ZDS_ACC_CHUNK;
 
