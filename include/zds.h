@@ -366,8 +366,10 @@ typedef struct zds_checkpoint_meta {
  *   state      the 64-byte step state (device or host as `loc` says)
  *   stream     ZDS_ON_DEVICE: the save first waits for the work already
  *              enqueued on it, so it records the state that work leaves
- * Synchronous: returns once the file is complete. EINVAL if meta does not
- * match the tensor table's partition, EIO on a file error. */
+ * Synchronous: returns once the file is complete (written through the page
+ * cache, not synced to disk). The arrays move in 32 MiB pieces on up to 8
+ * host threads with their own pinned buffers and streams. EINVAL if meta
+ * does not match the tensor table's partition, EIO on a file error. */
 zds_status zds_checkpoint_save(const char *path, const zds_checkpoint_meta *meta, const int64_t *numel,
                                const float *master, const float *exp_avg, const float *exp_avg_sq,
                                const zds_step_state *state, zds_location loc, void *stream);
@@ -384,7 +386,9 @@ zds_status zds_checkpoint_read_meta(const char *path, zds_checkpoint_meta *meta,
  * file's meta must equal *expect field by field and its tensor table must
  * equal numel (EINVAL otherwise: a different world size, rank, stage,
  * offload setting or model); every section is checked against its hash (EIO
- * on a mismatch). Synchronous. */
+ * on a mismatch; the arrays may then hold part of the file). Synchronous;
+ * the transfer runs on up to 8 host threads with their own pinned buffers
+ * and streams. */
 zds_status zds_checkpoint_load(const char *path, const zds_checkpoint_meta *expect, const int64_t *numel,
                                float *master, float *exp_avg, float *exp_avg_sq, zds_step_state *state,
                                zds_location loc, void *stream);

@@ -217,3 +217,30 @@ def test_read_meta_table_room():
     meta = zds.CheckpointMeta()
     with pytest.raises(zds.ZdsError):
         zds._check(zds.lib.zds_checkpoint_read_meta(b"x", ctypes.byref(meta), None, None, 3))
+
+
+def test_sections_of_several_pieces(tmp_path):
+    """Sections larger than one 32 MiB transfer piece (80 MB each here):
+    they are moved and hashed piece by piece on several threads."""
+    numels = [9_000_001, 11_000_003]
+    meta = zds.checkpoint_meta(numels, 1, 0, 64)
+    n = meta.hi - meta.lo
+    rng = np.random.default_rng(11)
+    arrays = [_bits_f32(rng, n) for _ in range(3)]
+    st = _state(rng)
+    p = str(tmp_path / "big.zckpt")
+    zds.zds_checkpoint_save(p, meta, numels, *arrays, st)
+    out = [np.empty(n, np.float32) for _ in range(3)]
+    zds.zds_checkpoint_load(p, meta, numels, *out, zds.StepState())
+    assert all(_same_bits(a, b) for a, b in zip(out, arrays))
+    got = zds.zds_consolidate_fp32([p], 2)
+    want = O.consolidate([(0, n, arrays[2])], numels, 64)
+    assert _same_bits(got, np.concatenate(want))
+    # a flipped byte in the third piece of exp_avg
+    _flip(p, 256 + 8 * len(numels) + 4 * n + 2 * (32 << 20) + 12345)
+    with pytest.raises(zds.ZdsError) as e:
+        zds.zds_checkpoint_load(p, meta, numels, *out, zds.StepState())
+    assert e.value.status == zds.ZDS_EIO and "exp_avg" in str(e.value)
+    with pytest.raises(zds.ZdsError):
+        zds.zds_consolidate_fp32([p], 1)
+    assert _same_bits(zds.zds_consolidate_fp32([p], 0), np.concatenate(O.consolidate([(0, n, arrays[0])], numels, 64)))
