@@ -187,7 +187,8 @@ zds_status zds_plan_entry(const zds_plan *plan, int32_t e, int64_t *out4);
  * update; the fp32 add rounds to nearest even. The source pointers are
  * copied to the device through the plan's pinned staging ring (8 slots), so
  * calls can be issued back to back without waiting; a call with the same
- * pointers as the previous one reuses that upload. A plan must not be used
+ * pointers as the previous one reuses that upload (on another stream than
+ * the previous call's, after a stream wait on it). A plan must not be used
  * from two host threads at once. */
 zds_status zds_grad_accumulate(zds_plan *plan, const void *const *src_ptrs, zds_dtype src_dtype,
                                void *dst, zds_dtype dst_dtype, zds_accum_mode mode, void *stream);

@@ -293,6 +293,35 @@ def test_accumulate_many_calls_reuse_staging():
     assert (to_host(acc).view(np.uint32) == wacc.view(np.uint32)).all()
 
 
+def test_accumulate_reused_upload_on_another_stream():
+    """A call that reuses the previous call's pointer upload on another stream
+    must not run before that upload: stream A is kept busy, the call on A
+    uploads the pointers, the next call (same pointers, its own destination,
+    no data dependency) runs on stream B."""
+    say("accumulate: reused pointer upload across streams")
+    numels, srcs_np, srcs = _make_table(np.random.default_rng(46), 9, "bf16")
+    _, total = O.flat_layout(numels, 64)
+    plan = zds.zds_plan_create(numels, 64, 0, total)
+    ent = O.shard_entries(numels, 64, 0, total)
+    a, b = torch.cuda.Stream(), torch.cuda.Stream()
+    busy = torch.ones(1 << 26, dtype=torch.float32, device="cuda")
+    outs = [torch.full((total,), 3.0, dtype=torch.float32, device="cuda") for _ in range(8)]
+    torch.cuda.synchronize()
+    for k in range(4):
+        with torch.cuda.stream(a):
+            for _ in range(20):
+                busy.mul_(1.0)
+            zds.zds_grad_accumulate(plan, srcs, outs[2 * k], zds.ZDS_OVERWRITE)
+        with torch.cuda.stream(b):
+            zds.zds_grad_accumulate(plan, srcs, outs[2 * k + 1], zds.ZDS_OVERWRITE)
+    torch.cuda.synchronize()
+    want = np.full(total, 3.0, np.float32)
+    O.flatten_accumulate(srcs_np, "bf16", ent, want, overwrite=True)
+    for o in outs:
+        assert (to_host(o).view(np.uint32) == want.view(np.uint32)).all()
+    plan.close()
+
+
 def test_sharded_updates_concatenate_to_unsharded():
     """Stage-1 invariant on the GPU: N shard updates with the global scalars
     equal the unsharded update bit for bit."""

@@ -149,7 +149,8 @@ struct zds_plan {
   hipEvent_t ev[kRing] = {};
   bool used[kRing] = {};
   uint32_t next = 0;
-  int last_slot = -1;  // slot holding the most recently uploaded pointer set
+  int last_slot = -1;                // slot holding the most recently uploaded pointer set
+  hipStream_t last_stream = nullptr;  // stream of the most recent launch
 };
 
 static void plan_free(zds_plan *p) {
@@ -288,6 +289,12 @@ static zds_status accumulate_impl(const char *fn, zds_plan *plan, const void *co
       if (he != hipSuccess) return hip_fail(he, "staging slot wait");
     }
   }
+  // a reused upload was enqueued on the stream of an earlier call: another
+  // stream must wait for it (ev[slot] follows the upload and that launch)
+  if (same && s != plan->last_stream) {
+    he = hipStreamWaitEvent(s, plan->ev[slot], 0);
+    if (he != hipSuccess) return hip_fail(he, "hipStreamWaitEvent");
+  }
   const void **h = plan->h_ptrs + static_cast<size_t>(slot) * E;
   const void **d = plan->d_ptrs + static_cast<size_t>(slot) * E;
   if (!same) {
@@ -301,6 +308,7 @@ static zds_status accumulate_impl(const char *fn, zds_plan *plan, const void *co
   he = hipEventRecord(plan->ev[slot], s);
   if (he != hipSuccess) return hip_fail(he, "hipEventRecord");
   plan->used[slot] = true;
+  plan->last_stream = s;
   if (!same) {
     plan->next += 1;
     plan->last_slot = static_cast<int>(slot);
