@@ -321,7 +321,8 @@ zds_status zds_onebit_decompress(const uint64_t *const *peer_words, const float 
  *   scalars, state   HOST copies of the step scalars / state (the norm pass
  *              runs on the device; copy the 64-byte structs down first); an
  *              overflow flag skips the update
- *   num_threads      host threads (0: all the process may use)
+ *   num_threads      host threads (0: the CPUs of the process's affinity
+ *                    mask)
  * Returns when the update is done. Host-memory bound, 28 B/param. */
 zds_status zds_cpu_adam_step(const zds_adamw_hparams *hp, const void *grads, zds_dtype grad_dtype,
                              float *master, float *exp_avg, float *exp_avg_sq, void *params_out,

@@ -38,6 +38,7 @@
 #include <thread>
 #include <vector>
 
+#include "zds_host.h"
 #include "zds_internal.h"
 
 namespace {
@@ -185,8 +186,8 @@ zds_status transfer(int fd, char *map, bool to_file, bool on_host, float *const 
   if (jobs == 0) return ZDS_OK;
   int dev = 0;
   if (!on_host && hipGetDevice(&dev) != hipSuccess) return fail(ZDS_EHIP, "%s: hipGetDevice", fn);
-  const unsigned hc = std::thread::hardware_concurrency();
-  const size_t workers = std::min<size_t>({static_cast<size_t>(kMaxWorkers), hc > 0 ? hc : 1, jobs});
+  const size_t workers =
+      std::min<size_t>({static_cast<size_t>(kMaxWorkers), static_cast<size_t>(host_thread_budget()), jobs});
 
   std::atomic<size_t> next(0);
   std::atomic<bool> bad(false);

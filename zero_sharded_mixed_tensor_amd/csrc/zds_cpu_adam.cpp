@@ -20,6 +20,7 @@
 #include <thread>
 #include <vector>
 
+#include "zds_host.h"
 #include "zds_scalar.h"
 
 namespace {
@@ -131,7 +132,7 @@ extern "C" zds_status zds_cpu_adam_step(const zds_adamw_hparams *hp, const void 
   if (!grads || !master || !exp_avg || !exp_avg_sq) return fail(ZDS_EINVAL, "%s: null pointer", fn);
   HostArgs a{grads, grad_dtype, master, exp_avg, exp_avg_sq, params_out, param_dtype, scalars->grad_scale,
              adam_constants(*hp, state->beta1_pow, state->beta2_pow)};
-  int64_t T = num_threads > 0 ? num_threads : static_cast<int64_t>(std::thread::hardware_concurrency());
+  int64_t T = num_threads > 0 ? num_threads : host_thread_budget();
   if (T < 1) T = 1;
   const int64_t blocks = (n + kBlock - 1) / kBlock;
   if (T > blocks) T = blocks;
