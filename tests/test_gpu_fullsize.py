@@ -18,6 +18,9 @@ that hold at any size.
 * Flags, skips and the loss-scale trajectory are compared exactly.
 The Stage-1 shards run the bench's step (the norm fused into the flatten or
 the last accumulate call); the whole-7B run uses the separate norm pass.
+The next rows at the 7B shard size: the 8-peer Stage-2 intake, the 1-bit
+codec on sampled chunks, one offloaded step (host optimizer state) on
+sampled elements, and a 10.1 GB checkpoint round trip compared bit for bit.
 """
 
 import sys
@@ -372,3 +375,70 @@ def test_llama7b_onebit_codec_shard():
                for pw, ps in peers]
         want = O.onebit_decompress(pay, b - a, chunk, None, False)
         assert (out[a:b].cpu().numpy().view(np.uint32) == want.view(np.uint32)).all(), j
+
+
+def test_llama7b_offloaded_shard_one_step():
+    """The 7B Stage-1 shard with its fp32 optimizer state in pinned host
+    memory (the bench's offload workload): flatten on the device, device norm,
+    chunked download, host AdamW on all host threads, upload of the bf16
+    params. Sampled elements against the oracle from the pre-step inputs; the
+    clip scalars from the oracle's own sum over the whole flat buffer."""
+    from zero_sharded_mixed_tensor_amd.step import OffloadStep
+    say("full size: Llama-7B shard, offloaded optimizer state, one step")
+    numels, plan, ents, n, srcs, master, m, v = _setup_shard(llama_7b_tensors(), 8, 0, "bf16", 2e-3, True, 81)
+    draw_sources_(srcs, 2e-3, 1.0, 81, 1)
+    hP, hM, hV = (torch.empty(n, dtype=torch.float32, pin_memory=True) for _ in range(3))
+    hP.copy_(master)
+    hM.copy_(m)
+    hV.copy_(v)
+    del master, m, v
+    torch.cuda.empty_cache()
+    idx = _sample_index(n, ents)
+    hidx = idx.cpu()
+    P0, M0, V0 = hP[hidx].numpy(), hM[hidx].numpy(), hV[hidx].numpy()
+    off = OffloadStep(n, hP, hM, hV, torch.bfloat16, torch.bfloat16, zds.hparams(),
+                      zds.scaler_config(dynamic=False, static_scale=1.0), max_norm=1.0, t0=1, beta1_pow0=B1,
+                      beta2_pow0=B2)
+    bucket = torch.empty(n, dtype=torch.bfloat16, device="cuda")
+    out = torch.empty(n, dtype=torch.bfloat16, device="cuda")
+    zds.zds_grad_accumulate(plan, srcs, bucket, zds.ZDS_COPY)
+    sc = off.step(bucket, out)
+    torch.cuda.synchronize()
+    _check_copy(bucket, srcs, ents)
+    flat = _h16(bucket)
+    osc = _oracle_scalars(O.sum_of_squares(flat, "bf16"), 1.0, 1, 1.0, O.overflow_flag(flat, "bf16"))
+    _compare_scalars(sc, osc)
+    ost = O.scaler_init(dynamic=False, static_scale=1.0, t=1, beta1_pow=B1, beta2_pow=B2)
+    want = _oracle_update(flat[hidx.numpy()], "bf16", osc, ost, P0, M0, V0, "bf16")
+    oP, oM, oV, oOUT = want
+    assert_state_close("offload master", hP[hidx].numpy(), oP, 2)
+    assert_state_close("offload exp_avg", hM[hidx].numpy(), oM, 2)
+    assert_state_close("offload exp_avg_sq", hV[hidx].numpy(), oV, 2)
+    assert_p16_close("offload params", _h16(out[idx]), oOUT, 1)
+    assert off.dev.read_state().t == 2
+    plan.close()
+
+
+def test_llama7b_shard_checkpoint_round_trip(tmp_path):
+    """Save the 7B shard's optimizer state (a 10.1 GB file) and load it into
+    fresh device buffers: bit for bit equal, state included, and the file's
+    size is the format's."""
+    say("full size: Llama-7B shard checkpoint round trip")
+    numels = [n for _, n in llama_7b_tensors()]
+    meta = zds.checkpoint_meta(numels, 8, 0, 64)
+    n = meta.hi - meta.lo
+    arrs = [draw_master_(torch.empty(n, dtype=torch.float32, device="cuda"), 91 + k) for k in range(3)]
+    state = zds.new_state()
+    zds.zds_step_state_init(state, zds.scaler_config(initial_scale_power=13, window=7, hysteresis=2), 5, 0.59,
+                            0.995)
+    p = str(tmp_path / "zero_rank0.zckpt")
+    zds.zds_checkpoint_save(p, meta, numels, *arrs, state)
+    import os
+    assert os.path.getsize(p) == 256 + 8 * len(numels) + 12 * n
+    back = [torch.full_like(a, float("nan")) for a in arrs]
+    state2 = zds.new_state()
+    zds.zds_checkpoint_load(p, meta, numels, *back, state2)
+    for a, b in zip(arrs, back):
+        assert torch.equal(a.view(torch.int32), b.view(torch.int32))
+    assert torch.equal(state, state2)
+    os.remove(p)
