@@ -40,6 +40,8 @@ def _parse():
                     help="host threads for the offloaded optimizer (0: all available)")
     ap.add_argument("--ckpt-dir", default=None,
                     help="directory for the checkpoint workload's shard file (default: a new one under $TMPDIR)")
+    ap.add_argument("--graph", action="store_true",
+                    help="also time the step captured into a HIP graph and replayed (copy-mode workloads)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--unfused", action="store_true",
                     help="separate overflow/norm pass instead of the one fused into the last "
@@ -165,6 +167,8 @@ def run_gpu(args, w):
                    beta1_pow0=b1p, beta2_pow0=b2p)
     fused = not args.unfused and w["mode"] != "intake"
     pws = zds.new_plan_workspace(plan)
+    # the grads live in fixed buffers: their pointers are marshalled once
+    bound = zds.SourceSet(plan, srcs) if w["mode"] != "intake" else None
     torch.cuda.synchronize()
 
     ev = {k: [] for k in ("accumulate", "norm", "adam", "scaler")}
@@ -181,9 +185,9 @@ def run_gpu(args, w):
             zds.zds_reduce_peer_slices(peers, bucket, zds.ZDS_OVERWRITE)
         for k, md in enumerate(modes):
             if fused and k == len(modes) - 1:
-                st.accumulate_norm(plan, srcs, bucket, md, pws)
+                st.accumulate_norm(plan, bound, bucket, md, pws)
             else:
-                zds.zds_grad_accumulate(plan, srcs, bucket, md)
+                zds.zds_grad_accumulate(plan, bound, bucket, md)
         e1 = mark() if record else None
         if not fused:
             st.norm(bucket)
@@ -231,7 +235,22 @@ def run_gpu(args, w):
         kern["intake"] = kern.pop("accumulate")
     step_bytes = (bpp["accum_total"] + bpp["norm"] + bpp["adam"]) * n
     ms_per_step = elapsed / args.steps * 1e3
+    graph = None
+    if args.graph and fused and w["mode"] == "copy":
+        # the same step captured once into a HIP graph, then replayed
+        g = st.capture(plan, bound, bucket, zds.ZDS_COPY, pws, master, m, v, p16)
+        for _ in range(max(1, args.warmup)):
+            g.replay()
+        torch.cuda.synchronize()
+        t_g = time.perf_counter()
+        for _ in range(args.steps):
+            g.replay()
+        torch.cuda.synchronize()
+        g_ms = (time.perf_counter() - t_g) / args.steps * 1e3
+        graph = {"ms_per_step": round(g_ms, 4), "params_per_s": round(n / (g_ms * 1e-3), 1),
+                 "vs_eager": round(ms_per_step / g_ms, 3)}
     return dict(n=n, entries=len(ents), elapsed=elapsed, ms_per_step=ms_per_step, kernels=kern, fused=fused,
+                graph=graph,
                 adam_gbs=achieved, step_gbs=step_bytes / (elapsed / args.steps) / 1e9,
                 step_bytes_per_param=bpp["accum_total"] + bpp["norm"] + bpp["adam"],
                 adam_bytes_per_param=bpp["adam"])
@@ -275,8 +294,10 @@ def run_offload(args, w):
     bucket = torch.empty(n, dtype=tdt[w["gdt"]], device=dev)
     p16 = torch.empty(n, dtype=tdt[w["pdt"]], device=dev)
 
+    bound = zds.SourceSet(plan, srcs)
+
     def one():
-        zds.zds_grad_accumulate(plan, srcs, bucket, zds.ZDS_COPY)
+        zds.zds_grad_accumulate(plan, bound, bucket, zds.ZDS_COPY)
         off.step(bucket, p16)
 
     for _ in range(args.warmup):
@@ -541,6 +562,7 @@ def main():
             "norm_fused_into_flatten": r["fused"],
         },
         "step_gbs": round(r["step_gbs"], 1),
+        **({"graph": r["graph"]} if r["graph"] else {}),
         "step_hbm_frac": round(r["step_gbs"] / HBM_PEAK_GBS, 4),
         "kernels": r["kernels"],
         "roofline": {

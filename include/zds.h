@@ -189,7 +189,12 @@ zds_status zds_plan_entry(const zds_plan *plan, int32_t e, int64_t *out4);
  * calls can be issued back to back without waiting; a call with the same
  * pointers as the previous one reuses that upload (on another stream than
  * the previous call's, after a stream wait on it). A plan must not be used
- * from two host threads at once. */
+ * from two host threads at once.
+ * HIP graphs: a call on a stream under capture records only its kernel. It
+ * must use the previous call's source pointers, after that eager call has
+ * completed (EINVAL otherwise); the slot holding them is then kept for the
+ * graph's replays and never refilled (a plan has 8 slots; the grads must
+ * stay at those addresses while the graph is used). */
 zds_status zds_grad_accumulate(zds_plan *plan, const void *const *src_ptrs, zds_dtype src_dtype,
                                void *dst, zds_dtype dst_dtype, zds_accum_mode mode, void *stream);
 

@@ -266,3 +266,59 @@ def test_offloaded_optimizer_shard_steps():
         assert (to_host(out) == o16).all(), k
         s = off.dev.read_state()
         assert (s.scale, s.t) == (np.float32(ost.scale), ost.t), k
+
+
+def test_tiny_shard_graph_replays():
+    """The tiny shard's step captured once into a HIP graph and replayed for
+    5 steps (grads refilled in place between replays, an overflow at step 3),
+    with eager work on the same plan between replays that cycles through more
+    source sets than the plan has staging slots. Every replay must equal the
+    eagerly run step bit for bit: state, params, step state and scalars."""
+    say("tiny shard: graph replays vs eager steps")
+    numels = [n for _, n in tiny_shard_sizes()]
+    offs, total, master = _flat_master(numels, 64, 0, 1)
+    cfg = dict(initial_scale_power=16, window=2, hysteresis=1)
+
+    def setup():
+        st = ShardStep(total, zds.hparams(), zds.scaler_config(**cfg), max_norm=1.0)
+        bufs = [to_dev(master, "fp32"), torch.zeros(total, dtype=torch.float32, device="cuda"),
+                torch.zeros(total, dtype=torch.float32, device="cuda"),
+                to_dev(O.narrow(master, "fp16"), "fp16")]
+        srcs = [torch.empty(n, dtype=torch.float16, device="cuda") for n in numels]
+        bucket = torch.zeros(total, dtype=torch.float16, device="cuda")
+        return st, bufs, srcs, bucket
+
+    def fill(srcs, k, scale):
+        for t, (o, n) in enumerate(zip(offs, numels)):
+            g = draw_grads(n, "fp16", 1e-3, scale, 0, 1, k, offset=o)
+            if k == 3 and t == 7:
+                g[5] = 0x7C00
+            srcs[t].copy_(to_dev(g, "fp16"))
+
+    plan_a = zds.zds_plan_create(numels, 64, 0, total)
+    plan_b = zds.zds_plan_create(numels, 64, 0, total)
+    ea, ba, sa, bka = setup()
+    eb, bb, sb, bkb = setup()
+    wsa, wsb = zds.new_plan_workspace(plan_a), zds.new_plan_workspace(plan_b)
+    graph = eb.capture(plan_b, sb, bkb, zds.ZDS_COPY, wsb, *bb)
+    others = [[torch.zeros(n, dtype=torch.float16, device="cuda") for n in numels] for _ in range(10)]
+    junk = torch.empty(total, dtype=torch.float16, device="cuda")
+    for k in range(1, 6):
+        scale = ea.read_state().scale
+        fill(sa, k, scale)
+        ea.accumulate_norm(plan_a, sa, bka, zds.ZDS_COPY, wsa)
+        ea.adam(bka, *ba)
+        ea.scaler()
+        fill(sb, k, eb.read_state().scale)
+        graph.replay()
+        for o in others:  # eager calls with other pointers between replays
+            zds.zds_grad_accumulate(plan_b, o, junk, zds.ZDS_COPY)
+        torch.cuda.synchronize()
+        for x, y in zip(ba, bb):
+            assert torch.equal(x.view(torch.int16 if x.element_size() == 2 else torch.int32),
+                               y.view(torch.int16 if y.element_size() == 2 else torch.int32)), k
+        assert bytes(ea.read_state()) == bytes(eb.read_state()), k
+        assert bytes(ea.read_scalars()) == bytes(eb.read_scalars()), k
+    assert eb.read_state().last_skip == 0 and ea.read_state().t == 4
+    plan_a.close()
+    plan_b.close()

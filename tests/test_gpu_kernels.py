@@ -474,3 +474,26 @@ def test_reduce_peer_slices_parity(N, sdt, ddt):
                 assert (got.view(np.uint32) == want.view(np.uint32)).all(), (n, acc)
             else:
                 assert (got == want).all(), (n, acc)
+
+
+def test_accumulate_with_bound_source_set():
+    """A SourceSet (pointers marshalled once) gives the same result as the
+    list, call after call, and is refused for a plan of another size."""
+    say("accumulate: bound source set")
+    numels, srcs_np, srcs = _make_table(np.random.default_rng(47), 12, "fp16")
+    _, total = O.flat_layout(numels, 64)
+    plan = zds.zds_plan_create(numels, 64, 0, total)
+    ent = O.shard_entries(numels, 64, 0, total)
+    bound = zds.SourceSet(plan, srcs)
+    acc = torch.zeros(total, dtype=torch.float32, device="cuda")
+    want = np.zeros(total, np.float32)
+    for k in range(3):
+        zds.zds_grad_accumulate(plan, bound, acc, zds.ZDS_OVERWRITE if k == 0 else zds.ZDS_ACCUMULATE)
+        O.flatten_accumulate(srcs_np, "fp16", ent, want, overwrite=(k == 0))
+    torch.cuda.synchronize()
+    assert (to_host(acc).view(np.uint32) == want.view(np.uint32)).all()
+    other = zds.zds_plan_create(numels[:-1], 64, 0, O.flat_layout(numels[:-1], 64)[1])
+    with pytest.raises(zds.ZdsError):
+        zds.zds_grad_accumulate(other, bound, acc, zds.ZDS_OVERWRITE)
+    other.close()
+    plan.close()

@@ -148,6 +148,7 @@ struct zds_plan {
   const void **h_ptrs = nullptr;  // pinned, kRing * E
   hipEvent_t ev[kRing] = {};
   bool used[kRing] = {};
+  bool pinned[kRing] = {};  // read by a captured graph on every replay: never refilled
   uint32_t next = 0;
   int last_slot = -1;                // slot holding the most recently uploaded pointer set
   hipStream_t last_stream = nullptr;  // stream of the most recent launch
@@ -279,10 +280,31 @@ static zds_status accumulate_impl(const char *fn, zds_plan *plan, const void *co
     const void **prev = plan->h_ptrs + static_cast<size_t>(plan->last_slot) * E;
     for (int32_t i = 0; i < E && same; ++i) same = prev[i] == src_ptrs[plan->entries[4 * static_cast<size_t>(i)]];
   }
+  // Under stream capture the launch is recorded into a graph and replayed
+  // later: it may only read an upload that is already complete (the caller
+  // ran the same source set eagerly and synchronized), and that slot is then
+  // never refilled. No upload, event record or wait is captured.
+  hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+  he = hipStreamIsCapturing(s, &cap);
+  if (he != hipSuccess) return hip_fail(he, "hipStreamIsCapturing");
+  if (cap != hipStreamCaptureStatusNone) {
+    if (!same)
+      return fail(ZDS_EINVAL,
+                  "%s: under stream capture the source pointers must be those of the previous call, after that "
+                  "call has completed (run it once eagerly and synchronize before capturing)", fn);
+    plan->pinned[plan->last_slot] = true;
+    const void **dp = plan->d_ptrs + static_cast<size_t>(plan->last_slot) * E;
+    return partials ? launch_accumulate_norm(pd, dp, src_dtype, dst, dst_dtype, mode, partials, s)
+                    : launch_accumulate(pd, dp, src_dtype, dst, dst_dtype, mode, s);
+  }
   uint32_t slot;
   if (same) {
     slot = static_cast<uint32_t>(plan->last_slot);
   } else {
+    int k = 0;
+    while (k < kRing && plan->pinned[(plan->next + k) % kRing]) ++k;
+    if (k == kRing) return fail(ZDS_EINVAL, "%s: every staging slot is held by a captured graph", fn);
+    plan->next += static_cast<uint32_t>(k);
     slot = plan->next % kRing;
     if (plan->used[slot]) {
       he = hipEventSynchronize(plan->ev[slot]);

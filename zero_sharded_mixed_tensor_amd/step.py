@@ -47,6 +47,29 @@ class ShardStep:
         self.adam(grads, master, exp_avg, exp_avg_sq, params_out, stream)
         self.scaler(stream)
 
+    def capture(self, plan, srcs, dst, mode, ws, master, exp_avg, exp_avg_sq, params_out):
+        """Records one whole step (the flatten/accumulate call with the norm
+        fused in, AdamW, the scaler) into a HIP graph and returns it;
+        graph.replay() then runs a step with one launch from the host. The
+        graph reads the grads from srcs' addresses and writes the same
+        buffers on every replay: refill the grads in place between replays.
+        Nothing but kernels is captured (no memset, copy or event)."""
+        import torch
+        bound = srcs if isinstance(srcs, zds.SourceSet) else zds.SourceSet(plan, srcs)
+        # upload the source pointers in an eager call into a scratch buffer
+        # (the step's own buffers are left alone), and let it complete
+        scratch = torch.empty_like(dst)
+        zds.zds_grad_accumulate(plan, bound, scratch, zds.ZDS_COPY if mode == zds.ZDS_COPY else zds.ZDS_OVERWRITE)
+        torch.cuda.synchronize()
+        del scratch
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            self.accumulate_norm(plan, bound, dst, mode, ws)
+            self.adam(dst, master, exp_avg, exp_avg_sq, params_out)
+            self.scaler()
+        graph.bound_sources = bound  # keeps the grads' storages alive with the graph
+        return graph
+
     def read_state(self):
         return zds.read_state(self.state)
 

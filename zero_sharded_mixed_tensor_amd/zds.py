@@ -255,10 +255,33 @@ def zds_plan_create(numels, flat_align, lo, hi):
 
 # ------------------------------------------------------------------ hot calls
 
+class SourceSet:
+    """A plan's source tensors, marshalled once: a training loop whose grads
+    live in fixed buffers binds them once and passes the set on every call
+    instead of the list (building the pointer array costs about 0.5 us per
+    tensor per call). Keeps the tensors' storages alive; rebind after
+    replacing a tensor or its storage."""
+
+    def __init__(self, plan, srcs):
+        self.ptrs, self.dtype = _src_array(plan, srcs)
+        self._storages = [None if t is None else t.untyped_storage() for t in srcs]
+        self.num_tensors = len(srcs)
+
+
+def _sources(plan, srcs):
+    if isinstance(srcs, SourceSet):
+        if srcs.num_tensors != plan.num_tensors:
+            raise ZdsError(ZDS_EINVAL, "source set of %d tensors for a plan of %d" % (srcs.num_tensors,
+                                                                                      plan.num_tensors))
+        return srcs.ptrs, srcs.dtype
+    return _src_array(plan, srcs)
+
+
 def zds_grad_accumulate(plan, srcs, dst, mode, stream=None):
     """srcs: one device tensor per tensor of the plan's layout (None where the
-    plan has no entry); dst: the flat device buffer of the plan's range."""
-    ptrs, sdt = _src_array(plan, srcs)
+    plan has no entry), or a SourceSet of them; dst: the flat device buffer
+    of the plan's range."""
+    ptrs, sdt = _sources(plan, srcs)
     _check(lib.zds_grad_accumulate(plan.handle, ptrs, sdt, _dev_ptr(dst, "dst"), dtype_code(dst),
                                    mode, _stream(stream)))
 
@@ -287,7 +310,7 @@ def zds_plan_norm_workspace_bytes(plan):
 def zds_grad_accumulate_norm(plan, srcs, dst, mode, accum_steps, max_norm, state, scalars, ws, stream=None):
     """zds_grad_accumulate plus the step's overflow flag, norm and clip
     scalars formed from the stored values (see include/zds.h)."""
-    ptrs, sdt = _src_array(plan, srcs)
+    ptrs, sdt = _sources(plan, srcs)
     _check(lib.zds_grad_accumulate_norm(plan.handle, ptrs, sdt, _dev_ptr(dst, "dst"), dtype_code(dst), mode,
                                         accum_steps, max_norm, _dev_ptr(state, "state"),
                                         _dev_ptr(scalars, "scalars"), _dev_ptr(ws, "workspace"),
