@@ -50,8 +50,8 @@ constexpr uint32_t kHeaderBytes = 256;
 constexpr size_t kPiece = size_t(32) << 20;  // bytes per hashed and transferred piece
 constexpr int kMaxWorkers = 8;
 // 1: a save writes through a shared mapping of the preallocated file; 0:
-// through pwrite (10 GB rank file to /tmp on the GPU host: 7.3-9.8 GB/s
-// mapped; 10.7 GB/s for a first pwrite save, 3.4-4.6 for the next ones).
+// through pwrite (a 10.1 GB rank file saved to /tmp: 7.3-9.8 GB/s mapped;
+// 10.7 GB/s for a first pwrite save, 3.4-4.6 for the next ones).
 #ifndef ZDS_CKPT_MMAP
 #define ZDS_CKPT_MMAP 1
 #endif
