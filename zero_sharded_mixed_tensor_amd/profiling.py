@@ -32,6 +32,7 @@ KERNEL_SOURCES = {
     "adam_tile_kernel": ["csrc/zds_adam.hip", "csrc/zds_device.h", "csrc/zds_internal.h", "build.py"],
     "norm_stage1": ["csrc/zds_norm.hip", "csrc/zds_device.h", "csrc/zds_internal.h", "build.py"],
     "accumulate_kernel": ["csrc/zds_accumulate.hip", "csrc/zds_device.h", "csrc/zds_internal.h", "build.py"],
+    "reduce_peers_kernel": ["csrc/zds_reduce.hip", "csrc/zds_device.h", "csrc/zds_internal.h", "build.py"],
     "onebit_encode_kernel": ["csrc/zds_onebit.hip", "csrc/zds_onebit.h", "csrc/zds_device.h", "csrc/zds_internal.h",
                              "build.py"],
     "onebit_decode_kernel": ["csrc/zds_onebit.hip", "csrc/zds_onebit.h", "csrc/zds_device.h", "csrc/zds_internal.h",
