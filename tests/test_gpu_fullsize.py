@@ -442,3 +442,59 @@ def test_llama7b_shard_checkpoint_round_trip(tmp_path):
         assert torch.equal(a.view(torch.int32), b.view(torch.int32))
     assert torch.equal(state, state2)
     os.remove(p)
+
+
+def test_beyond_the_grid_cap_intake_and_codec():
+    """n = 2^33 + 1003 elements (past 2^32 and past the 2^23-block grid cap,
+    so blocks loop): the 2-peer bf16 intake into fp32, and the 1-bit encode
+    (chunk 1024) and decode, checked against the oracle on sampled chunks
+    including the ragged last one."""
+    from workloads.device import fill_normal_
+    n = (1 << 33) + 1003
+    chunk = 1024
+    say("beyond the grid cap: n =", n)
+    nch = -(-n // chunk)
+    rng = np.random.default_rng(101)
+    pick = np.unique(np.concatenate([rng.integers(0, nch, 48), [0, nch // 2, nch - 2, nch - 1]]))
+    spans = [(int(j) * chunk, min(n, (int(j) + 1) * chunk)) for j in pick]
+
+    # intake: 2 bf16 peers -> fp32
+    peers = [fill_normal_(torch.empty(n, dtype=torch.bfloat16, device="cuda"), 1e-3, 110 + k) for k in range(2)]
+    acc = torch.empty(n, dtype=torch.float32, device="cuda")
+    zds.zds_reduce_peer_slices(peers, acc, zds.ZDS_OVERWRITE)
+    torch.cuda.synchronize()
+    for a, b in spans:
+        want = O.reduce_peer_slices([_h16(p[a:b]) for p in peers], "bf16", None, "fp32", accumulate=False)
+        assert (acc[a:b].cpu().numpy().view(np.uint32) == want.view(np.uint32)).all(), (a, b)
+    del peers
+    torch.cuda.empty_cache()
+
+    # encode with error feedback: x is the intake result, err a small draw
+    err = fill_normal_(torch.empty(n, dtype=torch.float32, device="cuda"), 1e-5, 120)
+    before = [(acc[a:b].cpu().numpy(), err[a:b].cpu().numpy()) for a, b in spans]
+    words, scales = zds.onebit_payload(n, chunk)
+    zds.zds_onebit_compress(acc, err, chunk, words, scales)
+    torch.cuda.synchronize()
+    differ = 0
+    for (a, b), j, (xs, es) in zip(spans, pick, before):
+        ow, osc, oe = O.onebit_compress(xs, es, chunk)
+        assert (words[a // 64:4 * ((b + 255) // 256)].cpu().numpy().view(np.uint64) == ow).all(), j
+        s = scales[int(j):int(j) + 1].cpu().numpy()
+        ge = err[a:b].cpu().numpy()
+        if s[0] == osc[0]:
+            assert (ge.view(np.uint32) == oe.view(np.uint32)).all(), j
+        else:
+            differ += 1
+            assert abs(int(s.view(np.int32)[0]) - int(osc.view(np.int32)[0])) == 1, j
+    assert differ <= 1
+    del err
+    torch.cuda.empty_cache()
+
+    # decode of that one message into the (reused) fp32 buffer
+    zds.zds_onebit_decompress([(words, scales)], chunk, acc)
+    torch.cuda.synchronize()
+    for (a, b), j in zip(spans, pick):
+        pay = [(words[a // 64:4 * ((b + 255) // 256)].cpu().numpy().view(np.uint64),
+                scales[int(j):int(j) + 1].cpu().numpy())]
+        want = O.onebit_decompress(pay, b - a, chunk, None, False)
+        assert (acc[a:b].cpu().numpy().view(np.uint32) == want.view(np.uint32)).all(), j
