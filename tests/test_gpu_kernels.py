@@ -293,6 +293,34 @@ def test_accumulate_many_calls_reuse_staging():
     assert (to_host(acc).view(np.uint32) == wacc.view(np.uint32)).all()
 
 
+def test_binding_refuses_short_buffers_before_launch():
+    """A source shorter than its plan entries, or a dst shorter than the
+    plan's range, is refused by the binding; the plan stays usable and the
+    next full-length call matches the oracle."""
+    say("binding: short source and dst refused with a real plan")
+    numels = [1000, 77, 4096]
+    _, total = O.flat_layout(numels, 64)
+    lo, hi = O.shard_range(total, 2, 1, 64)
+    plan = zds.zds_plan_create(numels, 64, lo, hi)
+    ent = O.shard_entries(numels, 64, lo, hi)
+    host = [draw_grads(n, "bf16", 1e-3, 1.0, 3, 5, i) for i, n in enumerate(numels)]
+    devs = [to_dev(a, "bf16") for a in host]
+    dst = torch.zeros(hi - lo, dtype=torch.bfloat16, device="cuda")
+    t_last = ent[-1][0]
+    short = list(devs)
+    short[t_last] = devs[t_last][:-1]
+    with pytest.raises(zds.ZdsError, match="source %d holds" % t_last):
+        zds.zds_grad_accumulate(plan, short, dst, zds.ZDS_COPY)
+    with pytest.raises(zds.ZdsError, match="dst holds"):
+        zds.zds_grad_accumulate(plan, devs, dst[:-1], zds.ZDS_COPY)
+    zds.zds_grad_accumulate(plan, devs, dst, zds.ZDS_COPY)
+    want = np.zeros(hi - lo, np.uint16)
+    O.flatten_copy(host, ent, want)
+    torch.cuda.synchronize()
+    assert (to_host(dst).view(np.uint16) == want).all()
+    plan.close()
+
+
 def test_accumulate_reused_upload_on_another_stream():
     """A call that reuses the previous call's pointer upload on another stream
     must not run before that upload: stream A is kept busy, the call on A

@@ -158,6 +158,25 @@ def dtype_code(t):
         raise ZdsError(ZDS_EINVAL, "unsupported dtype %s" % t.dtype)
 
 
+def _numel(x):
+    return x.numel() if isinstance(x, torch.Tensor) else int(x.size)
+
+
+def _need(x, n, what):
+    """The library takes plain pointers and sizes: a buffer shorter than the
+    call's n would be read or written past its end, so the binding refuses it."""
+    if x is not None and _numel(x) < n:
+        raise ZdsError(ZDS_EINVAL, "%s holds %d elements, the call needs %d" % (what, _numel(x), n))
+
+
+def _need_bytes(x, nbytes, what):
+    if x is None:
+        return
+    have = _numel(x) * (x.element_size() if isinstance(x, torch.Tensor) else x.itemsize)
+    if have < nbytes:
+        raise ZdsError(ZDS_EINVAL, "%s holds %d bytes, the call needs %d" % (what, have, nbytes))
+
+
 def _dev_ptr(t, what):
     if t is None:
         return None
@@ -222,6 +241,12 @@ class Plan:
     def __init__(self, handle, num_tensors):
         self.handle = handle
         self.num_tensors = num_tensors
+        ents = self.entries()
+        # elements each source tensor must hold, and the destination's length
+        self.src_need = {}
+        for t, start, length, _ in ents:
+            self.src_need[t] = max(self.src_need.get(t, 0), start + length)
+        self.span = max((off + length for _, _, length, off in ents), default=0)
 
     @property
     def num_entries(self):
@@ -281,6 +306,7 @@ def zds_grad_accumulate(plan, srcs, dst, mode, stream=None):
     """srcs: one device tensor per tensor of the plan's layout (None where the
     plan has no entry), or a SourceSet of them; dst: the flat device buffer
     of the plan's range."""
+    _need(dst, plan.span, "dst")
     ptrs, sdt = _sources(plan, srcs)
     _check(lib.zds_grad_accumulate(plan.handle, ptrs, sdt, _dev_ptr(dst, "dst"), dtype_code(dst),
                                    mode, _stream(stream)))
@@ -291,6 +317,10 @@ def _src_array(plan, srcs):
         raise ZdsError(ZDS_EINVAL, "need %d source tensors" % plan.num_tensors)
     sdt = None
     ptrs = (ctypes.c_void_p * max(1, len(srcs)))()
+    for i, need in plan.src_need.items():
+        if srcs[i] is None:
+            raise ZdsError(ZDS_EINVAL, "source %d is None but the plan reads %d of its elements" % (i, need))
+        _need(srcs[i], need, "source %d" % i)
     for i, t in enumerate(srcs):
         if t is None:
             continue
@@ -310,6 +340,7 @@ def zds_plan_norm_workspace_bytes(plan):
 def zds_grad_accumulate_norm(plan, srcs, dst, mode, accum_steps, max_norm, state, scalars, ws, stream=None):
     """zds_grad_accumulate plus the step's overflow flag, norm and clip
     scalars formed from the stored values (see include/zds.h)."""
+    _need(dst, plan.span, "dst")
     ptrs, sdt = _sources(plan, srcs)
     _check(lib.zds_grad_accumulate_norm(plan.handle, ptrs, sdt, _dev_ptr(dst, "dst"), dtype_code(dst), mode,
                                         accum_steps, max_norm, _dev_ptr(state, "state"),
@@ -323,12 +354,12 @@ def zds_reduce_peer_slices(peers, dst, mode, stream=None, n=None):
     if not peers:
         raise ZdsError(ZDS_EINVAL, "need at least one peer slice")
     n = dst.numel() if n is None else n
+    _need(dst, n, "dst")
     sdt = dtype_code(peers[0])
-    arr = (ctypes.c_void_p * len(peers))()
     for k, t in enumerate(peers):
         if dtype_code(t) != sdt or t.numel() < n:
             raise ZdsError(ZDS_EINVAL, "peer %d: wrong dtype or too short" % k)
-        arr[k] = _dev_ptr(t, "peer %d" % k)
+    arr = (ctypes.c_void_p * len(peers))(*[_dev_ptr(t, "peer %d" % k) for k, t in enumerate(peers)])
     _check(lib.zds_reduce_peer_slices(arr, len(peers), sdt, n, _dev_ptr(dst, "dst"), dtype_code(dst), mode,
                                       _stream(stream)))
 
@@ -339,6 +370,7 @@ def zds_workspace_bytes(n):
 
 def zds_overflow_and_norm(grads, accum_steps, max_norm, state, scalars, ws, stream=None, n=None):
     n = grads.numel() if n is None else n
+    _need(grads, n, "grads")
     _check(lib.zds_overflow_and_norm(_dev_ptr(grads, "grads"), dtype_code(grads), n, accum_steps,
                                      max_norm, _dev_ptr(state, "state"), _dev_ptr(scalars, "scalars"),
                                      _dev_ptr(ws, "workspace"), ws.numel() * ws.element_size(),
@@ -348,11 +380,9 @@ def zds_overflow_and_norm(grads, accum_steps, max_norm, state, scalars, ws, stre
 def zds_adam_step(hp, grads, master, exp_avg, exp_avg_sq, params_out, scalars, state, stream=None,
                   n=None):
     n = master.numel() if n is None else n
-    for name, t in (("grads", grads), ("exp_avg", exp_avg), ("exp_avg_sq", exp_avg_sq)):
-        if t.numel() < n:
-            raise ZdsError(ZDS_EINVAL, "%s shorter than master" % name)
-    if params_out is not None and params_out.numel() < n:
-        raise ZdsError(ZDS_EINVAL, "params_out shorter than master")
+    for name, t in (("master", master), ("grads", grads), ("exp_avg", exp_avg), ("exp_avg_sq", exp_avg_sq),
+                    ("params_out", params_out)):
+        _need(t, n, name)
     pdt = dtype_code(params_out) if params_out is not None else ZDS_FP16
     _check(lib.zds_adam_step(ctypes.byref(hp), _dev_ptr(grads, "grads"), dtype_code(grads),
                              _dev_ptr(master, "master"), _dev_ptr(exp_avg, "exp_avg"),
@@ -392,7 +422,10 @@ def zds_cpu_adam_step(hp, grads, master, exp_avg, exp_avg_sq, params_out, scalar
     tensors or numpy arrays; 16-bit numpy data given as uint16 needs
     grad_dtype / param_dtype (ZDS_FP16 or ZDS_BF16). scalars and state are
     StepScalars / StepState host structs."""
-    n = (master.numel() if isinstance(master, torch.Tensor) else master.size) if n is None else n
+    n = _numel(master) if n is None else n
+    for name, t in (("master", master), ("grads", grads), ("exp_avg", exp_avg), ("exp_avg_sq", exp_avg_sq),
+                    ("params_out", params_out)):
+        _need(t, n, name)
     gdt = _host_dtype(grads, grad_dtype)
     pdt = ZDS_FP16 if params_out is None else _host_dtype(params_out, param_dtype)
     _check(lib.zds_cpu_adam_step(ctypes.byref(hp), _host_ptr(grads, "grads"), gdt, _host_ptr(master, "master"),
@@ -409,10 +442,20 @@ def onebit_payload(n, chunk, device="cuda"):
             torch.zeros((n + chunk - 1) // chunk, dtype=torch.float32, device=device))
 
 
+def _need_payload(words, scales, n, chunk):
+    if chunk < 1:
+        raise ZdsError(ZDS_EINVAL, "chunk must be positive")
+    _need_bytes(words, 32 * ((n + 255) // 256), "words")
+    _need_bytes(scales, 4 * ((n + chunk - 1) // chunk), "scales")
+
+
 def zds_onebit_compress(x, error, chunk, words, scales, stream=None, n=None):
     n = x.numel() if n is None else n
     if x.dtype != torch.float32 or (error is not None and error.dtype != torch.float32):
         raise ZdsError(ZDS_EINVAL, "x and error must be fp32")
+    _need(x, n, "x")
+    _need(error, n, "error")
+    _need_payload(words, scales, n, chunk)
     _check(lib.zds_onebit_compress(_dev_ptr(x, "x"), _dev_ptr(error, "error"), n, chunk, _dev_ptr(words, "words"),
                                    _dev_ptr(scales, "scales"), _stream(stream)))
 
@@ -422,6 +465,9 @@ def zds_onebit_decompress(payloads, chunk, dst, mode=ZDS_OVERWRITE, stream=None,
     n = dst.numel() if n is None else n
     if dst.dtype != torch.float32:
         raise ZdsError(ZDS_EINVAL, "dst must be fp32")
+    _need(dst, n, "dst")
+    for w, sc in payloads:
+        _need_payload(w, sc, n, chunk)
     W = (_P * len(payloads))(*[_dev_ptr(w, "words") for w, _ in payloads])
     S = (_P * len(payloads))(*[_dev_ptr(s, "scales") for _, s in payloads])
     _check(lib.zds_onebit_decompress(W, S, len(payloads), n, chunk, _dev_ptr(dst, "dst"), mode, _stream(stream)))
@@ -440,10 +486,13 @@ def _is_device(x):
     return isinstance(x, torch.Tensor) and x.device.type == "cuda"
 
 
-def _ckpt_buffers(master, exp_avg, exp_avg_sq, state):
+def _ckpt_buffers(meta, master, exp_avg, exp_avg_sq, state):
     """Location and addresses of a shard: all device tensors (state: the
     64-byte device state), or all host buffers (state: a StepState)."""
+    for name, t in (("master", master), ("exp_avg", exp_avg), ("exp_avg_sq", exp_avg_sq)):
+        _need(t, meta.hi - meta.lo, name)
     if _is_device(master):
+        _need_bytes(state, STATE_BYTES, "state")
         ptrs = [_dev_ptr(master, "master"), _dev_ptr(exp_avg, "exp_avg"), _dev_ptr(exp_avg_sq, "exp_avg_sq"),
                 _dev_ptr(state, "state")]
         return ZDS_ON_DEVICE, ptrs
@@ -455,7 +504,7 @@ def _ckpt_buffers(master, exp_avg, exp_avg_sq, state):
 
 
 def zds_checkpoint_save(path, meta, numels, master, exp_avg, exp_avg_sq, state, stream=None):
-    loc, p = _ckpt_buffers(master, exp_avg, exp_avg_sq, state)
+    loc, p = _ckpt_buffers(meta, master, exp_avg, exp_avg_sq, state)
     _check(lib.zds_checkpoint_save(os.fsencode(path), ctypes.byref(meta), _i64arr(numels), p[0], p[1], p[2],
                                    p[3], loc, _stream(stream) if loc == ZDS_ON_DEVICE else None))
 
@@ -471,7 +520,7 @@ def zds_checkpoint_read_meta(path, max_tensors=1 << 20):
 
 
 def zds_checkpoint_load(path, meta, numels, master, exp_avg, exp_avg_sq, state, stream=None):
-    loc, p = _ckpt_buffers(master, exp_avg, exp_avg_sq, state)
+    loc, p = _ckpt_buffers(meta, master, exp_avg, exp_avg_sq, state)
     _check(lib.zds_checkpoint_load(os.fsencode(path), ctypes.byref(meta), _i64arr(numels), p[0], p[1], p[2],
                                    p[3], loc, _stream(stream) if loc == ZDS_ON_DEVICE else None))
 
@@ -500,11 +549,14 @@ def split_consolidated(flat, numels):
 
 
 def zds_step_state_init(state, cfg, t0=0, beta1_pow0=1.0, beta2_pow0=1.0, stream=None):
+    _need_bytes(state, STATE_BYTES, "state")
     _check(lib.zds_step_state_init(_dev_ptr(state, "state"), ctypes.byref(cfg), t0, beta1_pow0,
                                    beta2_pow0, _stream(stream)))
 
 
 def zds_loss_scaler_update(state, scalars, hp, stream=None):
+    _need_bytes(state, STATE_BYTES, "state")
+    _need_bytes(scalars, SCALARS_BYTES, "scalars")
     _check(lib.zds_loss_scaler_update(_dev_ptr(state, "state"), _dev_ptr(scalars, "scalars"),
                                       ctypes.byref(hp), _stream(stream)))
 
