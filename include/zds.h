@@ -343,7 +343,11 @@ zds_status zds_cpu_adam_step(const zds_adamw_hparams *hp, const void *grads, zds
  * and the checkpoint paragraph of the spoken answer).
  * A rank's file holds its fp32 master / exp_avg / exp_avg_sq shard, its step
  * state, the tensor table and a 64-bit hash per section; a save goes to
- * "<path>.tmp" and is renamed over <path> only once complete.
+ * "<path>.tmp" and is renamed over <path> only once complete. The save does
+ * not fsync: the rename protects <path> against a crash of the process, not
+ * of the machine (a load then finds a torn file by its hashes and fails with
+ * ZDS_EIO). A caller that needs the save to survive a power loss fsyncs the
+ * file and its directory after the call.
  * ------------------------------------------------------------------------- */
 
 #define ZDS_CHECKPOINT_FORMAT 1
