@@ -5,6 +5,9 @@ A step is one pass of the whole hot path over the rank's shard:
   zds_grad_accumulate_norm (copy the per-tensor grads into the flat bucket,
   with the overflow/norm pass fused in; --unfused runs zds_grad_accumulate
   and zds_overflow_and_norm instead), zds_adam_step, zds_loss_scaler_update.
+  The Stage-2 intake workload sums the peers' slices with
+  zds_reduce_peer_slices_norm (the norm fused in the same way) in place of
+  the flatten.
 Default workload: the Llama-7B-shaped Stage-1 shard at N = 8 (rank 0: 33
 table entries, 842,301,440 params), bf16 grads N(0, 2e-3), fp32 master
 N(0, 0.02), moments shaped like one prior step, static loss scale 1, clip
@@ -95,10 +98,10 @@ def _workload(name):
 def _bytes_per_param(w, fused):
     """Algorithmic HBM bytes per param of each kernel of one step. Fused, the
     norm reads nothing extra: it is formed from the values the last
-    flatten/accumulate call stores."""
+    flatten/accumulate call (or the intake) stores."""
     g = 2
     if w["mode"] == "intake":
-        return dict(accum_total=2 * w["peers"] + 4, norm=4, adam=30)
+        return dict(accum_total=2 * w["peers"] + 4, norm=0 if fused else 4, adam=30)
     if w["mode"] == "accumulate":
         acc = 6 + 10 * (w["accum"] - 1)      # overwrite once, then accumulate
         return dict(accum_total=acc, norm=0 if fused else 4, adam=30)
@@ -165,8 +168,9 @@ def run_gpu(args, w):
            else zds.scaler_config(initial_scale_power=w["scale"], window=1000, hysteresis=1))
     st = ShardStep(n, zds.hparams(), cfg, max_norm=1.0, accum_steps=w["accum"], t0=t0,
                    beta1_pow0=b1p, beta2_pow0=b2p)
-    fused = not args.unfused and w["mode"] != "intake"
+    fused = not args.unfused
     pws = zds.new_plan_workspace(plan)
+    rws = zds.new_reduce_workspace(n) if w["mode"] == "intake" else None
     # the grads live in fixed buffers: their pointers are marshalled once
     bound = zds.SourceSet(plan, srcs) if w["mode"] != "intake" else None
     torch.cuda.synchronize()
@@ -182,7 +186,10 @@ def run_gpu(args, w):
         modes = ([zds.ZDS_OVERWRITE] + [zds.ZDS_ACCUMULATE] * (w["accum"] - 1)
                  if w["mode"] == "accumulate" else [] if w["mode"] == "intake" else [zds.ZDS_COPY])
         if w["mode"] == "intake":
-            zds.zds_reduce_peer_slices(peers, bucket, zds.ZDS_OVERWRITE)
+            if fused:
+                st.intake_norm(peers, bucket, zds.ZDS_OVERWRITE, rws)
+            else:
+                zds.zds_reduce_peer_slices(peers, bucket, zds.ZDS_OVERWRITE)
         for k, md in enumerate(modes):
             if fused and k == len(modes) - 1:
                 st.accumulate_norm(plan, bound, bucket, md, pws)
@@ -225,7 +232,8 @@ def run_gpu(args, w):
         if k == "accumulate":
             entry["gbs"] = round(bpp["accum_total"] * n / (ms * 1e-3) / 1e9, 1)
             if fused:
-                entry["includes"] = "overflow/norm fused into the last call"
+                entry["includes"] = ("overflow/norm fused into the intake" if w["mode"] == "intake"
+                                     else "overflow/norm fused into the last call")
         elif k in ("norm", "adam"):
             entry["gbs"] = round(bpp[k] * n / (ms * 1e-3) / 1e9, 1)
         kern[k] = entry

@@ -279,6 +279,24 @@ zds_status zds_reduce_peer_slices(const void *const *peer_ptrs, int32_t num_peer
                                   int64_t n, void *dst, zds_dtype dst_dtype, zds_accum_mode mode,
                                   void *stream);
 
+/* The Stage-2 intake with the step's row a2 fused in: the same as
+ * zds_reduce_peer_slices followed by zds_overflow_and_norm over dst
+ * (dst_dtype, n elements), except that the sum of squares is formed from the
+ * values as the kernel stores them (for a 16-bit dst, the rounded values), so
+ * the shard gradient is not read a second time. The overflow flag, norm and
+ * clip scalars are those row a2 defines for dst. The sum is accumulated in
+ * float64 per block in a fixed order, then the block partials in index
+ * order, so it is run-to-run identical for n and the pointers' alignment; it
+ * may differ from zds_overflow_and_norm's sum of the same data in the last
+ * bits (another order). n == 0 writes the scalars of an empty shard. Other
+ * arguments as for the two calls; ws holds at least
+ * zds_reduce_norm_workspace_bytes(n) bytes (8-byte aligned). */
+size_t zds_reduce_norm_workspace_bytes(int64_t n);
+zds_status zds_reduce_peer_slices_norm(const void *const *peer_ptrs, int32_t num_peers, zds_dtype src_dtype,
+                                       int64_t n, void *dst, zds_dtype dst_dtype, zds_accum_mode mode,
+                                       int32_t accum_steps, float max_norm, const zds_step_state *state_dev,
+                                       zds_step_scalars *out_dev, void *ws, size_t ws_bytes, void *stream);
+
 /* 1-bit compression with error compensation (a next row): the rank-local
  * encode / decode of a sign-compressed exchange. 1-bit Adam sends only the
  * sign of each element and compensates the compression error afterwards

@@ -328,6 +328,17 @@ def test_llama7b_stage2_intake_eight_peers():
     ost = O.scaler_init(dynamic=False, static_scale=1.0, t=1, beta1_pow=B1, beta2_pow=B2)
     want = _oracle_update(want_acc, "fp32", osc, ost, P0, M0, V0, "bf16")
     _compare_samples("7B stage-2 intake", idx, master, m, v, out, want)
+    # the intake with the norm fused in: the same shard gradient, and the
+    # oracle's scalars of it (its ~822K block partials take two folding levels)
+    say("full size: Llama-7B Stage-2 intake with the norm fused in")
+    st2 = ShardStep(n, zds.hparams(), zds.scaler_config(dynamic=False, static_scale=1.0), max_norm=1.0,
+                    accum_steps=8, t0=1, beta1_pow0=B1, beta2_pow0=B2)
+    acc2 = torch.empty(n, dtype=torch.float32, device="cuda")
+    zds.zds_reduce_peer_slices_norm(peers, acc2, zds.ZDS_OVERWRITE, 8, 1.0, st2.state, st2.scalars,
+                                    zds.new_reduce_workspace(n))
+    torch.cuda.synchronize()
+    assert torch.equal(acc2.view(torch.int32), acc.view(torch.int32))
+    _compare_scalars(st2.read_scalars(), osc)
     plan.close()
 
 

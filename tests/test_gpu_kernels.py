@@ -504,6 +504,64 @@ def test_reduce_peer_slices_parity(N, sdt, ddt):
                 assert (got == want).all(), (n, acc)
 
 
+@pytest.mark.parametrize("N", [1, 3, 8, 16])
+@pytest.mark.parametrize("sdt,ddt", [("bf16", "fp32"), ("fp16", "fp32"), ("bf16", "bf16"), ("fp16", "fp16")])
+def test_reduce_peer_slices_norm_parity(N, sdt, ddt):
+    """zds_reduce_peer_slices_norm: the stored values equal the oracle's
+    intake, and the scalars equal the oracle's overflow and norm of them."""
+    say("reduce peers + norm N=%d %s -> %s" % (N, sdt, ddt))
+    for n, offset in ((0, 0), (1, 0), (7, 0), (513, 0), (512 * 37 + 13, 0), (1024 * 2049 + 5, 0), (4099, 1)):
+        peers = [draw_grads(n, sdt, 1e-2, 1.0, 60 + k, 96, n) for k in range(N)]
+        dpeers = [to_dev(np.concatenate([np.zeros(offset, np.uint16), p]), sdt)[offset:] for p in peers]
+        for acc in (False, True):
+            if ddt == "fp32":
+                base = draw_master(n, 0.5, 9, 97)
+                dst = to_dev(np.concatenate([np.zeros(offset, np.float32), base]), "fp32")[offset:]
+            else:
+                base = draw_grads(n, ddt, 0.5, 1.0, 10, 97, 0)
+                dst = to_dev(np.concatenate([np.zeros(offset, np.uint16), base]), ddt)[offset:]
+            st = ShardStep(max(n, 1), zds.hparams(), zds.scaler_config(initial_scale_power=3), max_norm=1.0,
+                           accum_steps=N)
+            ws = zds.new_reduce_workspace(n)
+            zds.zds_reduce_peer_slices_norm(dpeers, dst, zds.ZDS_ACCUMULATE if acc else zds.ZDS_OVERWRITE, N, 1.0,
+                                            st.state, st.scalars, ws)
+            torch.cuda.synchronize()
+            want = O.reduce_peer_slices(peers, sdt, base.copy(), ddt, accumulate=acc)
+            got = to_host(dst)
+            if ddt == "fp32":
+                assert (got.view(np.uint32) == want.view(np.uint32)).all(), (n, acc)
+            else:
+                assert (got == want).all(), (n, acc)
+            sc = st.read_scalars()
+            r = O.overflow_and_norm(want, ddt, 2.0 ** 3, N, 1.0)
+            assert sc.overflow == r["overflow"] == 0, (n, acc)
+            assert abs(sc.sumsq - r["sumsq"]) <= 1e-12 * max(r["sumsq"], 1e-300), (n, acc)
+            assert sc.grad_scale == r["grad_scale"], (n, acc)
+            if n == 0:
+                assert sc.sumsq == 0.0 and sc.grad_scale == np.float32(1.0 / (8.0 * N))
+
+
+@pytest.mark.parametrize("ddt", ["fp32", "bf16"])
+@pytest.mark.parametrize("bad", [np.inf, -np.inf, np.nan])
+def test_reduce_peer_slices_norm_overflow(ddt, bad):
+    """A non-finite element in one peer's slice sets the overflow flag."""
+    say("reduce peers + norm overflow %s %r" % (ddt, bad))
+    n, N = 512 * 300 + 3, 4
+    peers = [draw_grads(n, "bf16", 1e-2, 1.0, 70 + k, 98, 0) for k in range(N)]
+    for where in (0, n // 2, n - 1):
+        ps = [p.copy() for p in peers]
+        ps[2][where] = (np.array([bad], np.float32).view(np.uint32) >> 16).astype(np.uint16)[0]
+        dst = torch.zeros(n, dtype=torch.float32 if ddt == "fp32" else torch.bfloat16, device="cuda")
+        st = ShardStep(n, zds.hparams(), zds.scaler_config(initial_scale_power=3), max_norm=1.0, accum_steps=N)
+        zds.zds_reduce_peer_slices_norm([to_dev(p, "bf16") for p in ps], dst, zds.ZDS_OVERWRITE, N, 1.0, st.state,
+                                        st.scalars, zds.new_reduce_workspace(n))
+        torch.cuda.synchronize()
+        want = O.reduce_peer_slices(ps, "bf16", np.zeros(n, np.float32 if ddt == "fp32" else np.uint16), ddt,
+                                    accumulate=False)
+        assert O.overflow_and_norm(want, ddt, 8.0, N, 1.0)["overflow"] == 1
+        assert st.read_scalars().overflow == 1, where
+
+
 def test_accumulate_with_bound_source_set():
     """A SourceSet (pointers marshalled once) gives the same result as the
     list, call after call, and is refused for a plan of another size."""

@@ -102,3 +102,4 @@ def test_bench_byte_model():
     assert bench._bytes_per_param(w, True) == dict(accum_total=6 + 10 * 15, norm=0, adam=30)
     w = bench._workload("llama7b_s2_intake8")
     assert bench._bytes_per_param(w, False) == dict(accum_total=20, norm=4, adam=30)
+    assert bench._bytes_per_param(w, True) == dict(accum_total=20, norm=0, adam=30)

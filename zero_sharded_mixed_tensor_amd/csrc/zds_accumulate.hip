@@ -44,11 +44,6 @@ struct AccArgs {
   double *partials;  // NORM: one sum of squares per block
 };
 
-__device__ __forceinline__ double sq_add(float x, double acc) {
-  const double d = static_cast<double>(x);
-  return fma(d, d, acc);  // x^2 is exact in float64
-}
-
 // Chunks a block takes per iteration: copy mode moves little per chunk, so a
 // block takes two and overlaps their table lookups and loads.
 // Work units per chunk: the fp32 modes move more bytes per element, so a

@@ -375,11 +375,8 @@ extern "C" zds_status zds_grad_accumulate_norm(zds_plan *plan, const void *const
                             out_dev, static_cast<hipStream_t>(stream));
 }
 
-extern "C" zds_status zds_reduce_peer_slices(const void *const *peer_ptrs, int32_t num_peers, zds_dtype src_dtype,
-                                             int64_t n, void *dst, zds_dtype dst_dtype, zds_accum_mode mode,
-                                             void *stream) {
-  clear_error();
-  const char *fn = "zds_reduce_peer_slices";
+static zds_status reduce_checks(const char *fn, const void *const *peer_ptrs, int32_t num_peers,
+                                zds_dtype src_dtype, int64_t n, void *dst, zds_dtype dst_dtype, zds_accum_mode mode) {
   if (num_peers < 1 || num_peers > kMaxPeers) return fail(ZDS_EINVAL, "%s: num_peers must be in [1, %d]", fn, kMaxPeers);
   if (src_dtype != ZDS_FP16 && src_dtype != ZDS_BF16) return fail(ZDS_EINVAL, "%s: peers must be fp16 or bf16", fn);
   if (dst_dtype != ZDS_FP32 && dst_dtype != src_dtype)
@@ -393,8 +390,49 @@ extern "C" zds_status zds_reduce_peer_slices(const void *const *peer_ptrs, int32
     if (!aligned(peer_ptrs[k], 2)) return fail(ZDS_EALIGN, "%s: peer %d misaligned", fn, k);
   }
   if (!aligned(dst, static_cast<uintptr_t>(dtype_size(dst_dtype)))) return fail(ZDS_EALIGN, "%s: dst misaligned", fn);
-  return launch_reduce_peers(peer_ptrs, num_peers, src_dtype, n, dst, dst_dtype, mode == ZDS_ACCUMULATE,
-                             static_cast<hipStream_t>(stream));
+  return ZDS_OK;
+}
+
+extern "C" zds_status zds_reduce_peer_slices(const void *const *peer_ptrs, int32_t num_peers, zds_dtype src_dtype,
+                                             int64_t n, void *dst, zds_dtype dst_dtype, zds_accum_mode mode,
+                                             void *stream) {
+  clear_error();
+  zds_status st = reduce_checks("zds_reduce_peer_slices", peer_ptrs, num_peers, src_dtype, n, dst, dst_dtype, mode);
+  if (st != ZDS_OK || n == 0) return st;
+  return launch_reduce_peers(peer_ptrs, num_peers, src_dtype, n, dst, dst_dtype, mode == ZDS_ACCUMULATE, nullptr,
+                             nullptr, static_cast<hipStream_t>(stream));
+}
+
+extern "C" size_t zds_reduce_norm_workspace_bytes(int64_t n) {
+  const int64_t a = partials_workspace_doubles(reduce_grid_max(n < 0 ? 0 : n));
+  const int64_t b = partials_workspace_doubles(norm_grid(0));  // n == 0 runs the plain norm pass
+  return static_cast<size_t>(a > b ? a : b) * sizeof(double);
+}
+
+extern "C" zds_status zds_reduce_peer_slices_norm(const void *const *peer_ptrs, int32_t num_peers,
+                                                  zds_dtype src_dtype, int64_t n, void *dst, zds_dtype dst_dtype,
+                                                  zds_accum_mode mode, int32_t accum_steps, float max_norm,
+                                                  const zds_step_state *state_dev, zds_step_scalars *out_dev,
+                                                  void *ws, size_t ws_bytes, void *stream) {
+  clear_error();
+  const char *fn = "zds_reduce_peer_slices_norm";
+  zds_status st = reduce_checks(fn, peer_ptrs, num_peers, src_dtype, n, dst, dst_dtype, mode);
+  if (st != ZDS_OK) return st;
+  if (accum_steps < 1) return fail(ZDS_EINVAL, "%s: accum_steps must be >= 1", fn);
+  if (!state_dev || !out_dev) return fail(ZDS_EINVAL, "%s: null state or output", fn);
+  if (!aligned(state_dev, 8) || !aligned(out_dev, 8)) return fail(ZDS_EALIGN, "%s: state/output not 8-byte aligned", fn);
+  const size_t need = zds_reduce_norm_workspace_bytes(n);
+  if (!ws || ws_bytes < need || !aligned(ws, 8))
+    return fail(ZDS_EINVAL, "%s: workspace of %zu bytes needed (8-byte aligned)", fn, need);
+  double *partials = static_cast<double *>(ws);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  // nothing to sum: the scalars of an empty shard (norm 0), as zds_overflow_and_norm writes them
+  if (n == 0) return launch_norm(nullptr, ZDS_FP32, 0, accum_steps, max_norm, state_dev, out_dev, partials, s);
+  int64_t nparts = 0;
+  st = launch_reduce_peers(peer_ptrs, num_peers, src_dtype, n, dst, dst_dtype, mode == ZDS_ACCUMULATE, partials,
+                           &nparts, s);
+  if (st != ZDS_OK) return st;
+  return launch_norm_stage2(partials, nparts, state_dev, accum_steps, max_norm, out_dev, s);
 }
 
 static bool onebit_chunk_ok(int32_t c) {

@@ -181,6 +181,12 @@ __device__ __forceinline__ double wave_sum(double x) {
   return (readlane_f64(x, 0) + readlane_f64(x, 16)) + (readlane_f64(x, 32) + readlane_f64(x, 48));
 }
 
+// acc + x^2 in float64; the square of a 16-bit or fp32 value is exact there.
+__device__ __forceinline__ double sq_add(float x, double acc) {
+  const double d = static_cast<double>(x);
+  return fma(d, d, acc);
+}
+
 // Sum over a block of BLOCK threads (all of them must call it); the result is
 // valid in thread 0. Waves add in lane order, the wave totals in wave order.
 template <int BLOCK>

@@ -63,8 +63,13 @@ zds_status launch_accumulate_norm(const PlanDev &p, const void *const *dev_ptrs,
 
 // Most peers zds_reduce_peer_slices sums in one call.
 constexpr int kMaxPeers = 16;
+// With partials != null each block also writes the float64 sum of squares of
+// the values it stored; *nparts (if given) receives the number of blocks.
 zds_status launch_reduce_peers(const void *const *peers, int32_t npeers, zds_dtype src, int64_t n, void *dst,
-                               zds_dtype dst_dtype, bool accumulate, hipStream_t stream);
+                               zds_dtype dst_dtype, bool accumulate, double *partials, int64_t *nparts,
+                               hipStream_t stream);
+// Most partial sums the fused intake norm writes for n elements.
+int64_t reduce_grid_max(int64_t n);
 
 zds_status launch_adam(const zds_adamw_hparams &hp, const void *grads, zds_dtype gdt, float *master,
                        float *m, float *v, void *out, zds_dtype pdt, int64_t n, zds_step_scalars *scalars,

@@ -16,6 +16,11 @@
 // tile, the tiles meet in LDS where each thread sums 2 elements over the
 // peers in order, and waves 0 and 1 store the result. A block takes two
 // consecutive tiles per grid step.
+//
+// NORM (the step's overflow / norm pass fused in): each thread adds the
+// float64 square of every value it stores (the rounded value for a 16-bit
+// destination) and each block writes one partial sum, so the shard gradient
+// is not read a second time.
 #include "zds_device.h"
 #include "zds_internal.h"
 
@@ -23,6 +28,13 @@
 // 5,772 GB/s, 2 tiles 6,066, 4 tiles 6,039).
 #ifndef ZDS_REDUCE_TPB
 #define ZDS_REDUCE_TPB 2
+#endif
+// The same with the norm fused in: each block ends with a float64 block
+// reduction, so a block takes more tiles (8 peers into fp32 with the norm,
+// interleaved on one box: 2 tiles 2.945 ms, 4 tiles 2.856, 8 tiles 3.017;
+// the intake then a separate norm pass 3.255).
+#ifndef ZDS_REDUCE_NORM_TPB
+#define ZDS_REDUCE_NORM_TPB 4
 #endif
 
 namespace zds {
@@ -32,6 +44,7 @@ struct ReduceArgs {
   int32_t npeers;
   int64_t n;
   void *dst;
+  double *partials;  // NORM: one sum of squares per block
 };
 
 template <int SD>
@@ -42,7 +55,7 @@ __device__ __forceinline__ float widen16(uint16_t h) {
 
 // SD: peer dtype (16-bit). DD: destination dtype (fp32 or SD). ACC: add the
 // destination's previous value.
-template <int SD, int DD, bool ACC>
+template <int SD, int DD, bool ACC, bool NORM>
 __global__ void __launch_bounds__(256) reduce_peers_kernel(ReduceArgs a) {
   __shared__ u32x4 sx[kMaxPeers][64];     // peer tiles, 512 x 16-bit each
   __shared__ f32x4 sd[DD == ZDS_FP32 ? 128 : 1];  // fp32 destination tile
@@ -52,9 +65,10 @@ __global__ void __launch_bounds__(256) reduce_peers_kernel(ReduceArgs a) {
   const int N = a.npeers;
   const int64_t g8 = a.n >> 3;  // whole groups of 8 elements
   const int64_t ntiles = (g8 + 63) >> 6;
-  for (int64_t it = static_cast<int64_t>(blockIdx.x) * ZDS_REDUCE_TPB; it < ntiles;
-       it += static_cast<int64_t>(gridDim.x) * ZDS_REDUCE_TPB)
-  for (int64_t tile = it; tile < it + ZDS_REDUCE_TPB && tile < ntiles; ++tile) {  // uniform per block
+  constexpr int TPB = NORM ? ZDS_REDUCE_NORM_TPB : ZDS_REDUCE_TPB;
+  double ss = 0.0;
+  for (int64_t it = static_cast<int64_t>(blockIdx.x) * TPB; it < ntiles; it += static_cast<int64_t>(gridDim.x) * TPB)
+  for (int64_t tile = it; tile < it + TPB && tile < ntiles; ++tile) {  // uniform per block
     const int64_t grp = tile * 64 + lane;  // this lane's 8-element group
     const bool gok = grp < g8;
     u32x4 r[4];
@@ -97,11 +111,15 @@ __global__ void __launch_bounds__(256) reduce_peers_kernel(ReduceArgs a) {
         for (int k = 1; k < N; ++k) acc = acc + widen16<SD>(reinterpret_cast<const uint16_t *>(sx[k])[e]);
         if constexpr (DD == ZDS_FP32) {
           float *o = reinterpret_cast<float *>(sd);
-          o[e] = ACC ? o[e] + acc : acc;
+          const float r = ACC ? o[e] + acc : acc;
+          o[e] = r;
+          if (NORM) ss = sq_add(r, ss);
         } else {
           uint16_t *o = reinterpret_cast<uint16_t *>(sh);
           const float r2 = ACC ? widen16<DD>(o[e]) + acc : acc;
-          o[e] = narrow1<DD>(r2);
+          const uint16_t h = narrow1<DD>(r2);
+          o[e] = h;
+          if (NORM) ss = sq_add(widen16<DD>(h), ss);
         }
       }
     }
@@ -123,60 +141,92 @@ __global__ void __launch_bounds__(256) reduce_peers_kernel(ReduceArgs a) {
     for (int k = 1; k < N; ++k) acc = acc + widen1<SD>(a.peers[k], e);
     if constexpr (DD == ZDS_FP32) {
       float *o = static_cast<float *>(a.dst);
-      o[e] = ACC ? o[e] + acc : acc;
+      const float r = ACC ? o[e] + acc : acc;
+      o[e] = r;
+      if (NORM) ss = sq_add(r, ss);
     } else {
       uint16_t *o = static_cast<uint16_t *>(a.dst);
       const float r2 = ACC ? widen1<DD>(a.dst, e) + acc : acc;
-      o[e] = narrow1<DD>(r2);
+      const uint16_t h = narrow1<DD>(r2);
+      o[e] = h;
+      if (NORM) ss = sq_add(widen16<DD>(h), ss);
     }
+  }
+  if (NORM) {
+    const double b = block_sum<256>(ss);
+    if (threadIdx.x == 0) a.partials[blockIdx.x] = b;
   }
 }
 
 // Element-wise path for peers or destinations without 16-byte alignment.
-template <int SD, int DD, bool ACC>
+template <int SD, int DD, bool ACC, bool NORM>
 __global__ void __launch_bounds__(256) reduce_peers_scalar(ReduceArgs a) {
   const int64_t stride = static_cast<int64_t>(gridDim.x) * 256;
+  double ss = 0.0;
   for (int64_t e = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; e < a.n; e += stride) {
     float acc = widen1<SD>(a.peers[0], e);
     for (int k = 1; k < a.npeers; ++k) acc = acc + widen1<SD>(a.peers[k], e);
     if constexpr (DD == ZDS_FP32) {
       float *o = static_cast<float *>(a.dst);
-      o[e] = ACC ? o[e] + acc : acc;
+      const float r = ACC ? o[e] + acc : acc;
+      o[e] = r;
+      if (NORM) ss = sq_add(r, ss);
     } else {
       uint16_t *o = static_cast<uint16_t *>(a.dst);
       const float r2 = ACC ? widen1<DD>(a.dst, e) + acc : acc;
-      o[e] = narrow1<DD>(r2);
+      const uint16_t h = narrow1<DD>(r2);
+      o[e] = h;
+      if (NORM) ss = sq_add(widen16<DD>(h), ss);
     }
   }
-}
-
-template <int SD, int DD, bool ACC>
-static void go(bool vec, int64_t n, hipStream_t s, const ReduceArgs &a) {
-  if (vec) {
-    int64_t g = (((n >> 3) + 63) / 64 + ZDS_REDUCE_TPB - 1) / ZDS_REDUCE_TPB;
-    if (g < 1) g = 1;
-    if (g > max_blocks(256)) g = max_blocks(256);
-    hipLaunchKernelGGL((reduce_peers_kernel<SD, DD, ACC>), dim3(static_cast<uint32_t>(g)), dim3(256), 0, s, a);
-  } else {
-    int64_t g = (n + 255) / 256;
-    const int64_t cap = static_cast<int64_t>(device_cu_count()) * 8;
-    if (g > cap) g = cap;
-    if (g < 1) g = 1;
-    hipLaunchKernelGGL((reduce_peers_scalar<SD, DD, ACC>), dim3(static_cast<uint32_t>(g)), dim3(256), 0, s, a);
+  if (NORM) {
+    const double b = block_sum<256>(ss);
+    if (threadIdx.x == 0) a.partials[blockIdx.x] = b;
   }
 }
 
-template <int SD>
-static void go_sd(zds_dtype dd, bool acc, bool vec, int64_t n, hipStream_t s, const ReduceArgs &a) {
+// Grid of the intake kernels (also the number of partials the fused norm
+// writes).
+static int64_t reduce_grid(int64_t n, bool vec, bool norm) {
+  if (vec) {
+    const int tpb = norm ? ZDS_REDUCE_NORM_TPB : ZDS_REDUCE_TPB;
+    int64_t g = (((n >> 3) + 63) / 64 + tpb - 1) / tpb;
+    if (g < 1) g = 1;
+    if (g > max_blocks(256)) g = max_blocks(256);
+    return g;
+  }
+  int64_t g = (n + 255) / 256;
+  const int64_t cap = static_cast<int64_t>(device_cu_count()) * 8;
+  if (g > cap) g = cap;
+  if (g < 1) g = 1;
+  return g;
+}
+
+int64_t reduce_grid_max(int64_t n) {
+  const int64_t a = reduce_grid(n, true, true), b = reduce_grid(n, false, true);
+  return a > b ? a : b;
+}
+
+template <int SD, int DD, bool ACC, bool NORM>
+static void go(bool vec, int64_t g, hipStream_t s, const ReduceArgs &a) {
+  if (vec)
+    hipLaunchKernelGGL((reduce_peers_kernel<SD, DD, ACC, NORM>), dim3(static_cast<uint32_t>(g)), dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL((reduce_peers_scalar<SD, DD, ACC, NORM>), dim3(static_cast<uint32_t>(g)), dim3(256), 0, s, a);
+}
+
+template <int SD, bool NORM>
+static void go_sd(zds_dtype dd, bool acc, bool vec, int64_t g, hipStream_t s, const ReduceArgs &a) {
   if (dd == ZDS_FP32) {
-    if (acc) go<SD, ZDS_FP32, true>(vec, n, s, a); else go<SD, ZDS_FP32, false>(vec, n, s, a);
+    if (acc) go<SD, ZDS_FP32, true, NORM>(vec, g, s, a); else go<SD, ZDS_FP32, false, NORM>(vec, g, s, a);
   } else {
-    if (acc) go<SD, SD, true>(vec, n, s, a); else go<SD, SD, false>(vec, n, s, a);
+    if (acc) go<SD, SD, true, NORM>(vec, g, s, a); else go<SD, SD, false, NORM>(vec, g, s, a);
   }
 }
 
 zds_status launch_reduce_peers(const void *const *peers, int32_t npeers, zds_dtype src, int64_t n, void *dst,
-                               zds_dtype dst_dtype, bool accumulate, hipStream_t stream) {
+                               zds_dtype dst_dtype, bool accumulate, double *partials, int64_t *nparts,
+                               hipStream_t stream) {
   ReduceArgs a{};
   bool vec = aligned(dst, 16);
   for (int k = 0; k < npeers; ++k) {
@@ -186,9 +236,17 @@ zds_status launch_reduce_peers(const void *const *peers, int32_t npeers, zds_dty
   a.npeers = npeers;
   a.n = n;
   a.dst = dst;
-  if (src == ZDS_BF16) go_sd<ZDS_BF16>(dst_dtype, accumulate, vec, n, stream, a);
-  else go_sd<ZDS_FP16>(dst_dtype, accumulate, vec, n, stream, a);
-  return check_launch("reduce_peer_slices kernel");
+  a.partials = partials;
+  const int64_t g = reduce_grid(n, vec, partials != nullptr);
+  if (nparts) *nparts = g;
+  if (partials) {
+    if (src == ZDS_BF16) go_sd<ZDS_BF16, true>(dst_dtype, accumulate, vec, g, stream, a);
+    else go_sd<ZDS_FP16, true>(dst_dtype, accumulate, vec, g, stream, a);
+  } else {
+    if (src == ZDS_BF16) go_sd<ZDS_BF16, false>(dst_dtype, accumulate, vec, g, stream, a);
+    else go_sd<ZDS_FP16, false>(dst_dtype, accumulate, vec, g, stream, a);
+  }
+  return check_launch(partials ? "reduce_peer_slices_norm kernel" : "reduce_peer_slices kernel");
 }
 
 }  // namespace zds

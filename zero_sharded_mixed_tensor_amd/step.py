@@ -31,6 +31,12 @@ class ShardStep:
         zds.zds_grad_accumulate_norm(plan, srcs, dst, mode, self.accum_steps, self.max_norm, self.state,
                                      self.scalars, ws, stream)
 
+    def intake_norm(self, peers, dst, mode, ws, stream=None):
+        """The Stage-2 intake of the peers' slices with the overflow/norm
+        pass fused in."""
+        zds.zds_reduce_peer_slices_norm(peers, dst, mode, self.accum_steps, self.max_norm, self.state,
+                                        self.scalars, ws, stream, n=self.n)
+
     def norm(self, grads, stream=None):
         zds.zds_overflow_and_norm(grads, self.accum_steps, self.max_norm, self.state, self.scalars,
                                   self.ws, stream, n=self.n)

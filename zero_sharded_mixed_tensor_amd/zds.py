@@ -90,6 +90,9 @@ _SIGS = {
     "zds_workspace_bytes": (ctypes.c_size_t, [_I64]),
     "zds_reduce_peer_slices": (_I32, [ctypes.POINTER(_P), _I32, _I32, _I64, _P, _I32, _I32, _P]),
     "zds_plan_norm_workspace_bytes": (ctypes.c_size_t, [_P]),
+    "zds_reduce_norm_workspace_bytes": (ctypes.c_size_t, [_I64]),
+    "zds_reduce_peer_slices_norm": (_I32, [ctypes.POINTER(_P), _I32, _I32, _I64, _P, _I32, _I32, _I32,
+                                           ctypes.c_float, _P, _P, _P, ctypes.c_size_t, _P]),
     "zds_grad_accumulate_norm": (_I32, [_P, ctypes.POINTER(_P), _I32, _P, _I32, _I32, _I32, ctypes.c_float,
                                         _P, _P, _P, ctypes.c_size_t, _P]),
     "zds_overflow_and_norm": (_I32, [_P, _I32, _I64, _I32, ctypes.c_float, _P, _P, _P,
@@ -351,17 +354,43 @@ def zds_grad_accumulate_norm(plan, srcs, dst, mode, accum_steps, max_norm, state
 def zds_reduce_peer_slices(peers, dst, mode, stream=None, n=None):
     """dst (+)= sum over the peer slices (device tensors of one 16-bit dtype),
     in peer order, in fp32 (see include/zds.h)."""
-    if not peers:
-        raise ZdsError(ZDS_EINVAL, "need at least one peer slice")
     n = dst.numel() if n is None else n
     _need(dst, n, "dst")
+    arr, sdt = _peer_array(peers, n)
+    _check(lib.zds_reduce_peer_slices(arr, len(peers), sdt, n, _dev_ptr(dst, "dst"), dtype_code(dst), mode,
+                                      _stream(stream)))
+
+
+def _peer_array(peers, n):
+    if not peers:
+        raise ZdsError(ZDS_EINVAL, "need at least one peer slice")
     sdt = dtype_code(peers[0])
     for k, t in enumerate(peers):
         if dtype_code(t) != sdt or t.numel() < n:
             raise ZdsError(ZDS_EINVAL, "peer %d: wrong dtype or too short" % k)
-    arr = (ctypes.c_void_p * len(peers))(*[_dev_ptr(t, "peer %d" % k) for k, t in enumerate(peers)])
-    _check(lib.zds_reduce_peer_slices(arr, len(peers), sdt, n, _dev_ptr(dst, "dst"), dtype_code(dst), mode,
-                                      _stream(stream)))
+    return (ctypes.c_void_p * len(peers))(*[_dev_ptr(t, "peer %d" % k) for k, t in enumerate(peers)]), sdt
+
+
+def zds_reduce_norm_workspace_bytes(n):
+    return lib.zds_reduce_norm_workspace_bytes(n)
+
+
+def new_reduce_workspace(n, device="cuda"):
+    return torch.empty((zds_reduce_norm_workspace_bytes(n) + 7) // 8, dtype=torch.float64, device=device)
+
+
+def zds_reduce_peer_slices_norm(peers, dst, mode, accum_steps, max_norm, state, scalars, ws, stream=None, n=None):
+    """zds_reduce_peer_slices plus the step's overflow flag, norm and clip
+    scalars formed from the stored values (see include/zds.h)."""
+    n = dst.numel() if n is None else n
+    _need(dst, n, "dst")
+    _need_bytes(state, STATE_BYTES, "state")
+    _need_bytes(scalars, SCALARS_BYTES, "scalars")
+    arr, sdt = _peer_array(peers, n)
+    _check(lib.zds_reduce_peer_slices_norm(arr, len(peers), sdt, n, _dev_ptr(dst, "dst"), dtype_code(dst), mode,
+                                           accum_steps, max_norm, _dev_ptr(state, "state"),
+                                           _dev_ptr(scalars, "scalars"), _dev_ptr(ws, "workspace"),
+                                           ws.numel() * ws.element_size(), _stream(stream)))
 
 
 def zds_workspace_bytes(n):
