@@ -371,7 +371,7 @@ def run_onebit(args, w):
         enc_ms.append(ev[0].elapsed_time(ev[1]))
         dec_ms.append(ev[1].elapsed_time(ev[2]))
     el = time.perf_counter() - t0
-    payload_b = (n + 255) // 256 * 32 + (n + chunk - 1) // chunk * 4  # sign words + scales
+    payload_b = (n + 2047) // 2048 * 256 + (n + chunk - 1) // chunk * 4  # sign words + scales
     enc_b = 12 * n + payload_b
     dec_b = N * payload_b + 4 * n
     e_ms, d_ms = sum(enc_ms) / len(enc_ms), sum(dec_ms) / len(dec_ms)

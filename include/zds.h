@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define ZDS_ABI_VERSION 1
+#define ZDS_ABI_VERSION 2
 
 typedef enum zds_status {
   ZDS_OK = 0,
@@ -312,24 +312,27 @@ zds_status zds_reduce_peer_slices_norm(const void *const *peer_ptrs, int32_t num
  *            s = fp32(sqrt(sum over the chunk of c^2 / its length)), squares
  *            summed in float64; the new error is c - s (bit 1) or c + s.
  *   chunk    1024, 2048, 4096, 8192 or 16384
- *   words    4 * ceil(n / 256) uint64, 16-byte aligned: bit l of word
- *            4g + i is element 256g + 4l + i (the lane mask of a wave whose
- *            lane l holds quad l of group g); bits past n are 0
+ *   words    64 * ceil(n / 2048) uint32, 4-byte aligned: bit 4r + i of
+ *            word 64u + l is element 2048u + 256r + 4l + i (r < 8, l < 64,
+ *            i < 4): word l of a 2048-element unit holds the signs of the
+ *            l-th quad of each of its eight 256-element groups; bits past n
+ *            are 0
  *   scales   ceil(n / chunk) fp32
  * Non-finite inputs give non-finite scales (check for overflow first).
  * HBM-bound: 12 B/element + the payload (1/8 B + 4/chunk B). */
-zds_status zds_onebit_compress(const float *x, float *error, int64_t n, int32_t chunk, uint64_t *words,
+zds_status zds_onebit_compress(const float *x, float *error, int64_t n, int32_t chunk, uint32_t *words,
                                float *scales, void *stream);
 
 /* Decode of num_peers (1..16) payloads of n elements each, all made with the
  * same chunk: dst[i] (+)= sum over peers k = 0.. in that order of
  * +-scales_k[i / chunk] (fp32, one rounding per add; with ZDS_ACCUMULATE the
  * previous dst is added last). The mean over peers is left to the caller
- * (pass K * N as accum_steps to the step). Words 8-byte aligned; dst: n
+ * (pass K * N as accum_steps to the step). Words 4-byte aligned; dst: n
  * fp32, 16-byte aligned, not overlapping any payload.
- * Moves N/8 + 4N/chunk B of payload + 4 B (8 B accumulating) per element;
- * with many peers the per-element select-and-add work, not HBM, bounds it. */
-zds_status zds_onebit_decompress(const uint64_t *const *peer_words, const float *const *peer_scales,
+ * Moves N/8 + 4N/chunk B of payload + 4 B (8 B accumulating) per element.
+ * The first 8 peers cost a table lookup per element whatever their number;
+ * each peer past 8 adds a select and an add per element. */
+zds_status zds_onebit_decompress(const uint32_t *const *peer_words, const float *const *peer_scales,
                                  int32_t num_peers, int64_t n, int32_t chunk, float *dst, zds_accum_mode mode,
                                  void *stream);
 

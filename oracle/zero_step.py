@@ -439,17 +439,19 @@ def consolidate(shards, numels, align):
 #    encoded. Every end that encodes (the sender, and the receiver when it
 #    sends the combined result on) keeps its own buffer;
 #  - a sign bit is 1 for c >= 0 (so -0 encodes as +) and 0 otherwise (NaN
-#    included). The signs travel in 64-bit words, four per group of 256
-#    elements: bit l of word 4g + i is element 256g + 4l + i, so that word i
-#    of a group holds the i-th element of each of 64 consecutive quads; bits
-#    past the end are 0;
+#    included). The signs travel in 32-bit words, 64 per unit of 2048
+#    elements: bit 4r + i of word 64u + l is element 2048u + 256r + 4l + i
+#    (r < 8, l < 64, i < 4), so that word l of a unit holds the signs of the
+#    l-th quad of each of the unit's eight groups of 256 elements; bits past
+#    the end are 0. (The pages fix one sign bit per element; this order is
+#    the library's wire format.);
 #  - the receiver's decode of N peers' payloads is their sum, formed in fp32
 #    in peer order; the mean over peers is left to the caller (as for the
 #    Stage-2 intake above).
 # ---------------------------------------------------------------------------
 
 def onebit_compress(x, err, chunk):
-    """Encode c = x + err (fp32). Returns (words uint64[4 * ceil(n/256)],
+    """Encode c = x + err (fp32). Returns (words uint32[64 * ceil(n/2048)],
     scales float32[ceil(n/chunk)], new_err float32[n]) with, per chunk j,
     s_j = fp32(sqrt(sum(c_i^2) / len_j)) (exact squares, correctly rounded sum,
     float64 divide and sqrt) and new_err_i = c_i - s_j * sign_i (one fp32
@@ -466,20 +468,21 @@ def onebit_compress(x, err, chunk):
         s = np.float32(math.sqrt(sumsq / (b - a)))
         scales[j] = s
         new_err[a:b] = np.where(pos[a:b], c[a:b] - s, c[a:b] + s)
-    words = np.zeros(4 * -(-n // 256), np.uint64)
+    words = np.zeros(64 * -(-n // 2048), np.uint32)
     for i in np.nonzero(pos)[0]:
-        g, r = divmod(int(i), 256)
-        lane, k = divmod(r, 4)
-        words[4 * g + k] |= np.uint64(1) << np.uint64(lane)
+        u, rem = divmod(int(i), 2048)
+        r, q = divmod(rem, 256)
+        lane, k = divmod(q, 4)
+        words[64 * u + lane] |= np.uint32(1) << np.uint32(4 * r + k)
     return words, scales, new_err
 
 
 def onebit_signs(words, n):
     """+1 / -1 (fp32) of elements 0 .. n-1 of a packed sign stream."""
     i = np.arange(n)
-    word = 4 * (i // 256) + i % 4
-    lane = (i % 256) // 4
-    bit = (words[word] >> lane.astype(np.uint64)) & np.uint64(1)
+    word = 64 * (i // 2048) + (i % 256) // 4
+    pos = 4 * ((i % 2048) // 256) + i % 4
+    bit = (np.asarray(words, np.uint32)[word] >> pos.astype(np.uint32)) & np.uint32(1)
     return np.where(bit == 1, np.float32(1.0), np.float32(-1.0))
 
 

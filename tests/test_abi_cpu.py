@@ -30,7 +30,7 @@ def test_exports_every_declared_function():
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(zds._SIGS), set(names) ^ set(zds._SIGS)
-    assert zds.zds_abi_version() == 1
+    assert zds.zds_abi_version() == 2
 
 
 def test_struct_layouts():

@@ -60,7 +60,7 @@ def test_norm_and_reduce_lengths():
 @pytest.mark.parametrize("n,chunk", [(1, 1024), (256, 2048), (257, 1024), (5000, 4096)])
 def test_onebit_payload_lengths(n, chunk):
     words, scales = zds.onebit_payload(n, chunk, device="cpu")
-    assert words.numel() * 8 == 32 * ((n + 255) // 256) and scales.numel() == (n + chunk - 1) // chunk
+    assert words.numel() * 4 == 256 * ((n + 2047) // 2048) and scales.numel() == (n + chunk - 1) // chunk
     x, err = _f32(n), _f32(n)
     _raises(lambda: zds.zds_onebit_compress(x, err, chunk, words[:-1], scales), "words holds")
     _raises(lambda: zds.zds_onebit_compress(x, err, chunk, words, scales[:-1]), "scales holds")

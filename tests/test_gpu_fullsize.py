@@ -366,7 +366,7 @@ def test_llama7b_onebit_codec_shard():
     differ = 0
     for (a, b), j, (xs, es) in zip(spans, pick, before):
         ow, osc, oe = O.onebit_compress(xs, es, chunk)
-        assert (words[a // 64:4 * ((b + 255) // 256)].cpu().numpy().view(np.uint64) == ow).all(), j
+        assert (words[a // 32:64 * ((b + 2047) // 2048)].cpu().numpy().view(np.uint32) == ow).all(), j
         s = scales[int(j):int(j) + 1].cpu().numpy()
         ge = e[a:b].cpu().numpy()
         if s[0] == osc[0]:
@@ -382,7 +382,7 @@ def test_llama7b_onebit_codec_shard():
     zds.zds_onebit_decompress(peers, chunk, out)
     torch.cuda.synchronize()
     for (a, b), j in zip(spans, pick):
-        pay = [(pw[a // 64:4 * ((b + 255) // 256)].cpu().numpy().view(np.uint64), ps[int(j):int(j) + 1].cpu().numpy())
+        pay = [(pw[a // 32:64 * ((b + 2047) // 2048)].cpu().numpy().view(np.uint32), ps[int(j):int(j) + 1].cpu().numpy())
                for pw, ps in peers]
         want = O.onebit_decompress(pay, b - a, chunk, None, False)
         assert (out[a:b].cpu().numpy().view(np.uint32) == want.view(np.uint32)).all(), j
@@ -464,10 +464,12 @@ def test_beyond_the_grid_cap_intake_and_codec():
     n = (1 << 33) + 1003
     chunk = 1024
     say("beyond the grid cap: n =", n)
-    nch = -(-n // chunk)
+    # sampled 2048-element units (two 1024-element chunks each; the last unit
+    # is ragged): a unit's sign words are its own 64 words of the payload
+    nun = -(-n // 2048)
     rng = np.random.default_rng(101)
-    pick = np.unique(np.concatenate([rng.integers(0, nch, 48), [0, nch // 2, nch - 2, nch - 1]]))
-    spans = [(int(j) * chunk, min(n, (int(j) + 1) * chunk)) for j in pick]
+    pick = np.unique(np.concatenate([rng.integers(0, nun, 24), [0, nun // 2, nun - 2, nun - 1]]))
+    spans = [(int(u) * 2048, min(n, (int(u) + 1) * 2048)) for u in pick]
 
     # intake: 2 bf16 peers -> fp32
     peers = [fill_normal_(torch.empty(n, dtype=torch.bfloat16, device="cuda"), 1e-3, 110 + k) for k in range(2)]
@@ -487,16 +489,18 @@ def test_beyond_the_grid_cap_intake_and_codec():
     zds.zds_onebit_compress(acc, err, chunk, words, scales)
     torch.cuda.synchronize()
     differ = 0
-    for (a, b), j, (xs, es) in zip(spans, pick, before):
+    for (a, b), u, (xs, es) in zip(spans, pick, before):
         ow, osc, oe = O.onebit_compress(xs, es, chunk)
-        assert (words[a // 64:4 * ((b + 255) // 256)].cpu().numpy().view(np.uint64) == ow).all(), j
-        s = scales[int(j):int(j) + 1].cpu().numpy()
+        assert (words[64 * int(u):64 * int(u) + 64].cpu().numpy().view(np.uint32) == ow).all(), u
+        s = scales[a // chunk:a // chunk + osc.size].cpu().numpy()
         ge = err[a:b].cpu().numpy()
-        if s[0] == osc[0]:
-            assert (ge.view(np.uint32) == oe.view(np.uint32)).all(), j
-        else:
-            differ += 1
-            assert abs(int(s.view(np.int32)[0]) - int(osc.view(np.int32)[0])) == 1, j
+        for c in range(osc.size):
+            ca, cb = c * chunk, min(b - a, (c + 1) * chunk)
+            if s[c] == osc[c]:
+                assert (ge[ca:cb].view(np.uint32) == oe[ca:cb].view(np.uint32)).all(), (u, c)
+            else:
+                differ += 1
+                assert abs(int(s[c:c + 1].view(np.int32)[0]) - int(osc[c:c + 1].view(np.int32)[0])) == 1, (u, c)
     assert differ <= 1
     del err
     torch.cuda.empty_cache()
@@ -504,8 +508,8 @@ def test_beyond_the_grid_cap_intake_and_codec():
     # decode of that one message into the (reused) fp32 buffer
     zds.zds_onebit_decompress([(words, scales)], chunk, acc)
     torch.cuda.synchronize()
-    for (a, b), j in zip(spans, pick):
-        pay = [(words[a // 64:4 * ((b + 255) // 256)].cpu().numpy().view(np.uint64),
-                scales[int(j):int(j) + 1].cpu().numpy())]
+    for (a, b), u in zip(spans, pick):
+        pay = [(words[64 * int(u):64 * int(u) + 64].cpu().numpy().view(np.uint32),
+                scales[a // chunk:(b + chunk - 1) // chunk].cpu().numpy())]
         want = O.onebit_decompress(pay, b - a, chunk, None, False)
-        assert (acc[a:b].cpu().numpy().view(np.uint32) == want.view(np.uint32)).all(), j
+        assert (acc[a:b].cpu().numpy().view(np.uint32) == want.view(np.uint32)).all(), u

@@ -39,7 +39,7 @@ def _dev(a):
 
 
 def _words_host(t):
-    return t.cpu().numpy().view(np.uint64)
+    return t.cpu().numpy().view(np.uint32)
 
 
 def _inputs(n, seed):
@@ -112,7 +112,7 @@ def test_error_feedback_rounds():
         du = ulp_diff32(sc, o_scales)
         keep = ~apart
         el = np.repeat(keep, chunk)[:n]
-        wl = np.repeat(keep, chunk // 64)[:w.size]  # 4 words per 256 elements
+        wl = np.repeat(keep, chunk // 32)[:w.size]  # 64 words per 2048 elements
         assert (w[wl] == o_words[wl]).all(), r
         assert du[keep].max() <= 1 and (du > 0).sum() <= 2, r
         same = el & np.repeat(du == 0, chunk)[:n]
@@ -132,7 +132,7 @@ def test_decode_matches_oracle(peers, mode):
         x, e = _inputs(n, 100 + k)
         w, s, _ = O.onebit_compress(x, e, chunk)
         payloads.append((w, s))
-        dev_payloads.append((torch.from_numpy(w.view(np.int64)).cuda(), _dev(s)))
+        dev_payloads.append((torch.from_numpy(w.view(np.int32)).cuda(), _dev(s)))
     base = np.random.default_rng(7).standard_normal(n).astype(np.float32)
     acc = mode == "accumulate"
     want = O.onebit_decompress(payloads, n, chunk, base.copy(), acc)

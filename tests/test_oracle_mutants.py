@@ -37,8 +37,9 @@ MUTANTS = {
  "consolidate_unsorted": ("    shards = sorted(shards, key=lambda s: s[0])\n    pos = 0", "    pos = shards[0][0] if shards else 0"),
  "consolidate_keep_pad": ("return [flat[o:o + n].copy() for o, n in zip(offsets, numels)]", "return [flat[i * n:(i + 1) * n].copy() for i, n in enumerate(numels)]"),
  "onebit_no_err": ("    c = x + np.asarray(err, np.float32)\n", "    c = x.copy()\n"),
- "onebit_lane_order": ("        lane, k = divmod(r, 4)\n", "        k, lane = divmod(r, 64)\n"),
- "onebit_msb_first": ("words[4 * g + k] |= np.uint64(1) << np.uint64(lane)", "words[4 * g + k] |= np.uint64(1) << np.uint64(63 - lane)"),
+ "onebit_lane_order": ("        lane, k = divmod(q, 4)\n", "        k, lane = divmod(q, 64)\n"),
+ "onebit_msb_first": ("words[64 * u + lane] |= np.uint32(1) << np.uint32(4 * r + k)", "words[64 * u + lane] |= np.uint32(1) << np.uint32(31 - 4 * r - k)"),
+ "onebit_group_major": ("words[64 * u + lane] |= np.uint32(1) << np.uint32(4 * r + k)", "words[64 * u + lane] |= np.uint32(1) << np.uint32(8 * k + r)"),
  "onebit_mean_abs": ("s = np.float32(math.sqrt(sumsq / (b - a)))", "s = np.float32(math.fsum(abs(float(v)) for v in c[a:b]) / (b - a))"),
  "onebit_full_len": ("s = np.float32(math.sqrt(sumsq / (b - a)))", "s = np.float32(math.sqrt(sumsq / chunk))"),
  "onebit_err_sign": ("np.where(pos[a:b], c[a:b] - s, c[a:b] + s)", "np.where(pos[a:b], c[a:b] + s, c[a:b] - s)"),

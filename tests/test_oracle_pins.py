@@ -727,9 +727,10 @@ def _f32_sqrt_of_fraction(q):
 def test_onebit_hand_example():
     x = np.array([1, -2, 3, -4, 0, -0.0], np.float32)
     words, scales, err = O.onebit_compress(x, np.zeros(6, np.float32), 4)
-    # signs + - + - (+0) (-0 counts as +); element e sits in word e % 4 at
-    # bit e // 4 (one group of 256)
-    assert words.tolist() == [0b11, 0b10, 0b1, 0]
+    # signs + - + - (+0) (-0 counts as +); in the first unit and group,
+    # element e sits in word e // 4 at bit e % 4
+    assert words.dtype == np.uint32 and words.size == 64
+    assert words[:2].tolist() == [0b0101, 0b11] and not words[2:].any()
     s = _f32_sqrt_of_fraction(Fraction(1 + 4 + 9 + 16, 4))
     assert scales[0] == s and scales[1] == 0.0
     assert err[:4].tolist() == [np.float32(1) - s, np.float32(-2) + s, np.float32(3) - s, np.float32(-4) + s]
@@ -739,20 +740,25 @@ def test_onebit_hand_example():
 
 
 def test_onebit_bit_layout():
-    n = 700
-    for i in (0, 1, 3, 4, 255, 256, 259, 511, 699):
+    # element 2048u + 256r + 4l + i is bit 4r + i of word 64u + l
+    n = 4700
+    for i, (word, bit) in {0: (0, 0), 1: (0, 1), 3: (0, 3), 4: (1, 0), 255: (63, 3), 256: (0, 4), 259: (0, 7),
+                           511: (63, 7), 1792: (0, 28), 2047: (63, 31), 2048: (64, 0), 2300: (127, 0),
+                           4699: (150, 11)}.items():
         x = -np.ones(n, np.float32)
         x[i] = 1.0
         words, _, _ = O.onebit_compress(x, np.zeros(n, np.float32), 1024)
-        want = np.zeros(12, np.uint64)
-        want[4 * (i // 256) + i % 4] = np.uint64(1) << np.uint64((i % 256) // 4)
+        want = np.zeros(192, np.uint32)
+        want[word] = np.uint32(1) << np.uint32(bit)
         assert (words == want).all(), i
         assert O.onebit_signs(words, n).tolist() == [1.0 if j == i else -1.0 for j in range(n)]
-    # NaN encodes as 0, and bits past the end stay 0: 40 elements fill lanes 0..9
+    # NaN encodes as 0, and bits past the end stay 0: 40 elements fill the
+    # low nibble of words 0..9
     x = np.ones(40, np.float32)
     x[3] = np.nan
     words, scales, err = O.onebit_compress(x, np.zeros(40, np.float32), 1024)
-    assert words.tolist() == [0x3FF, 0x3FF, 0x3FF, 0x3FE] and np.isnan(scales[0]) and np.isnan(err).all()
+    assert words[:10].tolist() == [0x7] + [0xF] * 9 and not words[10:].any()
+    assert np.isnan(scales[0]) and np.isnan(err).all()
 
 
 @pytest.mark.parametrize("k", [-20, -3, 0, 5])

@@ -439,7 +439,7 @@ static bool onebit_chunk_ok(int32_t c) {
   return c == 1024 || c == 2048 || c == 4096 || c == 8192 || c == 16384;
 }
 
-extern "C" zds_status zds_onebit_compress(const float *x, float *error, int64_t n, int32_t chunk, uint64_t *words,
+extern "C" zds_status zds_onebit_compress(const float *x, float *error, int64_t n, int32_t chunk, uint32_t *words,
                                           float *scales, void *stream) {
   clear_error();
   const char *fn = "zds_onebit_compress";
@@ -449,12 +449,11 @@ extern "C" zds_status zds_onebit_compress(const float *x, float *error, int64_t 
   if (!x || !words || !scales) return fail(ZDS_EINVAL, "%s: null pointer", fn);
   if (!aligned(x, 16) || (error && !aligned(error, 16)))
     return fail(ZDS_EALIGN, "%s: x and error must be 16-byte aligned", fn);
-  if (!aligned(words, 16) || !aligned(scales, 4))
-    return fail(ZDS_EALIGN, "%s: words must be 16-byte and scales 4-byte aligned", fn);
+  if (!aligned(words, 4) || !aligned(scales, 4)) return fail(ZDS_EALIGN, "%s: words and scales must be 4-byte aligned", fn);
   return launch_onebit_encode(x, error, n, chunk, words, scales, static_cast<hipStream_t>(stream));
 }
 
-extern "C" zds_status zds_onebit_decompress(const uint64_t *const *peer_words, const float *const *peer_scales,
+extern "C" zds_status zds_onebit_decompress(const uint32_t *const *peer_words, const float *const *peer_scales,
                                             int32_t num_peers, int64_t n, int32_t chunk, float *dst,
                                             zds_accum_mode mode, void *stream) {
   clear_error();
@@ -467,7 +466,7 @@ extern "C" zds_status zds_onebit_decompress(const uint64_t *const *peer_words, c
   if (!peer_words || !peer_scales || !dst) return fail(ZDS_EINVAL, "%s: null pointer", fn);
   for (int k = 0; k < num_peers; ++k) {
     if (!peer_words[k] || !peer_scales[k]) return fail(ZDS_EINVAL, "%s: peer %d is null", fn, k);
-    if (!aligned(peer_words[k], 8) || !aligned(peer_scales[k], 4)) return fail(ZDS_EALIGN, "%s: peer %d misaligned", fn, k);
+    if (!aligned(peer_words[k], 4) || !aligned(peer_scales[k], 4)) return fail(ZDS_EALIGN, "%s: peer %d misaligned", fn, k);
   }
   if (!aligned(dst, 16)) return fail(ZDS_EALIGN, "%s: dst must be 16-byte aligned", fn);
   return launch_onebit_decode(peer_words, peer_scales, num_peers, n, chunk, dst, mode == ZDS_ACCUMULATE,

@@ -7,29 +7,31 @@
 // be shorter): c = x + error (fp32), scale s = fp32(sqrt(sum c^2 / len)) with
 // the squares summed in float64, sign bit 1 for c >= 0, new error = c - s
 // (bit 1) or c + s (bit 0).
-// Sign words are wave lane masks: bit l of 64-bit word 4g + i is element
-// 256g + 4l + i, i.e. when lane l of a wave holds quad l of group g, word
-// 4g + i is the ballot of the lanes' i-th sign. The encoder writes a word
-// with one ballot; the decoder uses it directly as the per-lane condition of
-// a select between s and -s.
+// Sign words: 32 bits, 64 per unit of 2048 elements; bit 4r + i of word
+// 64u + l is element 2048u + 256r + 4l + i. Word l of a unit thus holds the
+// 32 signs of the elements a lane l touches when a wave walks the unit's
+// eight 256-element groups one quad per lane: the encoder's lane l ORs its
+// 4-bit nibble of each group into it, and the decoder's lane l gets all of
+// its signs for the unit from one word per peer.
 // Decode: the fp32 sum over peers, in peer order, of +-s per element.
 //
 // Both are HBM-bound streams. Encode moves 12 B/element (read x and error,
 // write error) plus 1/8 B of signs and 4/C B of scales; one block owns one
 // chunk at a time and keeps its c values in registers across the
 // block-wide sum. Decode moves N/8 + 4N/C B of payload plus 4 B out (8 B
-// when adding to the destination); its vector work per element and peer is
-// two readlanes (the sign word into scalar registers), one select and one
-// add, so with many peers it is bound by issue rather than by HBM.
+// when adding to the destination). For the first 8 peers it does not add
+// per peer: every element's result is one of the 2^N in-order fp32 sums of
+// +-s_k, which a wave tabulates in LDS per unit; the lane turns its 8 peers'
+// words into one 8-bit table index per element with a bit-matrix transpose
+// (byte gathers and three masked swap rounds) and reads its results from the
+// table. Peers 9..16 are then added in order, one select and add each.
 #include "zds_device.h"
 #include "zds_onebit.h"
 
 namespace zds {
 
-typedef uint64_t u64x2 __attribute__((ext_vector_type(2)));
-
 struct DecodeArgs {
-  const uint64_t *words[kMaxPeers];
+  const uint32_t *words[kMaxPeers];
   const float *scales[kMaxPeers];
   int32_t npeers;
   int64_t n;
@@ -42,17 +44,21 @@ struct DecodeArgs {
 // quad l of group (chunk base / 256) + 4 r + w.
 template <int R, bool EF>
 __global__ void __launch_bounds__(256) onebit_encode_kernel(const float *__restrict__ x, float *__restrict__ err,
-                                                            uint64_t *__restrict__ words,
+                                                            uint32_t *__restrict__ words,
                                                             float *__restrict__ scales, int64_t n) {
   constexpr int64_t C = 1024 * R;
+  constexpr int UNITS = R >= 2 ? R / 2 : 1;  // sign-word units a chunk covers (half of one when C = 1024)
   __shared__ float s_sh;
+  __shared__ uint32_t sw[UNITS][64];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int64_t nchunks = (n + C - 1) / C;
+  const int64_t nunits = (n + 2047) >> 11;
   for (int64_t j = blockIdx.x; j < nchunks; j += gridDim.x) {  // uniform per block
     const int64_t base = j * C;
     const int64_t len = n - base < C ? n - base : C;
+    for (int k = tid; k < UNITS * 64; k += 256) (&sw[0][0])[k] = 0u;
     float c[R][4];
     bool full[R];
 #pragma unroll
@@ -82,7 +88,7 @@ __global__ void __launch_bounds__(256) onebit_encode_kernel(const float *__restr
         const double d = c[r][i];
         ss = ss + d * d;  // the square of an fp32 value is exact in float64
       }
-    const double total = block_sum<256>(ss);
+    const double total = block_sum<256>(ss);  // its barrier also orders the zeroing of sw before the ORs
     if (tid == 0) {
       const float s = static_cast<float>(sqrt(total / static_cast<double>(len)));
       s_sh = s;
@@ -110,91 +116,164 @@ __global__ void __launch_bounds__(256) onebit_encode_kernel(const float *__restr
             if (e0 + i < n) err[e0 + i] = e[i];
         }
       }
-      const uint64_t m0 = __ballot(pos[0]), m1 = __ballot(pos[1]);
-      const uint64_t m2 = __ballot(pos[2]), m3 = __ballot(pos[3]);
+      // group g = base / 256 + 4 r + wave: unit g >> 3, nibble g & 7
       const int64_t g = (base >> 8) + 4 * r + wave;
-      if (lane < 2 && (g << 8) < n) {  // 32 bytes of words per group, 16 per lane
-        const u64x2 v = lane == 0 ? u64x2{m0, m1} : u64x2{m2, m3};
-        *reinterpret_cast<u64x2 *>(words + 4 * g + 2 * lane) = v;
-      }
+      const uint32_t nib = (pos[0] ? 1u : 0u) | (pos[1] ? 2u : 0u) | (pos[2] ? 4u : 0u) | (pos[3] ? 8u : 0u);
+      const int ul = R >= 2 ? (4 * r + wave) >> 3 : 0;
+      if (nib) atomicOr(&sw[ul][lane], nib << (4 * (g & 7)));
     }
+    __syncthreads();
+    if constexpr (R >= 2) {
+      // the chunk's whole units, 64 words each
+      const int64_t u0 = base >> 11;
+      for (int k = tid; k < UNITS * 64; k += 256)
+        if (u0 + (k >> 6) < nunits) words[64 * u0 + k] = (&sw[0][0])[k];
+    } else {
+      // half a unit: the 16-bit half of each word that holds this chunk's groups
+      const int64_t u = base >> 11, h = (base >> 10) & 1;
+      if (tid < 64) reinterpret_cast<uint16_t *>(words)[2 * (64 * u + tid) + h] =
+          static_cast<uint16_t>(sw[0][tid] >> (16 * h));
+    }
+    __syncthreads();  // the words are read out before the next chunk clears them
   }
 }
 
-// Wave w of block b decodes U consecutive groups (U = 2 for up to 8 peers,
-// else 1), starting at group U (4 b + w) and moving on by 4 U groups per
-// block of the grid; lane l takes quad l of each group. One vector load per
-// iteration brings all signs and scales of the U groups: lane t loads sign
-// word i = t % 4 of peer k = (t / 4) % NP for group t / (4 NP), and lane
-// t < U NP one scale. Each word then reaches scalar registers by readlane and
-// serves as the select condition of one element per lane. The next
-// iteration's loads are issued before this one's decode.
+// Bit-matrix transpose of the 8 peers' sign words of a lane. In: w[k] bit j
+// = sign of the lane's element j for peer k. Out: byte c of x[2b] (c < 4) or
+// of x[2b + 1] (c >= 4, byte c - 4) = sum over k of (bit 8b + c of w[k]) << k,
+// the table index of element 8b + c. Per byte b the 8x8 block (row k = byte b
+// of w[k]) is gathered into a 64-bit pair and transposed by three masked
+// swap rounds (distances 7, 14 and 28 bits).
+__device__ __forceinline__ void transpose8x32(const uint32_t (&w)[8], uint32_t (&x)[8]) {
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    const int sh = 8 * b;
+    uint32_t lo = ((w[0] >> sh) & 0xffu) | (((w[1] >> sh) & 0xffu) << 8) | (((w[2] >> sh) & 0xffu) << 16) |
+                  (((w[3] >> sh) & 0xffu) << 24);
+    uint32_t hi = ((w[4] >> sh) & 0xffu) | (((w[5] >> sh) & 0xffu) << 8) | (((w[6] >> sh) & 0xffu) << 16) |
+                  (((w[7] >> sh) & 0xffu) << 24);
+    uint32_t t;
+    t = (lo ^ (lo >> 7)) & 0x00AA00AAu;
+    lo = lo ^ t ^ (t << 7);
+    t = (hi ^ (hi >> 7)) & 0x00AA00AAu;
+    hi = hi ^ t ^ (t << 7);
+    t = (lo ^ (lo >> 14)) & 0x0000CCCCu;
+    lo = lo ^ t ^ (t << 14);
+    t = (hi ^ (hi >> 14)) & 0x0000CCCCu;
+    hi = hi ^ t ^ (t << 14);
+    t = (lo ^ (hi << 4)) & 0xF0F0F0F0u;
+    lo = lo ^ t;
+    hi = hi ^ (t >> 4);
+    x[2 * b] = lo;
+    x[2 * b + 1] = hi;
+  }
+}
+
+// Wave w of block b decodes unit 4 b + w (2048 elements) and moves on by 4
+// units per block of the grid; lane l takes quad l of each of the unit's 8
+// groups. Per unit: each lane loads its word of every peer and the peers'
+// scales; the wave writes the table of the 2^min(N, 8) in-order sums (two
+// tables when a chunk is 1024 elements, one per half unit); the lane
+// transposes its 8 words into table indices, reads its 32 results and adds
+// peers 9..N in order; then it stores its 8 quads (the wave's store of
+// quad r covers 1 KiB).
 template <bool ACC, int NP>
 __global__ void __launch_bounds__(256) onebit_decode_kernel(DecodeArgs a) {
-  constexpr int U = NP <= 8 ? 2 : 1;
+  constexpr int NT = NP < 8 ? NP : 8;  // peers in the table
+  constexpr int TS = 1 << NT;         // table entries
+  __shared__ float tab[4][2][256];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int64_t ngroups = (a.n + 255) >> 8;
-  const int wk = (lane >> 2) % NP, wu = lane / (4 * NP), wi = lane & 3;
-  const int sk = lane % NP, su = lane / NP;
-  const uint64_t *myw = a.words[0];
+  float *T0 = tab[wave][0];
+  float *T1 = tab[wave][1];
+  const int64_t nunits = (a.n + 2047) >> 11;
+  const bool halves = a.chunk_shift == 10;  // a unit spans two chunks
+  // lane k < NP loads peer k's scale of the unit's first chunk, lane 16 + k
+  // that of its second half's chunk
+  const int sk = lane & 15;
   const float *mys = a.scales[0];
 #pragma unroll
-  for (int k = 1; k < NP; ++k) {
-    if (wk == k) myw = a.words[k];
+  for (int k = 1; k < NP; ++k)
     if (sk == k) mys = a.scales[k];
-  }
-  const int64_t step = U * 4 * static_cast<int64_t>(gridDim.x);
-  int64_t g = U * (4 * static_cast<int64_t>(blockIdx.x) + wave);
-  auto fetch = [&](int64_t g0, uint64_t &w, float &sc) {
-    const int64_t gw = g0 + wu, gs = g0 + su;
-    if (wu < U && gw < ngroups) w = myw[4 * gw + wi];
-    if (su < U && gs < ngroups) sc = mys[(gs << 8) >> a.chunk_shift];
-  };
-  uint64_t w = 0;
-  float sc = 0.0f;
-  if (g < ngroups) fetch(g, w, sc);
-  for (; g < ngroups; g += step) {
-    uint64_t wn = 0;
-    float scn = 0.0f;
-    if (g + step < ngroups) fetch(g + step, wn, scn);
+  for (int64_t u = 4 * static_cast<int64_t>(blockIdx.x) + wave; u < nunits;
+       u += 4 * static_cast<int64_t>(gridDim.x)) {
+    uint32_t w[NP < 8 ? 8 : NP];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int64_t gg = g + u;
-      if (gg >= ngroups) break;
-      const int64_t e0 = (gg << 8) + 4 * lane;
-      float acc[4];
+    for (int k = 0; k < (NP < 8 ? 8 : NP); ++k) w[k] = k < NP ? a.words[k][64 * u + lane] : 0u;
+    float scl = 0.0f;
+    const int64_t e_half = (u << 11) + (lane >> 4) * 1024;  // first element of the half this lane's scale is for
+    if (sk < NP && lane < 32 && e_half < a.n) scl = mys[e_half >> a.chunk_shift];
+    float s0[NP], s1[NP];
 #pragma unroll
-      for (int k = 0; k < NP; ++k) {
-        const float s = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, sc), u * NP + k));
+    for (int k = 0; k < NP; ++k) {
+      s0[k] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, scl), k));
+      s1[k] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, scl), 16 + k));
+    }
+    // tables: entry e = the in-order sum over k < NT of (bit k of e ? s_k : -s_k).
+    // Lane l writes entries l + 64 m; bits 0..5 come from the lane, 6 and 7 from m.
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int src = 4 * (u * NP + k) + i;
-          const uint32_t lo = __builtin_amdgcn_readlane(static_cast<int>(w & 0xffffffffu), src);
-          const uint32_t hi = __builtin_amdgcn_readlane(static_cast<int>(w >> 32), src);
-          const uint64_t m = (static_cast<uint64_t>(hi) << 32) | lo;
-          const float d = __builtin_amdgcn_inverse_ballot_w64(m) ? s : -s;
-          acc[i] = k == 0 ? d : acc[i] + d;
+    for (int t = 0; t < 2; ++t) {
+      if (t == 1 && !halves) break;
+      const float *s = t == 0 ? s0 : s1;
+      float *T = t == 0 ? T0 : T1;
+      constexpr int KL = NT < 6 ? NT : 6;
+      float p = (lane & 1) ? s[0] : -s[0];
+#pragma unroll
+      for (int k = 1; k < KL; ++k) p = p + (((lane >> k) & 1) ? s[k] : -s[k]);
+      if constexpr (NT <= 6) {
+        if (lane < TS) T[lane] = p;
+      } else {
+#pragma unroll
+        for (int m = 0; m < TS / 64; ++m) {
+          float q = p + ((m & 1) ? s[6] : -s[6]);
+          if constexpr (NT == 8) q = q + ((m & 2) ? s[7] : -s[7]);
+          T[64 * m + lane] = q;
         }
       }
+    }
+    __builtin_amdgcn_wave_barrier();
+    uint32_t wt[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) wt[k] = w[k];
+    uint32_t ix[8];
+    transpose8x32(wt, ix);
+    float v[32];
+#pragma unroll
+    for (int j = 0; j < 32; ++j) {
+      const uint32_t idx = (ix[2 * (j >> 3) + ((j >> 2) & 1)] >> (8 * (j & 3))) & 0xffu;
+      const int r = j >> 2;  // the group of element j (its bit is 4 r + i)
+      // element j of the lane is bit j of its words, i.e. quad r = j / 4
+      v[j] = (halves && r >= 4 ? T1 : T0)[idx];
+    }
+    // peers past the table, in order
+#pragma unroll
+    for (int k = NT; k < NP; ++k) {
+#pragma unroll
+      for (int j = 0; j < 32; ++j) {
+        const float sc = (halves && (j >> 2) >= 4) ? s1[k] : s0[k];
+        v[j] = v[j] + (((w[k] >> j) & 1u) ? sc : -sc);
+      }
+    }
+    __builtin_amdgcn_wave_barrier();  // the table is read before the next unit rewrites it
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      const int64_t e0 = (u << 11) + 256 * r + 4 * lane;
       if (e0 + 4 <= a.n) {
-        f32x4 o = {acc[0], acc[1], acc[2], acc[3]};
+        f32x4 o = {v[4 * r], v[4 * r + 1], v[4 * r + 2], v[4 * r + 3]};
         if (ACC) {
           const f32x4 old = ld_stream(reinterpret_cast<const f32x4 *>(a.dst + e0));
-          o = f32x4{old.x + acc[0], old.y + acc[1], old.z + acc[2], old.w + acc[3]};
+          o = f32x4{old.x + o.x, old.y + o.y, old.z + o.z, old.w + o.w};
         }
         st_stream(reinterpret_cast<f32x4 *>(a.dst + e0), o);
       } else {
-        for (int i = 0; i < 4 && e0 + i < a.n; ++i) a.dst[e0 + i] = ACC ? a.dst[e0 + i] + acc[i] : acc[i];
+        for (int i = 0; i < 4 && e0 + i < a.n; ++i) a.dst[e0 + i] = ACC ? a.dst[e0 + i] + v[4 * r + i] : v[4 * r + i];
       }
     }
-    w = wn;
-    sc = scn;
   }
 }
 
 template <int R>
-static void encode_go(const float *x, float *err, uint64_t *words, float *scales, int64_t n, hipStream_t s) {
+static void encode_go(const float *x, float *err, uint32_t *words, float *scales, int64_t n, hipStream_t s) {
   int64_t g = (n + 1024 * R - 1) / (1024 * R);
   if (g > max_blocks(256)) g = max_blocks(256);
   if (err)
@@ -205,7 +284,7 @@ static void encode_go(const float *x, float *err, uint64_t *words, float *scales
                        words, scales, n);
 }
 
-zds_status launch_onebit_encode(const float *x, float *err, int64_t n, int32_t chunk, uint64_t *words, float *scales,
+zds_status launch_onebit_encode(const float *x, float *err, int64_t n, int32_t chunk, uint32_t *words, float *scales,
                                 hipStream_t s) {
   switch (chunk / 1024) {
     case 1: encode_go<1>(x, err, words, scales, n, s); break;
@@ -245,7 +324,7 @@ static void decode_np(const DecodeArgs &a, int64_t g, hipStream_t s) {
   }
 }
 
-zds_status launch_onebit_decode(const uint64_t *const *words, const float *const *scales, int32_t npeers, int64_t n,
+zds_status launch_onebit_decode(const uint32_t *const *words, const float *const *scales, int32_t npeers, int64_t n,
                                 int32_t chunk, float *dst, bool accumulate, hipStream_t s) {
   DecodeArgs a{};
   for (int k = 0; k < npeers; ++k) {
@@ -257,8 +336,7 @@ zds_status launch_onebit_decode(const uint64_t *const *words, const float *const
   a.chunk_shift = 0;
   while ((1 << a.chunk_shift) < chunk) ++a.chunk_shift;
   a.dst = dst;
-  const int64_t per_block = 4 * (npeers <= 8 ? 2 : 1);  // groups of 256 elements per block
-  int64_t g = ((n + 255) / 256 + per_block - 1) / per_block;
+  int64_t g = ((n + 2047) / 2048 + 3) / 4;  // 4 units of 2048 elements per block
   if (g > max_blocks(256)) g = max_blocks(256);
   if (accumulate) decode_np<true>(a, g, s);
   else decode_np<false>(a, g, s);

@@ -466,15 +466,16 @@ def zds_cpu_adam_step(hp, grads, master, exp_avg, exp_avg_sq, params_out, scalar
 # ------------------------------------------------------------------ 1-bit codec
 
 def onebit_payload(n, chunk, device="cuda"):
-    """Device buffers of one encoded message: (words, scales)."""
-    return (torch.zeros(4 * ((n + 255) // 256), dtype=torch.int64, device=device),
+    """Device buffers of one encoded message: (words, scales); words are
+    32-bit, 64 per 2048 elements."""
+    return (torch.zeros(64 * ((n + 2047) // 2048), dtype=torch.int32, device=device),
             torch.zeros((n + chunk - 1) // chunk, dtype=torch.float32, device=device))
 
 
 def _need_payload(words, scales, n, chunk):
     if chunk < 1:
         raise ZdsError(ZDS_EINVAL, "chunk must be positive")
-    _need_bytes(words, 32 * ((n + 255) // 256), "words")
+    _need_bytes(words, 256 * ((n + 2047) // 2048), "words")
     _need_bytes(scales, 4 * ((n + chunk - 1) // chunk), "scales")
 
 
