@@ -322,3 +322,57 @@ def test_tiny_shard_graph_replays():
     assert eb.read_state().last_skip == 0 and ea.read_state().t == 4
     plan_a.close()
     plan_b.close()
+
+
+def test_stage2_step_graph_replays():
+    """The Stage-2 step (the fused intake of 4 bf16 peers into the fp32 shard
+    grad, AdamW, the scaler) captured once into a HIP graph and replayed for
+    5 steps, the peers' slices refilled in place (an inf in one of them at
+    step 3) and eager intake work between replays. Every replay must equal
+    the same step run eagerly, bit for bit: shard grad, state, params, step
+    state and scalars."""
+    say("stage-2 step: graph replays vs eager steps")
+    n, N = 100003, 4
+    master = draw_master(n, 0.02, 3, 11)
+    cfg = dict(initial_scale_power=10, window=2, hysteresis=1)
+
+    def setup():
+        st = ShardStep(n, zds.hparams(), zds.scaler_config(**cfg), max_norm=1.0, accum_steps=N)
+        bufs = [to_dev(master, "fp32"), torch.zeros(n, dtype=torch.float32, device="cuda"),
+                torch.zeros(n, dtype=torch.float32, device="cuda"),
+                torch.zeros(n, dtype=torch.bfloat16, device="cuda")]
+        peers = [torch.empty(n, dtype=torch.bfloat16, device="cuda") for _ in range(N)]
+        return st, bufs, peers, torch.zeros(n, dtype=torch.float32, device="cuda"), zds.new_reduce_workspace(n)
+
+    def fill(peers, k, scale):
+        for i, p in enumerate(peers):
+            g = draw_grads(n, "bf16", 1e-3, scale, 5 + i, 2, k)
+            if k == 3 and i == 1:
+                g[777] = 0x7F80  # +inf
+            p.copy_(to_dev(g, "bf16"))
+
+    sa, ba, pa, acc_a, wsa = setup()
+    sb, bb, pb, acc_b, wsb = setup()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        sb.intake_norm(pb, acc_b, zds.ZDS_OVERWRITE, wsb)
+        sb.adam(acc_b, *bb)
+        sb.scaler()
+    junk = torch.empty(n, dtype=torch.float32, device="cuda")
+    for k in range(1, 6):
+        fill(pa, k, sa.read_state().scale)
+        sa.intake_norm(pa, acc_a, zds.ZDS_OVERWRITE, wsa)
+        sa.adam(acc_a, *ba)
+        sa.scaler()
+        fill(pb, k, sb.read_state().scale)
+        graph.replay()
+        zds.zds_reduce_peer_slices(pa, junk, zds.ZDS_OVERWRITE)  # eager work between replays
+        torch.cuda.synchronize()
+        for x, y in zip(ba + [acc_a], bb + [acc_b]):
+            assert torch.equal(x.view(torch.int16 if x.element_size() == 2 else torch.int32),
+                               y.view(torch.int16 if y.element_size() == 2 else torch.int32)), k
+        assert bytes(sa.read_state()) == bytes(sb.read_state()), k
+        assert bytes(sa.read_scalars()) == bytes(sb.read_scalars()), k
+    st = sb.read_state()
+    assert st.steps_skipped == 1 and st.t == 4
