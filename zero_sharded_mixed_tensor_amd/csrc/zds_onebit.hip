@@ -24,7 +24,9 @@
 // +-s_k, which a wave tabulates in LDS per unit; the lane turns its 8 peers'
 // words into one 8-bit table index per element with a bit-matrix transpose
 // (byte gathers and three masked swap rounds) and reads its results from the
-// table. Peers 9..16 are then added in order, one select and add each.
+// table. Peers 9..16 are then added in order, one select and add each. With
+// 1 or 2 peers a wave takes a quarter of a unit instead, so that it stores
+// 2 quads per lane rather than 8.
 #include "zds_device.h"
 #include "zds_onebit.h"
 
@@ -144,6 +146,26 @@ __global__ void __launch_bounds__(256) onebit_encode_kernel(const float *__restr
 // the table index of element 8b + c. Per byte b the 8x8 block (row k = byte b
 // of w[k]) is gathered into a 64-bit pair and transposed by three masked
 // swap rounds (distances 7, 14 and 28 bits).
+__device__ __forceinline__ void transpose8x8(const uint32_t (&w)[8], int b, uint32_t &xlo, uint32_t &xhi) {
+  const int sh = 8 * b;
+  uint32_t lo = ((w[0] >> sh) & 0xffu) | (((w[1] >> sh) & 0xffu) << 8) | (((w[2] >> sh) & 0xffu) << 16) |
+                (((w[3] >> sh) & 0xffu) << 24);
+  uint32_t hi = ((w[4] >> sh) & 0xffu) | (((w[5] >> sh) & 0xffu) << 8) | (((w[6] >> sh) & 0xffu) << 16) |
+                (((w[7] >> sh) & 0xffu) << 24);
+  uint32_t t;
+  t = (lo ^ (lo >> 7)) & 0x00AA00AAu;
+  lo = lo ^ t ^ (t << 7);
+  t = (hi ^ (hi >> 7)) & 0x00AA00AAu;
+  hi = hi ^ t ^ (t << 7);
+  t = (lo ^ (lo >> 14)) & 0x0000CCCCu;
+  lo = lo ^ t ^ (t << 14);
+  t = (hi ^ (hi >> 14)) & 0x0000CCCCu;
+  hi = hi ^ t ^ (t << 14);
+  t = (lo ^ (hi << 4)) & 0xF0F0F0F0u;
+  xlo = lo ^ t;
+  xhi = hi ^ (t >> 4);
+}
+
 __device__ __forceinline__ void transpose8x32(const uint32_t (&w)[8], uint32_t (&x)[8]) {
 #pragma unroll
   for (int b = 0; b < 4; ++b) {
@@ -272,6 +294,89 @@ __global__ void __launch_bounds__(256) onebit_decode_kernel(DecodeArgs a) {
   }
 }
 
+// The same for 1 or 2 peers, where the table and the transpose cost little
+// and the stores dominate: block b decodes unit b (moving on by the grid),
+// wave w the unit's groups 2w and 2w + 1, i.e. byte w of every lane word;
+// each wave builds its own copy of the unit's table and stores 2 quads per
+// lane instead of 8 (decoding into the 7B shard, interleaved A/B: 1 / 2
+// peers 0.533 / 0.537 ms against 0.608 / 0.610 for the unit kernel; at 3 / 8
+// peers 0.722 / 0.865 against 0.667 / 0.796, the quarter kernel reloading
+// every word and rebuilding the table for a quarter of the elements).
+template <bool ACC, int NP>
+__global__ void __launch_bounds__(256) onebit_decode_quarter_kernel(DecodeArgs a) {
+  constexpr int NT = NP < 8 ? NP : 8;
+  constexpr int TS = 1 << NT;
+  constexpr int WN = NP < 8 ? 8 : NP;
+  __shared__ float tab[4][256];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  float *T = tab[wave];
+  const int64_t nunits = (a.n + 2047) >> 11;
+  const int sk = lane & 15;
+  const float *mys = a.scales[0];
+#pragma unroll
+  for (int k = 1; k < NP; ++k)
+    if (sk == k) mys = a.scales[k];
+  for (int64_t u = blockIdx.x; u < nunits; u += gridDim.x) {
+    const int64_t ebase = (u << 11) + 512 * wave;  // the wave's 512 elements lie in one chunk
+    if (ebase >= a.n) continue;                    // uniform per wave
+    uint32_t w[WN];
+#pragma unroll
+    for (int k = 0; k < WN; ++k) w[k] = k < NP ? a.words[k][64 * u + lane] : 0u;
+    float scl = 0.0f;
+    if (sk < NP && lane < 16) scl = mys[ebase >> a.chunk_shift];
+    float sv[NP];
+#pragma unroll
+    for (int k = 0; k < NP; ++k)
+      sv[k] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, scl), k));
+    {
+      constexpr int KL = NT < 6 ? NT : 6;
+      float p = (lane & 1) ? sv[0] : -sv[0];
+#pragma unroll
+      for (int k = 1; k < KL; ++k) p = p + (((lane >> k) & 1) ? sv[k] : -sv[k]);
+      if constexpr (NT <= 6) {
+        if (lane < TS) T[lane] = p;
+      } else {
+#pragma unroll
+        for (int m = 0; m < TS / 64; ++m) {
+          float q = p + ((m & 1) ? sv[6] : -sv[6]);
+          if constexpr (NT == 8) q = q + ((m & 2) ? sv[7] : -sv[7]);
+          T[64 * m + lane] = q;
+        }
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
+    uint32_t wt[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) wt[k] = w[k];
+    uint32_t xlo, xhi;
+    transpose8x8(wt, wave, xlo, xhi);
+    float v[8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) v[c] = T[((c < 4 ? xlo : xhi) >> (8 * (c & 3))) & 0xffu];
+#pragma unroll
+    for (int k = NT; k < NP; ++k) {
+#pragma unroll
+      for (int c = 0; c < 8; ++c) v[c] = v[c] + (((w[k] >> (8 * wave + c)) & 1u) ? sv[k] : -sv[k]);
+    }
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int64_t e0 = (u << 11) + 256 * (2 * wave + q) + 4 * lane;
+      if (e0 + 4 <= a.n) {
+        f32x4 o = {v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]};
+        if (ACC) {
+          const f32x4 old = ld_stream(reinterpret_cast<const f32x4 *>(a.dst + e0));
+          o = f32x4{old.x + o.x, old.y + o.y, old.z + o.z, old.w + o.w};
+        }
+        st_stream(reinterpret_cast<f32x4 *>(a.dst + e0), o);
+      } else {
+        for (int i = 0; i < 4 && e0 + i < a.n; ++i) a.dst[e0 + i] = ACC ? a.dst[e0 + i] + v[4 * q + i] : v[4 * q + i];
+      }
+    }
+  }
+}
+
 template <int R>
 static void encode_go(const float *x, float *err, uint32_t *words, float *scales, int64_t n, hipStream_t s) {
   int64_t g = (n + 1024 * R - 1) / (1024 * R);
@@ -298,29 +403,35 @@ zds_status launch_onebit_encode(const float *x, float *err, int64_t n, int32_t c
 }
 
 template <bool ACC, int NP>
-static void decode_go(const DecodeArgs &a, int64_t g, hipStream_t s) {
-  hipLaunchKernelGGL((onebit_decode_kernel<ACC, NP>), dim3(static_cast<uint32_t>(g)), dim3(256), 0, s, a);
+static void decode_go(const DecodeArgs &a, hipStream_t s) {
+  const int64_t nunits = (a.n + 2047) / 2048;
+  int64_t g = NP <= 2 ? nunits : (nunits + 3) / 4;  // units per block: 1 (quarter kernel) or 4
+  if (g > max_blocks(256)) g = max_blocks(256);
+  if constexpr (NP <= 2)
+    hipLaunchKernelGGL((onebit_decode_quarter_kernel<ACC, NP>), dim3(static_cast<uint32_t>(g)), dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL((onebit_decode_kernel<ACC, NP>), dim3(static_cast<uint32_t>(g)), dim3(256), 0, s, a);
 }
 
 template <bool ACC>
-static void decode_np(const DecodeArgs &a, int64_t g, hipStream_t s) {
+static void decode_np(const DecodeArgs &a, hipStream_t s) {
   switch (a.npeers) {
-    case 1: decode_go<ACC, 1>(a, g, s); break;
-    case 2: decode_go<ACC, 2>(a, g, s); break;
-    case 3: decode_go<ACC, 3>(a, g, s); break;
-    case 4: decode_go<ACC, 4>(a, g, s); break;
-    case 5: decode_go<ACC, 5>(a, g, s); break;
-    case 6: decode_go<ACC, 6>(a, g, s); break;
-    case 7: decode_go<ACC, 7>(a, g, s); break;
-    case 8: decode_go<ACC, 8>(a, g, s); break;
-    case 9: decode_go<ACC, 9>(a, g, s); break;
-    case 10: decode_go<ACC, 10>(a, g, s); break;
-    case 11: decode_go<ACC, 11>(a, g, s); break;
-    case 12: decode_go<ACC, 12>(a, g, s); break;
-    case 13: decode_go<ACC, 13>(a, g, s); break;
-    case 14: decode_go<ACC, 14>(a, g, s); break;
-    case 15: decode_go<ACC, 15>(a, g, s); break;
-    default: decode_go<ACC, 16>(a, g, s); break;
+    case 1: decode_go<ACC, 1>(a, s); break;
+    case 2: decode_go<ACC, 2>(a, s); break;
+    case 3: decode_go<ACC, 3>(a, s); break;
+    case 4: decode_go<ACC, 4>(a, s); break;
+    case 5: decode_go<ACC, 5>(a, s); break;
+    case 6: decode_go<ACC, 6>(a, s); break;
+    case 7: decode_go<ACC, 7>(a, s); break;
+    case 8: decode_go<ACC, 8>(a, s); break;
+    case 9: decode_go<ACC, 9>(a, s); break;
+    case 10: decode_go<ACC, 10>(a, s); break;
+    case 11: decode_go<ACC, 11>(a, s); break;
+    case 12: decode_go<ACC, 12>(a, s); break;
+    case 13: decode_go<ACC, 13>(a, s); break;
+    case 14: decode_go<ACC, 14>(a, s); break;
+    case 15: decode_go<ACC, 15>(a, s); break;
+    default: decode_go<ACC, 16>(a, s); break;
   }
 }
 
@@ -336,10 +447,8 @@ zds_status launch_onebit_decode(const uint32_t *const *words, const float *const
   a.chunk_shift = 0;
   while ((1 << a.chunk_shift) < chunk) ++a.chunk_shift;
   a.dst = dst;
-  int64_t g = ((n + 2047) / 2048 + 3) / 4;  // 4 units of 2048 elements per block
-  if (g > max_blocks(256)) g = max_blocks(256);
-  if (accumulate) decode_np<true>(a, g, s);
-  else decode_np<false>(a, g, s);
+  if (accumulate) decode_np<true>(a, s);
+  else decode_np<false>(a, s);
   return check_launch("onebit decode kernel");
 }
 

@@ -37,6 +37,8 @@ KERNEL_SOURCES = {
                              "build.py"],
     "onebit_decode_kernel": ["csrc/zds_onebit.hip", "csrc/zds_onebit.h", "csrc/zds_device.h", "csrc/zds_internal.h",
                              "build.py"],
+    "onebit_decode_quarter_kernel": ["csrc/zds_onebit.hip", "csrc/zds_onebit.h", "csrc/zds_device.h",
+                                     "csrc/zds_internal.h", "build.py"],
 }
 CALIB_BYTES = 1 << 30
 
