@@ -79,6 +79,23 @@ def test_encode_matches_oracle(n, chunk):
     assert (to_host(dx) == x).all()  # x is read only
 
 
+@pytest.mark.parametrize("chunk", [1024, 2048, 4096])
+@pytest.mark.parametrize("n", [500, 2048 * 3 + 500, 2048 * 3 + 1500, 2048 * 4])
+def test_encode_overwrites_stale_words(n, chunk):
+    """Every word of the payload is written, bits past n as 0, whatever the
+    buffer held before (here all bits set)."""
+    say("encode into a stale payload n", n, "chunk", chunk)
+    x, e = _inputs(n, n + 3 * chunk)
+    o_words, o_scales, _ = O.onebit_compress(x, e, chunk)
+    words, scales = zds.onebit_payload(n, chunk)
+    words.fill_(-1)
+    scales.fill_(float("nan"))
+    zds.zds_onebit_compress(_dev(x), _dev(e), chunk, words, scales)
+    torch.cuda.synchronize()
+    assert (_words_host(words) == o_words).all()
+    assert ulp_diff32(to_host(scales), o_scales).max() <= 1
+
+
 def test_encode_without_error_buffer():
     n, chunk = 9000, 2048
     x, _ = _inputs(n, 5)

@@ -131,10 +131,16 @@ __global__ void __launch_bounds__(256) onebit_encode_kernel(const float *__restr
       for (int k = tid; k < UNITS * 64; k += 256)
         if (u0 + (k >> 6) < nunits) words[64 * u0 + k] = (&sw[0][0])[k];
     } else {
-      // half a unit: the 16-bit half of each word that holds this chunk's groups
+      // half a unit: the 16-bit half of each word that holds this chunk's
+      // groups; when the unit ends with this first half, the whole word (its
+      // upper half is past n, hence 0)
       const int64_t u = base >> 11, h = (base >> 10) & 1;
-      if (tid < 64) reinterpret_cast<uint16_t *>(words)[2 * (64 * u + tid) + h] =
-          static_cast<uint16_t>(sw[0][tid] >> (16 * h));
+      if (tid < 64) {
+        if (h == 0 && base + 1024 >= n)
+          words[64 * u + tid] = sw[0][tid];
+        else
+          reinterpret_cast<uint16_t *>(words)[2 * (64 * u + tid) + h] = static_cast<uint16_t>(sw[0][tid] >> (16 * h));
+      }
     }
     __syncthreads();  // the words are read out before the next chunk clears them
   }
