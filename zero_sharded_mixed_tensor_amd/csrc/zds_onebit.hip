@@ -41,14 +41,27 @@ struct DecodeArgs {
   float *dst;
 };
 
-// R = chunk / 1024: quads per thread per chunk. EF: an error buffer is given.
-// Iteration r of a chunk: wave w's lane l holds quad 256 r + 64 w + l, i.e.
-// quad l of group (chunk base / 256) + 4 r + w.
-template <int R, bool EF>
-__global__ void __launch_bounds__(256) onebit_encode_kernel(const float *__restrict__ x, float *__restrict__ err,
-                                                            uint32_t *__restrict__ words,
-                                                            float *__restrict__ scales, int64_t n) {
+// Threads per encode block for a chunk of 1024 R elements. Fewer quads in
+// flight per thread pay up to 8192-element chunks; at 16384 the 256-thread
+// block is best again (7B shard, encode GB/s for 256 / 512 / 1024 threads,
+// interleaved on one box: chunk 2048 5,985 / 6,149 / 6,161 (512 is the most
+// a 2048 chunk allows), 4096 5,943 / 6,124 / 6,336, 8192 5,626 / 5,686 /
+// 5,882, 16384 5,423 / 5,278 / 5,365).
+template <int R>
+constexpr int enc_block() {
+  return R == 2 ? 512 : (R == 4 || R == 8) ? 1024 : 256;
+}
+
+// R = chunk / 1024, B threads, Q = 256 R / B quads per thread. EF: an error
+// buffer is given. Iteration r of a chunk: wave w's lane l holds quad
+// B r + 64 w + l, i.e. quad l of group (chunk base / 256) + (B / 64) r + w.
+template <int R, bool EF, int B>
+__global__ void __launch_bounds__(B) onebit_encode_kernel(const float *__restrict__ x, float *__restrict__ err,
+                                                          uint32_t *__restrict__ words,
+                                                          float *__restrict__ scales, int64_t n) {
   constexpr int64_t C = 1024 * R;
+  constexpr int Q = 256 * R / B;  // quads per thread
+  constexpr int WPB = B / 64;     // waves per block
   constexpr int UNITS = R >= 2 ? R / 2 : 1;  // sign-word units a chunk covers (half of one when C = 1024)
   __shared__ float s_sh;
   __shared__ uint32_t sw[UNITS][64];
@@ -60,12 +73,12 @@ __global__ void __launch_bounds__(256) onebit_encode_kernel(const float *__restr
   for (int64_t j = blockIdx.x; j < nchunks; j += gridDim.x) {  // uniform per block
     const int64_t base = j * C;
     const int64_t len = n - base < C ? n - base : C;
-    for (int k = tid; k < UNITS * 64; k += 256) (&sw[0][0])[k] = 0u;
-    float c[R][4];
-    bool full[R];
+    for (int k = tid; k < UNITS * 64; k += B) (&sw[0][0])[k] = 0u;
+    float c[Q][4];
+    bool full[Q];
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-      const int64_t e0 = base + 4 * (r * 256 + tid);
+    for (int r = 0; r < Q; ++r) {
+      const int64_t e0 = base + 4 * (r * B + tid);
       full[r] = e0 + 4 <= n;
       if (full[r]) {
         const f32x4 a = ld_stream(reinterpret_cast<const f32x4 *>(x + e0));
@@ -84,13 +97,13 @@ __global__ void __launch_bounds__(256) onebit_encode_kernel(const float *__restr
     }
     double ss = 0.0;
 #pragma unroll
-    for (int r = 0; r < R; ++r)
+    for (int r = 0; r < Q; ++r)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const double d = c[r][i];
         ss = ss + d * d;  // the square of an fp32 value is exact in float64
       }
-    const double total = block_sum<256>(ss);  // its barrier also orders the zeroing of sw before the ORs
+    const double total = block_sum<B>(ss);  // its barrier also orders the zeroing of sw before the ORs
     if (tid == 0) {
       const float s = static_cast<float>(sqrt(total / static_cast<double>(len)));
       s_sh = s;
@@ -99,8 +112,8 @@ __global__ void __launch_bounds__(256) onebit_encode_kernel(const float *__restr
     __syncthreads();
     const float s = s_sh;
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-      const int64_t e0 = base + 4 * (r * 256 + tid);
+    for (int r = 0; r < Q; ++r) {
+      const int64_t e0 = base + 4 * (r * B + tid);
       bool pos[4];
       float e[4];
 #pragma unroll
@@ -119,16 +132,16 @@ __global__ void __launch_bounds__(256) onebit_encode_kernel(const float *__restr
         }
       }
       // group g = base / 256 + 4 r + wave: unit g >> 3, nibble g & 7
-      const int64_t g = (base >> 8) + 4 * r + wave;
+      const int64_t g = (base >> 8) + WPB * r + wave;
       const uint32_t nib = (pos[0] ? 1u : 0u) | (pos[1] ? 2u : 0u) | (pos[2] ? 4u : 0u) | (pos[3] ? 8u : 0u);
-      const int ul = R >= 2 ? (4 * r + wave) >> 3 : 0;
+      const int ul = R >= 2 ? (WPB * r + wave) >> 3 : 0;
       if (nib) atomicOr(&sw[ul][lane], nib << (4 * (g & 7)));
     }
     __syncthreads();
     if constexpr (R >= 2) {
       // the chunk's whole units, 64 words each
       const int64_t u0 = base >> 11;
-      for (int k = tid; k < UNITS * 64; k += 256)
+      for (int k = tid; k < UNITS * 64; k += B)
         if (u0 + (k >> 6) < nunits) words[64 * u0 + k] = (&sw[0][0])[k];
     } else {
       // half a unit: the 16-bit half of each word that holds this chunk's
@@ -385,13 +398,14 @@ __global__ void __launch_bounds__(256) onebit_decode_quarter_kernel(DecodeArgs a
 
 template <int R>
 static void encode_go(const float *x, float *err, uint32_t *words, float *scales, int64_t n, hipStream_t s) {
+  constexpr int B = enc_block<R>();
   int64_t g = (n + 1024 * R - 1) / (1024 * R);
-  if (g > max_blocks(256)) g = max_blocks(256);
+  if (g > max_blocks(B)) g = max_blocks(B);
   if (err)
-    hipLaunchKernelGGL((onebit_encode_kernel<R, true>), dim3(static_cast<uint32_t>(g)), dim3(256), 0, s, x, err,
+    hipLaunchKernelGGL((onebit_encode_kernel<R, true, B>), dim3(static_cast<uint32_t>(g)), dim3(B), 0, s, x, err,
                        words, scales, n);
   else
-    hipLaunchKernelGGL((onebit_encode_kernel<R, false>), dim3(static_cast<uint32_t>(g)), dim3(256), 0, s, x, err,
+    hipLaunchKernelGGL((onebit_encode_kernel<R, false, B>), dim3(static_cast<uint32_t>(g)), dim3(B), 0, s, x, err,
                        words, scales, n);
 }
 
