@@ -465,10 +465,12 @@ def run_checkpoint(args, w):
 # ------------------------------------------------------------------ CPU oracle part
 
 def run_cpu_baseline(w, sample, repeats, min_seconds=10.0):
-    """Time the oracle's step (flatten copy, overflow + norm, AdamW + cast,
-    scaler update) on the first `sample` params of the same workload, at least
-    `repeats` times and for at least `min_seconds`, with inputs generated before
-    timing. Single process: NumPy's elementwise kernels use one thread."""
+    """Time the oracle's step for the workload (the flatten copy, or the K
+    micro-batch accumulation, or the intake of the peers' slices; then
+    overflow + norm, AdamW + cast, scaler update) on the first `sample` params
+    of the same workload, at least `repeats` times and for at least
+    `min_seconds`, with inputs generated before timing. Single process:
+    NumPy's elementwise kernels use one thread."""
     import numpy as np
     import oracle as O
     from workloads import draw_grads, draw_master, draw_prior_moments
@@ -488,12 +490,51 @@ def run_cpu_baseline(w, sample, repeats, min_seconds=10.0):
                            static_scale=1.0)
     ent = [(0, 0, n, 0)]
     bucket = np.zeros(n, np.uint16)
+    acc = np.zeros(n, np.float32)
+    scale = 1.0 if w["scale"] is None else 2.0 ** w["scale"]
+    extra = []
+    if w["mode"] == "intake":
+        extra = [draw_grads(n, w["gdt"], w["sigma"], scale, 2 + k, 2, 0) for k in range(w["peers"] - 1)]
+    elif w["mode"] == "accumulate":
+        extra = [draw_grads(n, w["gdt"], w["sigma"], scale, 2 + k, 2, 0) for k in range(w["accum"] - 1)]
     t0 = time.perf_counter()
     done = 0
     while done < repeats or time.perf_counter() - t0 < min_seconds:
-        O.flatten_copy([g], ent, bucket)
-        r = O.optimizer_step(bucket, w["gdt"], master, m, v, st, O.AdamW(), 1.0, 1, w["pdt"])
+        if w["mode"] == "intake":
+            x = O.reduce_peer_slices([g] + extra, w["gdt"], None, "fp32", accumulate=False)
+            r = O.optimizer_step(x, "fp32", master, m, v, st, O.AdamW(), 1.0, w["accum"], w["pdt"])
+        elif w["mode"] == "accumulate":
+            for k, src in enumerate([g] + extra):
+                O.flatten_accumulate([src], w["gdt"], ent, acc, overwrite=(k == 0))
+            r = O.optimizer_step(acc, "fp32", master, m, v, st, O.AdamW(), 1.0, w["accum"], w["pdt"])
+        else:
+            O.flatten_copy([g], ent, bucket)
+            r = O.optimizer_step(bucket, w["gdt"], master, m, v, st, O.AdamW(), 1.0, 1, w["pdt"])
         assert r[3] is not None
+        done += 1
+    dt = time.perf_counter() - t0
+    what = {"intake": "intake of %d peers' slices" % w.get("peers", 0),
+            "accumulate": "accumulation of %d micro-batches" % w["accum"]}.get(w["mode"], "copy")
+    return dict(value=n * done / dt, seconds=dt, n=n, repeats=done, what=what)
+
+
+def run_cpu_baseline_onebit(w, sample, repeats, min_seconds=10.0):
+    """Time the oracle's codec work per exchange (encode with error feedback,
+    then the decode of N peers' payloads) on `sample` elements, at least
+    `repeats` times and for at least `min_seconds`."""
+    import numpy as np
+    import oracle as O
+    n, chunk, N = sample, w["chunk"], w["peers"]
+    rng = np.random.default_rng(3)
+    x = (rng.standard_normal(n) * w["sigma"]).astype(np.float32)
+    err = np.zeros(n, np.float32)
+    peers = [O.onebit_compress((rng.standard_normal(n) * w["sigma"]).astype(np.float32), np.zeros(n, np.float32),
+                               chunk)[:2] for _ in range(N)]
+    t0 = time.perf_counter()
+    done = 0
+    while done < repeats or time.perf_counter() - t0 < min_seconds:
+        _, _, err = O.onebit_compress(x, err, chunk)
+        O.onebit_decompress(peers, n, chunk, None, False)
         done += 1
     dt = time.perf_counter() - t0
     return dict(value=n * done / dt, seconds=dt, n=n, repeats=done)
@@ -537,6 +578,12 @@ def main():
         out = run_onebit(args, w)
         if args.copy_calibration:
             out["copy_calibration"] = _copy_calibration()
+        if not args.no_cpu_baseline:
+            c = run_cpu_baseline_onebit(w, min(args.cpu_sample, 1 << 18), args.cpu_repeats)
+            out["cpu_baseline"] = {
+                "value": round(c["value"], 1), "unit": "elements/s", "cores": 1, "kind": "oracle",
+                "sample": "%d passes of the oracle's encode (with error feedback) and %d-peer decode over %d "
+                          "elements, %.1f s" % (c["repeats"], w["peers"], c["n"], c["seconds"])}
         print(json.dumps(out), flush=True)
         return 0
     if w.get("checkpoint"):
@@ -593,9 +640,9 @@ def main():
             "unit": "params/s",
             "cores": 1,
             "kind": "oracle",
-            "sample": "%d passes of one whole oracle step (copy, overflow+norm, AdamW, cast, scaler) "
+            "sample": "%d passes of one whole oracle step (%s, overflow+norm, AdamW, cast, scaler) "
                       "over the first %d params of the same workload, %.1f s"
-                      % (c["repeats"], c["n"], c["seconds"]),
+                      % (c["repeats"], c["what"], c["n"], c["seconds"]),
         }
     print(json.dumps(out), flush=True)
     return 0

@@ -103,3 +103,17 @@ def test_bench_byte_model():
     w = bench._workload("llama7b_s2_intake8")
     assert bench._bytes_per_param(w, False) == dict(accum_total=20, norm=4, adam=30)
     assert bench._bytes_per_param(w, True) == dict(accum_total=20, norm=0, adam=30)
+
+
+@pytest.mark.parametrize("workload", ["llama7b_s1", "llama7b_s1_accum16", "llama7b_s2_intake8", "llama7b_s1_onebit8"])
+def test_cpu_baselines_time_the_workloads_own_oracle_step(workload):
+    sys.path.insert(0, ROOT)
+    import bench
+    w = bench._workload(workload)
+    if w.get("onebit"):
+        c = bench.run_cpu_baseline_onebit(w, 4096, 1, min_seconds=0.0)
+    else:
+        c = bench.run_cpu_baseline(w, 4096, 1, min_seconds=0.0)
+        assert c["what"] == {"llama7b_s1": "copy", "llama7b_s1_accum16": "accumulation of 16 micro-batches",
+                             "llama7b_s2_intake8": "intake of 8 peers' slices"}[workload]
+    assert c["repeats"] == 1 and c["n"] == 4096 and c["value"] > 0
