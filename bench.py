@@ -540,7 +540,7 @@ def run_cpu_baseline_onebit(w, sample, repeats, min_seconds=10.0):
     return dict(value=n * done / dt, seconds=dt, n=n, repeats=done)
 
 
-def _traffic(workload, n, kernel="adam_tile_kernel"):
+def _traffic(workload, n, kernel="adam_wide_kernel"):
     """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
     summary of this workload (FETCH_SIZE and WRITE_SIZE, each scaled by a
     copy of known size), or None when there is none or the kernel's sources

@@ -43,15 +43,18 @@ def _inputs(n, gdt, seed, scale=2.0 ** 12, sigma=1e-3, prior=True):
     return g, p, m, v
 
 
-def _run_step(g, p, m, v, gdt, pdt, scale_pow, t0, max_norm, hp, offset=0, accum=1, dynamic=True):
+def _run_step(g, p, m, v, gdt, pdt, scale_pow, t0, max_norm, hp, offset=0, accum=1, dynamic=True, offset16=0):
     """One step on the GPU. offset > 0 places every buffer `offset` elements
-    into a larger allocation (element-aligned, not 16-byte aligned)."""
+    into a larger allocation (element-aligned, not 16-byte aligned); offset16
+    does the same for the 16-bit buffers only (grads when 16-bit, params out)."""
     n = p.shape[0]
-    dg = to_dev(np.concatenate([np.zeros(offset, g.dtype), g]), gdt)[offset:]
+    og = offset + (offset16 if gdt != "fp32" else 0)
+    oo = offset + offset16
+    dg = to_dev(np.concatenate([np.zeros(og, g.dtype), g]), gdt)[og:]
     dp = to_dev(np.concatenate([np.zeros(offset, np.float32), p]), "fp32")[offset:]
     dm = to_dev(np.concatenate([np.zeros(offset, np.float32), m]), "fp32")[offset:]
     dv = to_dev(np.concatenate([np.zeros(offset, np.float32), v]), "fp32")[offset:]
-    dout = to_dev(np.concatenate([np.zeros(offset, np.uint16), np.full(n, 0x7E00, np.uint16)]), pdt)[offset:]
+    dout = to_dev(np.concatenate([np.zeros(oo, np.uint16), np.full(n, 0x7E00, np.uint16)]), pdt)[oo:]
     b1p = float(np.float32(hp.beta1)) ** t0
     b2p = float(np.float32(hp.beta2)) ** t0
     cfg = zds.scaler_config(dynamic=dynamic, initial_scale_power=scale_pow, window=1000, hysteresis=1,
@@ -104,6 +107,23 @@ def test_adam_step_misaligned_buffers(n, gdt):
     g, p, m, v = _inputs(n, gdt, 31 + n)
     P, M, V, OUT, sc, st, pows = _run_step(g, p, m, v, gdt, "bf16", 12, 1, 1.0, hp, offset=1)
     oP, oM, oV, oOUT, ost, osc = _oracle_step(g, p, m, v, gdt, "bf16", 2.0 ** 12, 1, pows, 1.0, hp)
+    assert sc.grad_scale == osc["grad_scale"]
+    assert_state_close("master", P, oP, 2)
+    assert_state_close("exp_avg", M, oM, 2)
+    assert_state_close("exp_avg_sq", V, oV, 2)
+    assert_p16_close("params_out", OUT, oOUT, 1)
+
+
+@pytest.mark.parametrize("n", [1, 9, 4099, 512 * 37 + 13, 65536 + 3])
+@pytest.mark.parametrize("gdt,pdt", [("fp16", "fp16"), ("bf16", "bf16"), ("fp32", "bf16")])
+def test_adam_step_8_byte_aligned_16bit_buffers(n, gdt, pdt):
+    """16-bit buffers 8- but not 16-byte aligned (fp32 arrays 16-byte aligned):
+    the 4-wave tile path instead of the 8-wave one."""
+    say("adam 16-bit buffers at 8-byte alignment n=%d grads=%s params=%s" % (n, gdt, pdt))
+    hp = O.AdamW()
+    g, p, m, v = _inputs(n, gdt, 57 + n)
+    P, M, V, OUT, sc, st, pows = _run_step(g, p, m, v, gdt, pdt, 12, 1, 1.0, hp, offset16=4)
+    oP, oM, oV, oOUT, ost, osc = _oracle_step(g, p, m, v, gdt, pdt, 2.0 ** 12, 1, pows, 1.0, hp)
     assert sc.grad_scale == osc["grad_scale"]
     assert_state_close("master", P, oP, 2)
     assert_state_close("exp_avg", M, oM, 2)

@@ -25,7 +25,13 @@
 // dispatcher keeps every CU full as blocks finish. Issuing the second tile's
 // loads before the first tile's update (software pipelining) measured slower
 // (6.0 TB/s): on this memory system more bytes in flight per wave lose to
-// more waves with one access each.
+// more waves with one access each. The default is the wide form of that
+// kernel (adam_wide_kernel): 8 waves and 512 elements per tile, so that the
+// 16-bit grads and params also move as one 1 KiB access per wave (16 bytes
+// per lane), like the fp32 arrays; in interleaved A/B runs on three boxes it
+// was 1-3 % faster than the 4-wave tile, which remains the path for 16-bit
+// buffers that are 8- but not 16-byte aligned. (Loading each wave's next tile
+// before storing its current one measured no better.)
 //
 // The step constants (lr / (1 - beta1^t), sqrt(1 - beta2^t), 1 - lr*wd, the
 // 1 - beta values) are derived once per call by a single-wave prep kernel
@@ -244,6 +250,83 @@ __global__ void __launch_bounds__(256) adam_tile_kernel(AdamArgs a) {
   }
 }
 
+// Wide wave-specialised variant. A block of 8 waves owns a tile of 512
+// elements: waves 0-1 move the two 1 KiB halves of the master tile, 2-3 m,
+// 4-5 v; 16-bit grads come in through wave 6 (8 elements per lane, one 1 KiB
+// access) and the 16-bit params go out through wave 7; fp32 grads come in
+// through waves 6 and 7 (a half each). Each of the 512 threads updates one
+// element. The tiles cover the first n & ~7 elements; block 0 takes the rest
+// element-wise. As in the 4-wave kernel, outside the update phase each wave
+// writes and reads only its own part of the LDS tiles, so two barriers per
+// tile suffice.
+template <int GD, int PD, bool WRITE_OUT>
+__global__ void __launch_bounds__(512) adam_wide_kernel(AdamArgs a) {
+  __shared__ f32x4 sf[3][128];
+  __shared__ f32x4 sgf[GD == ZDS_FP32 ? 128 : 1];
+  __shared__ u32x4 sg16[GD == ZDS_FP32 ? 1 : 64];
+  __shared__ u32x4 so16[64];
+  if (a.sc->overflow) return;
+  const ElemConsts c = load_consts(a);
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  const int64_t nv = a.n & ~int64_t(7);
+  const int64_t quads = nv >> 2;
+  const int64_t octs = nv >> 3;
+  const int64_t ntiles = (nv + 511) >> 9;
+  // This wave's half of a 128-quad tile (waves 0-5, and 6-7 for fp32 grads).
+  const int half = (w & 1) * 64 + lane;
+  float *arr = w < 2 ? a.p : (w < 4 ? a.m : a.v);
+  for (int64_t it = static_cast<int64_t>(blockIdx.x) * ZDS_ADAM_TPB; it < ntiles;
+       it += static_cast<int64_t>(gridDim.x) * ZDS_ADAM_TPB)
+  for (int64_t tile = it; tile < it + ZDS_ADAM_TPB && tile < ntiles; ++tile) {  // uniform per block
+    const int64_t q = tile * 128 + half;
+    const int64_t o = tile * 64 + lane;
+    if (w < 6) {
+      if (q < quads) sf[w >> 1][half] = ld_stream(reinterpret_cast<const f32x4 *>(arr) + q);
+    } else if (GD == ZDS_FP32) {
+      if (q < quads) sgf[half] = ld_stream(static_cast<const f32x4 *>(a.g) + q);
+    } else if (w == 6) {
+      if (o < octs) sg16[lane] = ld_stream(static_cast<const u32x4 *>(a.g) + o);
+    }
+    __syncthreads();
+    const int t = threadIdx.x;
+    if (tile * 512 + t < nv) {
+      float *fp = reinterpret_cast<float *>(sf[0]);
+      float *fm = reinterpret_cast<float *>(sf[1]);
+      float *fv = reinterpret_cast<float *>(sf[2]);
+      float x;
+      if (GD == ZDS_FP32) {
+        x = reinterpret_cast<const float *>(sgf)[t];
+      } else {
+        const uint32_t b = reinterpret_cast<const uint16_t *>(sg16)[t];
+        x = GD == ZDS_BF16 ? __uint_as_float(b << 16) : __half2float(__ushort_as_half(static_cast<unsigned short>(b)));
+      }
+      float p = fp[t], m = fm[t], v = fv[t];
+      adam_elem(x, c, p, m, v);
+      fp[t] = p;
+      fm[t] = m;
+      fv[t] = v;
+      if (WRITE_OUT) reinterpret_cast<uint16_t *>(so16)[t] = narrow1<PD>(p);
+    }
+    __syncthreads();
+    if (w < 6) {
+      if (q < quads) st_stream(reinterpret_cast<f32x4 *>(arr) + q, sf[w >> 1][half]);
+    } else if (WRITE_OUT && w == 7) {
+      if (o < octs) st_stream(static_cast<u32x4 *>(a.out) + o, so16[lane]);
+    }
+  }
+  // Ragged tail: the last n % 8 elements, one per lane of block 0.
+  if (blockIdx.x == 0 && nv + threadIdx.x < a.n) {
+    const int64_t e = nv + threadIdx.x;
+    float p = a.p[e], m = a.m[e], v = a.v[e];
+    adam_elem(widen1<GD>(a.g, e), c, p, m, v);
+    a.p[e] = p;
+    a.m[e] = m;
+    a.v[e] = v;
+    if (WRITE_OUT) static_cast<uint16_t *>(a.out)[e] = narrow1<PD>(p);
+  }
+}
+
 // Element-wise path for buffers without the vector alignment.
 template <int GD, int PD, bool WRITE_OUT>
 __global__ void __launch_bounds__(ZDS_ADAM_BLOCK) adam_scalar_kernel(AdamArgs a) {
@@ -289,8 +372,15 @@ static int resident_blocks_per_cu(K kernel) {
 static int64_t round8(int64_t g) { return ZDS_ADAM_XCD ? ((g + 7) / 8) * 8 : g; }
 
 template <int GD, int PD, bool WO>
-static void launch_one(bool vec, hipStream_t s, const AdamArgs &a) {
-  if (vec && ZDS_ADAM_TILE) {
+static void launch_one(bool vec, bool vec16, hipStream_t s, const AdamArgs &a) {
+  if (vec16 && ZDS_ADAM_TILE) {
+    // One block per ZDS_ADAM_TPB tiles up to max_blocks(512); larger arrays loop.
+    int64_t g = round8((((a.n & ~int64_t(7)) + 511) / 512 + ZDS_ADAM_TPB - 1) / ZDS_ADAM_TPB);
+    if (g < 8) g = 8;
+    if (g > max_blocks(512)) g = max_blocks(512) & ~int64_t(7);
+    if (g > ZDS_ADAM_TILE_GRID) g = ZDS_ADAM_TILE_GRID;
+    hipLaunchKernelGGL((adam_wide_kernel<GD, PD, WO>), dim3(static_cast<uint32_t>(g)), dim3(512), 0, s, a);
+  } else if (vec && ZDS_ADAM_TILE) {
     // One block per tile up to max_blocks(256) (a dispatch holds fewer than 2^32
     // work-items); larger arrays loop over the tiles.
     int64_t g = round8((((a.n >> 2) + 63) / 64 + ZDS_ADAM_TPB - 1) / ZDS_ADAM_TPB);
@@ -326,13 +416,13 @@ static void launch_one(bool vec, hipStream_t s, const AdamArgs &a) {
 }
 
 template <int GD>
-static void launch_gd(zds_dtype pdt, bool wo, bool vec, hipStream_t s, const AdamArgs &a) {
+static void launch_gd(zds_dtype pdt, bool wo, bool vec, bool vec16, hipStream_t s, const AdamArgs &a) {
   if (!wo) {
-    launch_one<GD, ZDS_FP16, false>(vec, s, a);
+    launch_one<GD, ZDS_FP16, false>(vec, vec16, s, a);
   } else if (pdt == ZDS_BF16) {
-    launch_one<GD, ZDS_BF16, true>(vec, s, a);
+    launch_one<GD, ZDS_BF16, true>(vec, vec16, s, a);
   } else {
-    launch_one<GD, ZDS_FP16, true>(vec, s, a);
+    launch_one<GD, ZDS_FP16, true>(vec, vec16, s, a);
   }
 }
 
@@ -345,10 +435,11 @@ zds_status launch_adam(const zds_adamw_hparams &hp, const void *grads, zds_dtype
   AdamArgs a{grads, master, m, v, out, n, hp.beta1, hp.beta2, hp.eps, scalars};
   const bool vec = aligned(grads, gdt == ZDS_FP32 ? 16 : 8) && aligned(master, 16) && aligned(m, 16) &&
                    aligned(v, 16) && (out == nullptr || aligned(out, 8));
+  const bool vec16 = vec && aligned(grads, 16) && (out == nullptr || aligned(out, 16));
   switch (gdt) {
-    case ZDS_FP16: launch_gd<ZDS_FP16>(pdt, out != nullptr, vec, stream, a); break;
-    case ZDS_BF16: launch_gd<ZDS_BF16>(pdt, out != nullptr, vec, stream, a); break;
-    default: launch_gd<ZDS_FP32>(pdt, out != nullptr, vec, stream, a); break;
+    case ZDS_FP16: launch_gd<ZDS_FP16>(pdt, out != nullptr, vec, vec16, stream, a); break;
+    case ZDS_BF16: launch_gd<ZDS_BF16>(pdt, out != nullptr, vec, vec16, stream, a); break;
+    default: launch_gd<ZDS_FP32>(pdt, out != nullptr, vec, vec16, stream, a); break;
   }
   return check_launch("adam_step kernel");
 }
