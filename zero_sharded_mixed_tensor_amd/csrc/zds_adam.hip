@@ -10,28 +10,29 @@
 // 28 B (16-bit grads) or 30 B (fp32 accumulator).
 //
 // Access pattern. Every wave-level load or store covers one contiguous range
-// (1 KiB of fp32, 512 B of 16-bit) so each 128-byte line is requested by
-// exactly one instruction; non-temporal hints on all of them. (Two 16-byte
-// pieces per lane at stride 32 B make two instructions each touch every line
-// half, which measured far slower.) The default kernel is wave-specialised: a
-// 4-wave block owns a tile of 256 elements and each wave moves one array of
-// it (master, m, v, grads in / 16-bit params out), the tiles meeting in LDS
-// where every thread updates one element. Measured against a kernel in which
-// each lane moves all arrays of its own 4 elements (kept as adam_quad_kernel),
-// this lowers the memory footprint per wave from 4 loads + 4 stores to 1 + 1
-// and raised the pass from about 5.8 to 6.0 TB/s on the 7B shard. Each block
-// then takes 2 consecutive tiles (6.0 -> 6.3 TB/s: half the block launches,
-// same footprint per wave), and the grid has one block per tile pair, so the
-// dispatcher keeps every CU full as blocks finish. Issuing the second tile's
-// loads before the first tile's update (software pipelining) measured slower
-// (6.0 TB/s): on this memory system more bytes in flight per wave lose to
-// more waves with one access each. The default is the wide form of that
-// kernel (adam_wide_kernel): 8 waves and 512 elements per tile, so that the
-// 16-bit grads and params also move as one 1 KiB access per wave (16 bytes
-// per lane), like the fp32 arrays; in interleaved A/B runs on three boxes it
-// was 1-3 % faster than the 4-wave tile, which remains the path for 16-bit
-// buffers that are 8- but not 16-byte aligned. (Loading each wave's next tile
-// before storing its current one measured no better.)
+// so each 128-byte line is requested by exactly one instruction;
+// non-temporal hints on all of them. (Two 16-byte pieces per lane at stride
+// 32 B make two instructions each touch every line half, which measured far
+// slower.) The kernels are wave-specialised: each wave of a block moves one
+// array piece of the block's tile (master, m, v, grads in / 16-bit params
+// out), and the pieces meet in LDS where every thread updates one element.
+// Against a kernel in which each lane moves all arrays of its own 4 elements
+// (kept as adam_quad_kernel), this lowers the memory footprint per wave from
+// 4 loads + 4 stores to 1 + 1 and raised the pass from about 5.8 to 6.0 TB/s
+// on the 7B shard. A block takes 2 consecutive tiles (6.0 -> 6.3 TB/s: half
+// the block launches, same footprint per wave) and the grid has one block per
+// tile pair, so the dispatcher keeps every CU full as blocks finish. Issuing
+// the second tile's loads before the first tile's update (software
+// pipelining) measured slower: on this memory system more bytes in flight per
+// wave lose to more waves with one access each.
+//
+// The default is adam_wide_kernel: 8 waves and 512 elements per tile, so that
+// the 16-bit grads and params also move as one 1 KiB access per wave (16
+// bytes per lane), like the fp32 halves; in A/B runs interleaved with the
+// order rotated each round it was 1.0 and 2.7 % faster (two boxes) than
+// adam_tile_kernel, the 4-wave form with 256-element tiles and 512-byte
+// 16-bit accesses, which remains the path for 16-bit buffers that are 8- but
+// not 16-byte aligned.
 //
 // The step constants (lr / (1 - beta1^t), sqrt(1 - beta2^t), 1 - lr*wd, the
 // 1 - beta values) are derived once per call by a single-wave prep kernel
