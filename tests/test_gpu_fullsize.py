@@ -513,3 +513,40 @@ def test_beyond_the_grid_cap_intake_and_codec():
                 scales[a // chunk:(b + chunk - 1) // chunk].cpu().numpy())]
         want = O.onebit_decompress(pay, b - a, chunk, None, False)
         assert (acc[a:b].cpu().numpy().view(np.uint32) == want.view(np.uint32)).all(), u
+
+
+def test_adam_step_beyond_the_grid_cap():
+    """n = 2^33 + 1003 elements, past the AdamW kernel's grid cap (2^23 blocks
+    of two 512-element tiles), so its blocks loop over a second round of tiles,
+    and with a ragged n % 8 tail: bf16 grads N(0, 2e-3), static scale 1, clip
+    1.0, prior moments. Sampled elements (random, both ends, and the tiles
+    around the first one a block reaches on its second round) against the
+    oracle; the sum of squares against a float64 sum on the device."""
+    from workloads.device import fill_normal_
+    n = (1 << 33) + 1003
+    say("AdamW beyond the grid cap: n =", n)
+    grads = fill_normal_(torch.empty(n, dtype=torch.bfloat16, device="cuda"), 2e-3, 131)
+    master = draw_master_(torch.empty(n, dtype=torch.float32, device="cuda"), 132)
+    m = torch.empty(n, dtype=torch.float32, device="cuda")
+    v = torch.empty(n, dtype=torch.float32, device="cuda")
+    draw_prior_moments_(m, v, 2e-3, 133)
+    out = torch.empty(n, dtype=torch.bfloat16, device="cuda")
+    wrap = (1 << 23) * 2 * 512  # first element past one round of the capped grid (an upper bound on the cap)
+    rng = np.random.default_rng(134)
+    idx = np.concatenate([rng.integers(0, n, 65536), np.arange(0, 64), np.arange(n - 1100, n),
+                          np.arange(wrap - 8192 - 600, wrap - 8192 + 600), np.arange(wrap - 600, wrap + 600)])
+    idx = torch.from_numpy(np.unique(idx).astype(np.int64)).cuda()
+    P0, M0, V0 = master[idx].cpu().numpy(), m[idx].cpu().numpy(), v[idx].cpu().numpy()
+    g_idx = _h16(grads[idx])
+    st = ShardStep(n, zds.hparams(), zds.scaler_config(dynamic=False, static_scale=1.0), max_norm=1.0,
+                   t0=1, beta1_pow0=B1, beta2_pow0=B2)
+    st.step(grads, master, m, v, out)
+    ssum = _torch_sumsq(grads)
+    torch.cuda.synchronize()
+    osc = _oracle_scalars(ssum, 1.0, 1, 1.0, 0)
+    _compare_scalars(st.read_scalars(), osc)
+    ost = O.scaler_init(dynamic=False, static_scale=1.0, t=1, beta1_pow=B1, beta2_pow=B2)
+    want = _oracle_update(g_idx, "bf16", osc, ost, P0, M0, V0, "bf16")
+    _compare_samples("beyond the grid cap", idx, master, m, v, out, want)
+    s = st.read_state()
+    assert s.t == 2 and s.last_skip == 0
