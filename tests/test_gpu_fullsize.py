@@ -515,26 +515,33 @@ def test_beyond_the_grid_cap_intake_and_codec():
         assert (acc[a:b].cpu().numpy().view(np.uint32) == want.view(np.uint32)).all(), u
 
 
-def test_adam_step_beyond_the_grid_cap():
-    """n = 2^33 + 1003 elements, past the AdamW kernel's grid cap (2^23 blocks
-    of two 512-element tiles), so its blocks loop over a second round of tiles,
-    and with a ragged n % 8 tail: bf16 grads N(0, 2e-3), static scale 1, clip
-    1.0, prior moments. Sampled elements (random, both ends, and the tiles
-    around the first one a block reaches on its second round) against the
-    oracle; the sum of squares against a float64 sum on the device."""
+@pytest.mark.parametrize("offset16", [0, 4])
+def test_adam_step_beyond_the_grid_cap(offset16):
+    """n = 2^33 + 1003 elements, past the AdamW kernels' grid caps, so blocks
+    loop over a second round of tiles, with a ragged n % 8 tail: bf16 grads
+    N(0, 2e-3), static scale 1, clip 1.0, prior moments. offset16 = 0: the
+    8-wave kernel (cap 8,388,600 blocks of two 512-element tiles); 4: the
+    16-bit buffers start 8 bytes into their allocations, which takes the 4-wave
+    kernel (cap 16,777,208 blocks of two 256-element tiles). Sampled elements
+    (random, both ends, and around the first tiles of each kernel's second
+    round) against the oracle; the sum of squares against a float64 sum on the
+    device."""
     from workloads.device import fill_normal_
     n = (1 << 33) + 1003
-    say("AdamW beyond the grid cap: n =", n)
-    grads = fill_normal_(torch.empty(n, dtype=torch.bfloat16, device="cuda"), 2e-3, 131)
+    say("AdamW beyond the grid cap: n =", n, "16-bit offset", offset16)
+    graw = fill_normal_(torch.empty(n + offset16, dtype=torch.bfloat16, device="cuda"), 2e-3, 131)
+    grads = graw[offset16:]
     master = draw_master_(torch.empty(n, dtype=torch.float32, device="cuda"), 132)
     m = torch.empty(n, dtype=torch.float32, device="cuda")
     v = torch.empty(n, dtype=torch.float32, device="cuda")
     draw_prior_moments_(m, v, 2e-3, 133)
-    out = torch.empty(n, dtype=torch.bfloat16, device="cuda")
-    wrap = (1 << 23) * 2 * 512  # first element past one round of the capped grid (an upper bound on the cap)
+    oraw = torch.empty(n + offset16, dtype=torch.bfloat16, device="cuda")
+    out = oraw[offset16:]
     rng = np.random.default_rng(134)
-    idx = np.concatenate([rng.integers(0, n, 65536), np.arange(0, 64), np.arange(n - 1100, n),
-                          np.arange(wrap - 8192 - 600, wrap - 8192 + 600), np.arange(wrap - 600, wrap + 600)])
+    idx = [rng.integers(0, n, 65536), np.arange(0, 64), np.arange(n - 1100, n)]
+    for wrap in (8_388_600 * 2 * 512, 16_777_208 * 2 * 256):
+        idx.append(np.arange(wrap - 600, min(n, wrap + 600)))
+    idx = np.concatenate(idx)
     idx = torch.from_numpy(np.unique(idx).astype(np.int64)).cuda()
     P0, M0, V0 = master[idx].cpu().numpy(), m[idx].cpu().numpy(), v[idx].cpu().numpy()
     g_idx = _h16(grads[idx])
