@@ -557,3 +557,40 @@ def test_adam_step_beyond_the_grid_cap(offset16):
     _compare_samples("beyond the grid cap", idx, master, m, v, out, want)
     s = st.read_state()
     assert s.t == 2 and s.last_skip == 0
+
+
+def test_accumulate_beyond_the_grid_cap():
+    """One bf16 tensor of 2^33 + 1003 elements into an fp32 buffer, overwrite
+    then accumulate with the overflow/norm pass fused in. The fp32 modes take
+    1024 elements per block, so past 8,388,607 blocks (8,589,933,568 elements)
+    blocks loop. Sampled elements (random, both ends, around the first unit of
+    the second round) bit-exact; the fused sum of squares against a float64
+    sum on the device."""
+    from workloads.device import fill_normal_
+    n = (1 << 33) + 1003
+    say("accumulate beyond the grid cap: n =", n)
+    _, total = zds.zds_flat_layout([n], 64)
+    plan = zds.zds_plan_create([n], 64, 0, total)
+    assert plan.entries() == [(0, 0, n, 0)]
+    a = fill_normal_(torch.empty(n, dtype=torch.bfloat16, device="cuda"), 1e-3, 141)
+    b = fill_normal_(torch.empty(n, dtype=torch.bfloat16, device="cuda"), 1e-3, 142)
+    acc = torch.zeros(total, dtype=torch.float32, device="cuda")
+    zds.zds_grad_accumulate(plan, [a], acc, zds.ZDS_OVERWRITE)
+    st = ShardStep(total, zds.hparams(), zds.scaler_config(dynamic=False, static_scale=1.0), max_norm=1.0,
+                   accum_steps=2, t0=1, beta1_pow0=B1, beta2_pow0=B2)
+    st.accumulate_norm(plan, [b], acc, zds.ZDS_ACCUMULATE, zds.new_plan_workspace(plan))
+    ssum = _torch_sumsq(acc)
+    torch.cuda.synchronize()
+    wrap = 8_388_607 * 1024
+    rng = np.random.default_rng(143)
+    idx = np.unique(np.concatenate([rng.integers(0, n, 65536), np.arange(0, 64), np.arange(n - 2100, n),
+                                    np.arange(wrap - 1100, wrap + 1100)]))
+    ti = torch.from_numpy(idx.astype(np.int64)).cuda()
+    wa = (_h16(a[ti]).astype(np.uint32) << 16).view(np.float32)
+    wb = (_h16(b[ti]).astype(np.uint32) << 16).view(np.float32)
+    want = wa + wb  # one fp32 round-to-nearest add, as the oracle's accumulate
+    assert (acc[ti].cpu().numpy().view(np.uint32) == want.view(np.uint32)).all()
+    assert (acc[n:] == 0).all()
+    osc = _oracle_scalars(ssum, 1.0, 2, 1.0, 0)
+    _compare_scalars(st.read_scalars(), osc)
+    plan.close()

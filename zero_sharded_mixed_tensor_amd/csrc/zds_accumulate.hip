@@ -6,17 +6,20 @@
 // micro-batches in memory before a single update (same tutorial §2.3) are done
 // here in one launch over the plan's device-side tensor table.
 //
-// Work is cut into chunks of kAccumChunk elements that never straddle two
-// table entries; the plan's table maps every chunk to its entry, so a block
-// finds its piece with a few uniform (scalar) loads. Copy mode moves 8
-// elements per lane (16-byte accesses); the fp32 modes move quads (8-byte
-// 16-bit loads, 16-byte fp32 accesses), lane l on quad l of a wave's range so
-// each wave-level access is contiguous. Unaligned entries fall back to
-// element-wise moves. Bytes per element: copy 2+2, overwrite 2+4,
-// accumulate 2+4+4. A block takes a whole chunk in copy mode and half a
-// chunk in the fp32 modes, and issues all of its vector loads before its
-// first store, so the two dependent table lookups and the data latency are
-// paid once per block.
+// Work is cut into chunks of kAccumChunk (4096) elements that never straddle
+// two table entries; the plan's table maps every chunk to its entry, so a
+// block finds its piece with two rounds of uniform scalar loads. Copy mode
+// moves 8 elements per lane (16-byte accesses); the fp32 modes move quads
+// (8-byte 16-bit loads, 16-byte fp32 accesses), lane l on quad l of a wave's
+// range so each wave-level access is contiguous. Unaligned entries fall back
+// to element-wise moves. Bytes per element: copy 2+2, overwrite 2+4,
+// accumulate 2+4+4. A block takes a whole chunk in copy mode (2 accesses per
+// lane) and a quarter chunk in the fp32 modes (1 quad per lane), and issues
+// all of its vector loads before its first store. Measured on the 7B shard
+// against 8192-element chunks (whole / half): copy with the fused norm
+// 0.535 vs 0.543-0.564 ms, 16 accumulated micro-batches 20.5 vs 21.1-22.2 ms,
+// the whole 7B model's flatten 4.08-4.15 vs 4.36-4.45 ms. Small units pay
+// only because the lookups are scalar loads (see unit_piece).
 #include "zds_device.h"
 #include "zds_internal.h"
 
@@ -44,14 +47,11 @@ struct AccArgs {
   double *partials;  // NORM: one sum of squares per block
 };
 
-// Chunks a block takes per iteration: copy mode moves little per chunk, so a
-// block takes two and overlaps their table lookups and loads.
 // Work units per chunk: the fp32 modes move more bytes per element, so a
-// block takes half a chunk there and the whole chunk in copy mode; either way
-// a block issues all of its unit's vector loads before its first store and
-// pays the two dependent table lookups once.
+// block takes a quarter chunk there (one quad per lane) and the whole chunk
+// in copy mode.
 #ifndef ZDS_ACC_FP32_PARTS
-#define ZDS_ACC_FP32_PARTS 2
+#define ZDS_ACC_FP32_PARTS 4
 #endif
 template <int MODE>
 constexpr int parts_per_chunk() { return MODE == ZDS_COPY ? 1 : ZDS_ACC_FP32_PARTS; }
@@ -67,20 +67,30 @@ struct Piece {
   bool vec;
 };
 
+// The plan's table and the call's pointer slots are written before the
+// launch and never during it, so the kernel reads them through the constant
+// address space: the uniform lookups then compile to scalar loads. (As plain
+// global loads behind the previous unit's stores they became vector loads
+// queued with the data stream, which made small units slow.)
+typedef const __attribute__((address_space(4))) int64_t *ConstI64;
+typedef const __attribute__((address_space(4))) char *const __attribute__((address_space(4))) *ConstPtrs;
+
 // Unit u: part u % P of chunk u / P of its entry.
 template <int SD, int MODE>
 __device__ __forceinline__ Piece unit_piece(const AccArgs &a, int64_t u) {
   constexpr int P = parts_per_chunk<MODE>();
   constexpr int64_t span = kAccumChunk / P;
   const int32_t E = a.num_entries;
-  const int64_t *t = a.table;  // [start E][len E][dst E][chunk0 E+1][entry of each chunk]
+  // [start E][len E][dst E][chunk0 E+1][entry of each chunk]
+  const ConstI64 t = (ConstI64)a.table;  // address-space cast
+  const ConstPtrs ptrs = (ConstPtrs)a.ptrs;
   const int64_t c = u / P;
   const int64_t e = t[4 * E + 1 + c];
   const int64_t local = (c - t[3 * E + e]) * kAccumChunk + (u % P) * span;
   const int64_t rem = t[E + e] - local;
   Piece pc;
   pc.cnt = rem < 0 ? 0 : (rem < span ? rem : span);
-  pc.src = static_cast<const char *>(a.ptrs[e]) + (t[e] + local) * (SD == ZDS_FP32 ? 4 : 2);
+  pc.src = (const char *)ptrs[e] + (t[e] + local) * (SD == ZDS_FP32 ? 4 : 2);
   pc.d0 = t[2 * E + e] + local;
   if (MODE == ZDS_COPY)
     pc.vec = aligned(pc.src, 16) && aligned(static_cast<uint16_t *>(a.dst) + pc.d0, 16);
