@@ -217,7 +217,9 @@ zds_status zds_grad_accumulate_norm(zds_plan *plan, const void *const *src_ptrs,
                                     void *ws, size_t ws_bytes, void *stream);
 
 /* Row a2. Size in bytes of the workspace zds_overflow_and_norm needs for n
- * elements. */
+ * elements: one float64 partial sum per 2048 elements and the levels that
+ * fold them (about 8 bytes per 2048 elements; it stops growing where the
+ * first stage's grid reaches its cap, past 2^34 elements). */
 size_t zds_workspace_bytes(int64_t n);
 
 /* Row a2. Overflow flag and global L2 norm of n grads (device, dtype), and the

@@ -154,4 +154,9 @@ def test_argument_errors():
     with pytest.raises(zds.ZdsError):
         zds.zds_flat_layout([10, -1], 8)
     assert zds.lib.zds_workspace_bytes(0) >= 8
-    assert zds.lib.zds_workspace_bytes(1 << 33) == zds.lib.zds_workspace_bytes(1 << 34)
+    # one float64 partial per 2048-element unit (plus their fold levels), so
+    # about 0.4 % of the bytes of n fp32 grads, constant past the grid cap
+    for n in (1, 2047, 2048, 2049, 842301440, 1 << 33):
+        units = -(-n // 2048)
+        assert units * 8 <= zds.lib.zds_workspace_bytes(n) <= units * 8 * 1.001 + 64, n
+    assert zds.lib.zds_workspace_bytes(1 << 35) == zds.lib.zds_workspace_bytes(1 << 36)

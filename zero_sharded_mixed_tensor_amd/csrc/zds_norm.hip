@@ -10,9 +10,13 @@
 // convert and one fma(x, x, acc) == acc + x^2. The wave sum uses DPP
 // (quad_perm and row_ror) inside each 16-lane row and readlane across the four
 // rows; waves meet in LDS; one partial per block. Stage 2 is one block that
-// adds the partials in index order and derives the scalars. The grid is a
-// fixed function of n, so the summation order, and the result, are the same
-// on every call.
+// adds the partials in index order and derives the scalars. Each block of
+// stage 1 reads one contiguous unit of ZDS_NORM_UNIT_BYTES (every load of
+// a whole unit issued before the sums, a unit per block as long as the grid
+// allows), and its partial is that unit's sum in a fixed order, so the
+// summation order, and the result, are the same on every call. (A grid of at
+// most 2048 blocks striding over the array ran the 7B shard's bf16 grads at
+// 6.3 TB/s; strided streams lose on this memory system.)
 //
 // The overflow flag comes from the sum itself: a square of a finite 16-bit or
 // fp32 value is at most 2^256, so a sum of fewer than 2^63 of them stays far
@@ -25,8 +29,10 @@
 #ifndef ZDS_NORM_BLOCK
 #define ZDS_NORM_BLOCK 256
 #endif
-#ifndef ZDS_NORM_MAX_GRID
-#define ZDS_NORM_MAX_GRID 2048
+// Bytes per block in the vector paths: 2 accesses of 16 bytes per lane
+// (4096 16-bit or 2048 fp32 elements).
+#ifndef ZDS_NORM_UNIT_BYTES
+#define ZDS_NORM_UNIT_BYTES 8192
 #endif
 
 namespace zds {
@@ -39,44 +45,59 @@ __device__ __forceinline__ double sq_acc(float x, double acc) {
   return fma(d, d, acc);
 }
 
+// Loads UPT vector groups of a unit (lane-contiguous per access) and adds
+// their squares; FULL: the whole unit is in range, so no load is guarded.
+template <int D, int UPT, bool FULL>
+__device__ __forceinline__ void unit_sumsq(const void *x, int64_t base, int64_t groups, double &acc0, double &acc1) {
+  constexpr int PER = D == ZDS_FP32 ? 4 : 8;
+  float v[UPT][PER];
+#pragma unroll
+  for (int r = 0; r < UPT; ++r) {
+    const int64_t i = base + r * ZDS_NORM_BLOCK;
+    if (FULL || i < groups) {
+      if constexpr (D == ZDS_FP32) load_quad<D>(x, i, v[r]);
+      else load8<D>(x, i, v[r]);
+    } else {
+#pragma unroll
+      for (int j = 0; j < PER; ++j) v[r][j] = 0.0f;
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < UPT; ++r) {
+#pragma unroll
+    for (int j = 0; j < PER; j += 2) {
+      acc0 = sq_acc<D>(v[r][j], acc0);
+      acc1 = sq_acc<D>(v[r][j + 1], acc1);
+    }
+  }
+}
+
+template <int D>
+constexpr int64_t norm_unit() { return ZDS_NORM_UNIT_BYTES / (D == ZDS_FP32 ? 4 : 2); }
+
 template <int D, bool VEC>
 __global__ void __launch_bounds__(ZDS_NORM_BLOCK) norm_stage1(const void *x, int64_t n, double *partials) {
   double acc0 = 0.0, acc1 = 0.0;
-  const int64_t stride = static_cast<int64_t>(gridDim.x) * ZDS_NORM_BLOCK;
-  const int64_t tid = static_cast<int64_t>(blockIdx.x) * ZDS_NORM_BLOCK + threadIdx.x;
-  int64_t done = 0;
-  if constexpr (VEC && D == ZDS_FP32) {
-    // fp32: one 16-byte quad per lane, lane-contiguous
-    const int64_t quads = n >> 2;
-    for (int64_t i = tid; i < quads; i += stride) {
-      float v[4];
-      load_quad<D>(x, i, v);
-      acc0 = sq_acc<D>(v[0], acc0);
-      acc1 = sq_acc<D>(v[1], acc1);
-      acc0 = sq_acc<D>(v[2], acc0);
-      acc1 = sq_acc<D>(v[3], acc1);
+  if constexpr (VEC) {
+    // lane-contiguous 16-byte accesses: fp32 quads or 8 16-bit elements
+    constexpr int PER = D == ZDS_FP32 ? 4 : 8;
+    constexpr int UPT = static_cast<int>(norm_unit<D>() / PER / ZDS_NORM_BLOCK);
+    static_assert(UPT >= 1 && UPT * PER * ZDS_NORM_BLOCK == norm_unit<D>(), "a unit is whole accesses");
+    const int64_t groups = n / PER;
+    const int64_t units = (groups + UPT * ZDS_NORM_BLOCK - 1) / (UPT * ZDS_NORM_BLOCK);
+    for (int64_t u = blockIdx.x; u < units; u += gridDim.x) {  // uniform per block
+      const int64_t first = u * UPT * ZDS_NORM_BLOCK;
+      if (first + UPT * ZDS_NORM_BLOCK <= groups)
+        unit_sumsq<D, UPT, true>(x, first + threadIdx.x, groups, acc0, acc1);
+      else
+        unit_sumsq<D, UPT, false>(x, first + threadIdx.x, groups, acc0, acc1);
     }
-    done = quads << 2;
-    if (blockIdx.x == 0 && done + threadIdx.x < n) acc0 = sq_acc<D>(widen1<D>(x, done + threadIdx.x), acc0);
-  } else if constexpr (VEC) {
-    // 16-bit: 8 elements (16 bytes) per lane, lane-contiguous
-    const int64_t groups = n >> 3;
-    for (int64_t i = tid; i < groups; i += stride) {
-      float v[8];
-      load8<D>(x, i, v);
-      acc0 = sq_acc<D>(v[0], acc0);
-      acc1 = sq_acc<D>(v[1], acc1);
-      acc0 = sq_acc<D>(v[2], acc0);
-      acc1 = sq_acc<D>(v[3], acc1);
-      acc0 = sq_acc<D>(v[4], acc0);
-      acc1 = sq_acc<D>(v[5], acc1);
-      acc0 = sq_acc<D>(v[6], acc0);
-      acc1 = sq_acc<D>(v[7], acc1);
-    }
-    done = groups << 3;
+    const int64_t done = groups * PER;
     if (blockIdx.x == 0 && done + threadIdx.x < n) acc0 = sq_acc<D>(widen1<D>(x, done + threadIdx.x), acc0);
   } else {
-    for (int64_t e = tid; e < n; e += stride) acc0 = sq_acc<D>(widen1<D>(x, e), acc0);
+    const int64_t stride = static_cast<int64_t>(gridDim.x) * ZDS_NORM_BLOCK;
+    for (int64_t e = static_cast<int64_t>(blockIdx.x) * ZDS_NORM_BLOCK + threadIdx.x; e < n; e += stride)
+      acc0 = sq_acc<D>(widen1<D>(x, e), acc0);
   }
   const double b = block_sum<ZDS_NORM_BLOCK>(acc0 + acc1);
   if (threadIdx.x == 0) partials[blockIdx.x] = b;
@@ -96,31 +117,35 @@ __global__ void __launch_bounds__(ZDS_NORM_BLOCK) norm_stage2(const double *part
   }
 }
 
-int norm_grid(int64_t n) {
-  const int64_t per_block = static_cast<int64_t>(ZDS_NORM_BLOCK) * 8 * 4;
-  int64_t g = (n + per_block - 1) / per_block;
-  if (g > ZDS_NORM_MAX_GRID) g = ZDS_NORM_MAX_GRID;
+static int grid_for(int64_t n, int64_t unit) {
+  int64_t g = (n + unit - 1) / unit;
+  if (g > max_blocks(ZDS_NORM_BLOCK)) g = max_blocks(ZDS_NORM_BLOCK);
   if (g < 1) g = 1;
   return static_cast<int>(g);
 }
 
+// The most blocks (partials) stage 1 uses for n elements of any dtype.
+int norm_grid(int64_t n) { return grid_for(n, norm_unit<ZDS_FP32>()); }
+
 template <int D>
-static void launch_d(bool vec, int grid, hipStream_t s, const void *x, int64_t n, double *partials) {
+static int launch_d(bool vec, hipStream_t s, const void *x, int64_t n, double *partials) {
+  const int grid = grid_for(n, norm_unit<D>());
   if (vec)
     hipLaunchKernelGGL((norm_stage1<D, true>), dim3(grid), dim3(ZDS_NORM_BLOCK), 0, s, x, n, partials);
   else
     hipLaunchKernelGGL((norm_stage1<D, false>), dim3(grid), dim3(ZDS_NORM_BLOCK), 0, s, x, n, partials);
+  return grid;
 }
 
 zds_status launch_norm(const void *grads, zds_dtype dtype, int64_t n, int32_t accum_steps,
                        float max_norm, const zds_step_state *state, zds_step_scalars *out,
                        double *partials, hipStream_t stream) {
-  const int grid = norm_grid(n);
   const bool vec = aligned(grads, 16);
+  int grid;
   switch (dtype) {
-    case ZDS_FP16: launch_d<ZDS_FP16>(vec, grid, stream, grads, n, partials); break;
-    case ZDS_BF16: launch_d<ZDS_BF16>(vec, grid, stream, grads, n, partials); break;
-    default: launch_d<ZDS_FP32>(vec, grid, stream, grads, n, partials); break;
+    case ZDS_FP16: grid = launch_d<ZDS_FP16>(vec, stream, grads, n, partials); break;
+    case ZDS_BF16: grid = launch_d<ZDS_BF16>(vec, stream, grads, n, partials); break;
+    default: grid = launch_d<ZDS_FP32>(vec, stream, grads, n, partials); break;
   }
   zds_status st = check_launch("overflow_and_norm stage 1");
   if (st != ZDS_OK) return st;
