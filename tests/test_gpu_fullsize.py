@@ -594,3 +594,21 @@ def test_accumulate_beyond_the_grid_cap():
     osc = _oracle_scalars(ssum, 1.0, 2, 1.0, 0)
     _compare_scalars(st.read_scalars(), osc)
     plan.close()
+
+
+def test_norm_beyond_the_grid_cap():
+    """zds_overflow_and_norm over 2^34 + 1003 fp32 elements: the first stage
+    takes 2048 fp32 elements per block, so past 8,388,607 blocks they loop
+    over a second round of units; the sum of squares against a float64 sum on
+    the device, and the clip scalars against the oracle's from that sum."""
+    from workloads.device import fill_normal_
+    n = (1 << 34) + 1003
+    say("overflow/norm beyond the grid cap: n =", n)
+    x = fill_normal_(torch.empty(n, dtype=torch.float32, device="cuda"), 1e-3, 151)
+    st = ShardStep(n, zds.hparams(), zds.scaler_config(dynamic=False, static_scale=1.0), max_norm=1.0)
+    st.norm(x)
+    ssum = _torch_sumsq(x)
+    torch.cuda.synchronize()
+    osc = _oracle_scalars(ssum, 1.0, 1, 1.0, 0)
+    _compare_scalars(st.read_scalars(), osc)
+    assert osc["coef"] < 1.0
