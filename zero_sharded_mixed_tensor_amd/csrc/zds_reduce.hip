@@ -14,8 +14,8 @@
 // a tile of 512 elements; wave w loads peers w, w+4, w+8, w+12 (one
 // contiguous 1 KiB wave-wide access each) and a share of the destination
 // tile, the tiles meet in LDS where each thread sums 2 elements over the
-// peers in order, and waves 0 and 1 store the result. A block takes two
-// consecutive tiles per grid step.
+// peers in order, and waves 0 and 1 store the result. A block takes one
+// tile (blocks loop only past the grid cap).
 //
 // NORM (the step's overflow / norm pass fused in): each thread adds the
 // float64 square of every value it stores (the rounded value for a 16-bit
@@ -24,17 +24,18 @@
 #include "zds_device.h"
 #include "zds_internal.h"
 
-// Consecutive tiles a block takes per grid step (8 peers into fp32: 1 tile
-// 5,772 GB/s, 2 tiles 6,066, 4 tiles 6,039).
+// Consecutive tiles a block takes per grid step, without and with the norm
+// fused in. One: each block streams one tile and ends (8 peers into fp32,
+// library builds swapped between bench runs, three rounds on one box: 2.52
+// ms against 2.69-2.73 with 2 tiles; with the norm fused in 2.55-2.65 against
+// 2.73-2.82 with 2 tiles and 2.93-2.96 with 4). When each wave's peer loads
+// were still serialised by the compiler (below), 2 and 4 tiles per block had
+// measured best.
 #ifndef ZDS_REDUCE_TPB
-#define ZDS_REDUCE_TPB 2
+#define ZDS_REDUCE_TPB 1
 #endif
-// The same with the norm fused in: each block ends with a float64 block
-// reduction, so a block takes more tiles (8 peers into fp32 with the norm,
-// interleaved on one box: 2 tiles 2.945 ms, 4 tiles 2.856, 8 tiles 3.017;
-// the intake then a separate norm pass 3.255).
 #ifndef ZDS_REDUCE_NORM_TPB
-#define ZDS_REDUCE_NORM_TPB 4
+#define ZDS_REDUCE_NORM_TPB 1
 #endif
 
 namespace zds {
@@ -54,14 +55,15 @@ __device__ __forceinline__ float widen16(uint16_t h) {
 }
 
 // SD: peer dtype (16-bit). DD: destination dtype (fp32 or SD). ACC: add the
-// destination's previous value.
-template <int SD, int DD, bool ACC, bool NORM>
+// destination's previous value. S = ceil(npeers / 4): the peer slots of each
+// wave (wave w takes peers w, w + 4, ...).
+template <int SD, int DD, bool ACC, bool NORM, int S>
 __global__ void __launch_bounds__(256) reduce_peers_kernel(ReduceArgs a) {
   __shared__ u32x4 sx[kMaxPeers][64];     // peer tiles, 512 x 16-bit each
   __shared__ f32x4 sd[DD == ZDS_FP32 ? 128 : 1];  // fp32 destination tile
   __shared__ u32x4 sh[DD == ZDS_FP32 ? 1 : 64];   // 16-bit destination tile
   const int lane = threadIdx.x & 63;
-  const int w = threadIdx.x >> 6;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: peer pointers by scalar loads
   const int N = a.npeers;
   const int64_t g8 = a.n >> 3;  // whole groups of 8 elements
   const int64_t ntiles = (g8 + 63) >> 6;
@@ -71,11 +73,26 @@ __global__ void __launch_bounds__(256) reduce_peers_kernel(ReduceArgs a) {
   for (int64_t tile = it; tile < it + TPB && tile < ntiles; ++tile) {  // uniform per block
     const int64_t grp = tile * 64 + lane;  // this lane's 8-element group
     const bool gok = grp < g8;
-    u32x4 r[4];
+    u32x4 r[S];
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const int k = w + 4 * s;
-      if (k < N && gok) r[s] = ld_stream(static_cast<const u32x4 *>(a.peers[k]) + grp);
+    for (int s = 0; s < S; ++s) r[s] = u32x4{0u, 0u, 0u, 0u};
+    if (tile * 64 + 64 <= g8) {
+      // A whole tile: the wave's S loads issue back to back with no condition
+      // (a slot past the last peer reloads peer 0 and is never summed). With a
+      // per-lane guard around each, and the wave index taken as varying per
+      // lane (so each peer pointer was a vector load), the compiler waited for
+      // every load before issuing the next.
+#pragma unroll
+      for (int s = 0; s < S; ++s) {
+        const int k = w + 4 * s;
+        r[s] = ld_stream(static_cast<const u32x4 *>(a.peers[k < N ? k : 0]) + grp);
+      }
+    } else {
+#pragma unroll
+      for (int s = 0; s < S; ++s) {
+        const int k = w + 4 * s;
+        if (k < N && gok) r[s] = ld_stream(static_cast<const u32x4 *>(a.peers[k]) + grp);
+      }
     }
     // fp32 destination quads of the tile: q = tile*128 + {0..127}; waves 2, 3
     // load them when accumulating (quad j of the tile holds elements 4j..4j+3)
@@ -91,10 +108,7 @@ __global__ void __launch_bounds__(256) reduce_peers_kernel(ReduceArgs a) {
       }
     }
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const int k = w + 4 * s;
-      if (k < N && gok) sx[k][lane] = r[s];
-    }
+    for (int s = 0; s < S; ++s) sx[w + 4 * s][lane] = r[s];  // slots past the peers or the tile are never read
     if (ACC) {
       if (DD == ZDS_FP32) {
         if (w >= 2 && dqok) sd[(w & 1) * 64 + lane] = dr;
@@ -209,9 +223,14 @@ int64_t reduce_grid_max(int64_t n) {
 
 template <int SD, int DD, bool ACC, bool NORM>
 static void go(bool vec, int64_t g, hipStream_t s, const ReduceArgs &a) {
-  if (vec)
-    hipLaunchKernelGGL((reduce_peers_kernel<SD, DD, ACC, NORM>), dim3(static_cast<uint32_t>(g)), dim3(256), 0, s, a);
-  else
+  if (vec) {
+    switch ((a.npeers + 3) / 4) {
+      case 1: hipLaunchKernelGGL((reduce_peers_kernel<SD, DD, ACC, NORM, 1>), dim3(static_cast<uint32_t>(g)), dim3(256), 0, s, a); break;
+      case 2: hipLaunchKernelGGL((reduce_peers_kernel<SD, DD, ACC, NORM, 2>), dim3(static_cast<uint32_t>(g)), dim3(256), 0, s, a); break;
+      case 3: hipLaunchKernelGGL((reduce_peers_kernel<SD, DD, ACC, NORM, 3>), dim3(static_cast<uint32_t>(g)), dim3(256), 0, s, a); break;
+      default: hipLaunchKernelGGL((reduce_peers_kernel<SD, DD, ACC, NORM, 4>), dim3(static_cast<uint32_t>(g)), dim3(256), 0, s, a); break;
+    }
+  } else
     hipLaunchKernelGGL((reduce_peers_scalar<SD, DD, ACC, NORM>), dim3(static_cast<uint32_t>(g)), dim3(256), 0, s, a);
 }
 
