@@ -47,6 +47,12 @@ __device__ __forceinline__ double sq_acc(float x, double acc) {
 
 // Loads UPT vector groups of a unit (lane-contiguous per access) and adds
 // their squares; FULL: the whole unit is in range, so no load is guarded.
+// 16-bit grads: the loads issue back to back. fp32: each wave has one load
+// in flight at a time (an explicit wait after each but the last), which the
+// fp32 accumulator reads faster (C3's 842M-element accumulator, library
+// builds swapped between bench runs, three rounds: 0.477-0.478 ms against
+// 0.503-0.507 back to back; the 16-bit grads the other way round, 0.247-0.250
+// back to back against 0.266-0.268).
 template <int D, int UPT, bool FULL>
 __device__ __forceinline__ void unit_sumsq(const void *x, int64_t base, int64_t groups, double &acc0, double &acc1) {
   constexpr int PER = D == ZDS_FP32 ? 4 : 8;
@@ -61,6 +67,8 @@ __device__ __forceinline__ void unit_sumsq(const void *x, int64_t base, int64_t 
 #pragma unroll
       for (int j = 0; j < PER; ++j) v[r][j] = 0.0f;
     }
+    // vmcnt(0), expcnt and lgkmcnt left at their maxima (GFX9 encoding)
+    if (D == ZDS_FP32 && r + 1 < UPT) __builtin_amdgcn_s_waitcnt(0x0F70);
   }
 #pragma unroll
   for (int r = 0; r < UPT; ++r) {
