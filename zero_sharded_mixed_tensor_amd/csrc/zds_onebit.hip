@@ -84,6 +84,11 @@ __global__ void __launch_bounds__(B) onebit_encode_kernel(const float *__restric
         const f32x4 a = ld_stream(reinterpret_cast<const f32x4 *>(x + e0));
         c[r][0] = a.x; c[r][1] = a.y; c[r][2] = a.z; c[r][3] = a.w;
         if (EF) {
+          // With one quad per thread, the error quad is loaded only after the
+          // input quad has arrived: one load in flight per wave (chunk 2048,
+          // the 7B shard, library builds swapped between bench runs, three
+          // rounds: 1.558-1.562 ms against 1.618 back to back).
+          if (Q == 1) __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0); expcnt, lgkmcnt at their maxima
           const f32x4 b = ld_stream(reinterpret_cast<const f32x4 *>(err + e0));
           c[r][0] = c[r][0] + b.x; c[r][1] = c[r][1] + b.y; c[r][2] = c[r][2] + b.z; c[r][3] = c[r][3] + b.w;
         }
