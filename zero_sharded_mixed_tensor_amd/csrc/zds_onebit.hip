@@ -311,6 +311,11 @@ __global__ void __launch_bounds__(256) onebit_decode_kernel(DecodeArgs a) {
           o = f32x4{old.x + o.x, old.y + o.y, old.z + o.z, old.w + o.w};
         }
         st_stream(reinterpret_cast<f32x4 *>(a.dst + e0), o);
+        // one store in flight per wave: 8 peers on the 7B shard, library
+        // builds swapped between bench runs, three rounds: 0.709-0.714 ms
+        // against 0.762-0.768 with the 8 stores back to back (a wait after
+        // every second store: 0.736-0.739)
+        if (r < 7) __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0); expcnt, lgkmcnt at their maxima
       } else {
         for (int i = 0; i < 4 && e0 + i < a.n; ++i) a.dst[e0 + i] = ACC ? a.dst[e0 + i] + v[4 * r + i] : v[4 * r + i];
       }
