@@ -311,11 +311,17 @@ __global__ void __launch_bounds__(256) onebit_decode_kernel(DecodeArgs a) {
           o = f32x4{old.x + o.x, old.y + o.y, old.z + o.z, old.w + o.w};
         }
         st_stream(reinterpret_cast<f32x4 *>(a.dst + e0), o);
-        // one store in flight per wave: 8 peers on the 7B shard, library
-        // builds swapped between bench runs, three rounds: 0.709-0.714 ms
-        // against 0.762-0.768 with the 8 stores back to back (a wait after
-        // every second store: 0.736-0.739)
-        if (r < 7) __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0); expcnt, lgkmcnt at their maxima
+        // Up to 8 peers, one store in flight per wave. 7B shard, library
+        // builds swapped between runs: 8 peers 0.709-0.714 ms against
+        // 0.762-0.768 with the 8 stores back to back in the bench (a wait
+        // after every second store: 0.736-0.739); peer-count sweeps on three
+        // boxes: 3 / 5 / 8 peers 0.61-0.62 / 0.62 / 0.67-0.71 against
+        // 0.69-0.70 / 0.67-0.72 / 0.79 on two of them, while the third ran 3
+        // and 4 peers slower with the waits (0.75-0.77 against 0.68-0.71) and
+        // 8 peers faster. Past 8 peers, where each element also takes an add
+        // per extra peer, the waits cost more than they save (16 peers 1.08
+        // against 0.97 ms).
+        if (NP <= 8 && r < 7) __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0); expcnt, lgkmcnt at their maxima
       } else {
         for (int i = 0; i < 4 && e0 + i < a.n; ++i) a.dst[e0 + i] = ACC ? a.dst[e0 + i] + v[4 * r + i] : v[4 * r + i];
       }
@@ -399,6 +405,9 @@ __global__ void __launch_bounds__(256) onebit_decode_quarter_kernel(DecodeArgs a
           o = f32x4{old.x + o.x, old.y + o.y, old.z + o.z, old.w + o.w};
         }
         st_stream(reinterpret_cast<f32x4 *>(a.dst + e0), o);
+        // one store in flight per wave: 1 / 2 peers 0.506-0.515 / 0.510-0.517
+        // ms against 0.541 / 0.537-0.538 with the 2 stores back to back
+        if (q == 0) __builtin_amdgcn_s_waitcnt(0x0F70);
       } else {
         for (int i = 0; i < 4 && e0 + i < a.n; ++i) a.dst[e0 + i] = ACC ? a.dst[e0 + i] + v[4 * q + i] : v[4 * q + i];
       }
