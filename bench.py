@@ -566,7 +566,7 @@ def _copy_calibration():
 def main():
     args = _parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU only: this library has no multi-GPU path "
               "(the step shards by running this same kernel set on each rank's "
               "slice); run with --gpus 1.", file=sys.stderr)
         return 2
