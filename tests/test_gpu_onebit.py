@@ -139,11 +139,23 @@ def test_error_feedback_rounds():
     assert apart.sum() <= 2
 
 
-@pytest.mark.parametrize("peers", [1, 3, 8, 16])
+@pytest.mark.parametrize("peers", list(range(1, 17)))
 @pytest.mark.parametrize("mode", ["overwrite", "accumulate"])
 def test_decode_matches_oracle(peers, mode):
-    say("decode peers", peers, mode)
-    n, chunk = 3 * 2048 + 1001, 2048
+    """Every peer count is its own kernel instance (1-2: the quarter-unit
+    kernel; 3-8: the unit kernel with one store in flight per wave; 9-16: the
+    unit kernel with the peers past the table added per element)."""
+    _decode_case(peers, mode, 3 * 2048 + 1001, 2048)
+
+
+@pytest.mark.parametrize("peers", [2, 5, 8, 12])
+def test_decode_matches_oracle_1024_chunks(peers):
+    """1024-element chunks: a 2048-element unit spans two chunks (two tables)."""
+    _decode_case(peers, "accumulate", 5 * 2048 + 777, 1024)
+
+
+def _decode_case(peers, mode, n, chunk):
+    say("decode peers", peers, mode, "n", n, "chunk", chunk)
     payloads, dev_payloads = [], []
     for k in range(peers):
         x, e = _inputs(n, 100 + k)
