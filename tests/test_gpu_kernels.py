@@ -500,7 +500,7 @@ def test_accumulate_norm_fused_overflow(bad):
     assert s0.overflow == 0 and s0.sumsq == 0.0 and s0.grad_scale == 1.0
 
 
-@pytest.mark.parametrize("N", [1, 2, 3, 5, 8, 16])
+@pytest.mark.parametrize("N", [1, 2, 3, 5, 8, 11, 12, 16])
 @pytest.mark.parametrize("sdt,ddt", [("bf16", "fp32"), ("fp16", "fp32"), ("bf16", "bf16"), ("fp16", "fp16")])
 def test_reduce_peer_slices_parity(N, sdt, ddt):
     say("reduce peers N=%d %s -> %s" % (N, sdt, ddt))
@@ -524,7 +524,7 @@ def test_reduce_peer_slices_parity(N, sdt, ddt):
                 assert (got == want).all(), (n, acc)
 
 
-@pytest.mark.parametrize("N", [1, 3, 8, 16])
+@pytest.mark.parametrize("N", [1, 3, 8, 11, 16])
 @pytest.mark.parametrize("sdt,ddt", [("bf16", "fp32"), ("fp16", "fp32"), ("bf16", "bf16"), ("fp16", "fp16")])
 def test_reduce_peer_slices_norm_parity(N, sdt, ddt):
     """zds_reduce_peer_slices_norm: the stored values equal the oracle's
