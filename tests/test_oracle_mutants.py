@@ -25,7 +25,10 @@ MUTANTS = {
  "sumsq_abs": ("total += float(np.sum(xc * xc))", "total += float(np.sum(np.abs(xc)))"),
  "shard_off1": ("out.append((t, a - o, b - a, a - lo))", "out.append((t, a - o, b - a - (1 if b - a > 1 else 0), a - lo))"),
  "layout_noalign": ("pos = align_up(pos + n, align)", "pos = pos + n"),
- "acc_overwrite": ("acc[d:d + n] = acc[d:d + n] + x", "acc[d:d + n] = x"),
+ "flatten_copy_ignores_start": ("bucket[d:d + n] = srcs[t][s:s + n]", "bucket[d:d + n] = srcs[t][:n]"),
+ "flatten_acc_ignores_start": ("x = widen(srcs[t][s:s + n], src_dtype)", "x = widen(srcs[t][:n], src_dtype)"),
+ "flatten_dst_off1": ("bucket[d:d + n] = srcs[t][s:s + n]", "bucket[d + 1:d + 1 + n] = srcs[t][s:s + n]"),
+ "acc_overwrite":("acc[d:d + n] = acc[d:d + n] + x", "acc[d:d + n] = x"),
  "no_K": ("sk = float(scale) * float(accum_steps)", "sk = float(scale)"),
  "scale_not_halved": ("return replace(st, scale=max(st.scale / 2.0, st.min_scale),", "return replace(st, scale=max(st.scale, st.min_scale),"),
  "t_on_skip": ("return replace(st, hyst_left=st.hyst_left - 1, good_steps=0, last_skip=1)", "return replace(st, hyst_left=st.hyst_left - 1, good_steps=0, last_skip=1, t=st.t+1)"),

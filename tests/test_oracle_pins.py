@@ -358,6 +358,74 @@ def test_accumulate_identical_microbatches():
     assert (bucket[ent[1][3]:ent[1][3] + 1000] == src[1]).all()
 
 
+def _labelled_flat(numels, align, world, label):
+    """The flat buffer written out element by element from its definition:
+    tensor i starts at the next multiple of `align` after tensor i-1 ends, the
+    buffer is padded to a multiple of world * align; padding holds None."""
+    flat = []
+    for t, n in enumerate(numels):
+        while len(flat) % align:
+            flat.append(None)
+        flat.extend(label(t, i) for i in range(n))
+    while len(flat) % (world * align):
+        flat.append(None)
+    return flat
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_flatten_at_shard_edges_labelled(seed):
+    """Stage-1 slices cut tensors mid-way ([csdn] §2.4 each rank updates its own
+    part; §3.2 contiguous_gradients), so a rank's first and last entries start
+    or end inside a tensor. Every source element carries a label that names
+    its tensor and its index inside the tensor; each rank's flatten (copy,
+    overwrite and += modes) must put exactly the labels the definition of the
+    flat buffer puts at each of its positions, and leave padding alone."""
+    rng = np.random.default_rng(700 + seed)
+    for world in (2, 3, 8):
+        numels = [int(x) for x in rng.integers(1, 400, size=int(rng.integers(1, 9)))]
+        align = int(rng.choice([1, 8, 64]))
+        # copy mode moves bit patterns: any 16-bit label will do
+        lab16 = lambda t, i: (t * 40503 + i * 2654435761 + 17) & 0xFFFF  # noqa: E731
+        # fp32 modes: small integers, exact in fp16 and bf16 and in their sums
+        labint = {O.FP16: lambda t, i: (t * 7 + i) % 2039 - 1000,
+                  O.BF16: lambda t, i: (t * 7 + i) % 251 - 125}
+        srcs16 = [np.array([lab16(t, i) for i in range(n)], np.uint16) for t, n in enumerate(numels)]
+        flat16 = _labelled_flat(numels, align, world, lab16)
+        per = len(flat16) // world
+        for rank in range(world):
+            lo, hi = rank * per, (rank + 1) * per
+            ent = O.shard_entries(numels, align, lo, hi)
+            sentinel = 0xABCD
+            bucket = O.flatten_copy(srcs16, ent, np.full(hi - lo, sentinel, np.uint16))
+            want = [sentinel if x is None else x for x in flat16[lo:hi]]
+            assert bucket.tolist() == want, (world, rank)
+            for dt, lab in labint.items():
+                srcs = [np.array([lab(t, i) for i in range(n)], np.float32) for t, n in enumerate(numels)]
+                srcs = [O.narrow(s, dt) for s in srcs]
+                flat = _labelled_flat(numels, align, world, lab)[lo:hi]
+                init = rng.integers(-3000, 3000, size=hi - lo).astype(np.float32)
+                acc = O.flatten_accumulate(srcs, dt, ent, init.copy(), overwrite=True)
+                assert acc.tolist() == [float(i) if x is None else float(x) for x, i in zip(flat, init)]
+                acc = O.flatten_accumulate(srcs, dt, ent, init.copy(), overwrite=False)
+                assert acc.tolist() == [float(i) if x is None else float(i) + x for x, i in zip(flat, init)]
+
+
+def test_flatten_llama_rank7_starts_inside_gate28():
+    """The 7B shard of rank 7 of 8 starts 31,195,136 elements into the 28th
+    layer's gate projection; its first bucket element is that tensor's element
+    at that index (checked on a labelled stand-in of the tensor's tail)."""
+    numels = [n for _, n in llama_7b_tensors()]
+    _, total = O.flat_layout(numels, 64)
+    lo, hi = O.shard_range(total, 8, 7, 64)
+    ent = O.shard_entries(numels, 64, lo, hi)
+    t0, s0, n0, d0 = ent[0]
+    assert (s0, n0, d0) == (31_195_136, 13_893_632, 0)
+    srcs = {t0: np.arange(numels[t0], dtype=np.int64).astype(np.uint16)}
+    bucket = O.flatten_copy(srcs, [ent[0]], np.zeros(n0, np.uint16))
+    assert bucket[0] == 31_195_136 & 0xFFFF and bucket[-1] == (31_195_136 + n0 - 1) & 0xFFFF
+    assert (np.diff(bucket.astype(np.int64)) % 65536 == 1).all()
+
+
 def test_accumulated_step_equals_single_step():
     """K identical micro-batches with the mean folded into grad_scale give the
     same update, bit for bit, as one micro-batch."""
