@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define ZDS_ABI_VERSION 2
+#define ZDS_ABI_VERSION 3
 
 typedef enum zds_status {
   ZDS_OK = 0,
@@ -58,12 +58,23 @@ typedef enum zds_status {
                      valid, intact checkpoint of this library */
 } zds_status;
 
-typedef enum zds_dtype { ZDS_FP16 = 0, ZDS_BF16 = 1, ZDS_FP32 = 2 } zds_dtype;
+/* The *_RANGE_ enumerators of the enums below are not valid arguments: they
+ * make every int32 value a value of the type, so that a call with any other
+ * integer is well defined and rejected with ZDS_EINVAL. */
+typedef enum zds_dtype {
+  ZDS_FP16 = 0,
+  ZDS_BF16 = 1,
+  ZDS_FP32 = 2,
+  ZDS_DTYPE_RANGE_MIN_ = -2147483647 - 1,
+  ZDS_DTYPE_RANGE_MAX_ = 2147483647
+} zds_dtype;
 
 typedef enum zds_accum_mode {
   ZDS_COPY = 0,       /* dst[j]  = src[j]          16-bit -> same 16-bit type */
   ZDS_OVERWRITE = 1,  /* dst[j]  = fp32(src[j])    first micro-batch          */
-  ZDS_ACCUMULATE = 2  /* dst[j] += fp32(src[j])    later micro-batches        */
+  ZDS_ACCUMULATE = 2, /* dst[j] += fp32(src[j])    later micro-batches        */
+  ZDS_ACCUM_MODE_RANGE_MIN_ = -2147483647 - 1,
+  ZDS_ACCUM_MODE_RANGE_MAX_ = 2147483647
 } zds_accum_mode;
 
 /* AdamW hyperparameters ([csdn] §3.2 optimizer block: lr, betas, eps,
@@ -119,13 +130,15 @@ typedef struct zds_step_scalars {
   float clip_coef;     /* max_norm / (norm + 1e-6) if norm > max_norm, else 1 */
   float grad_scale;    /* clip_coef / (S * K), the factor Adam applies      */
   float scale_used;    /* S read from the step state                        */
-  /* written by zds_adam_step: */
+  /* written by zds_adam_step: its step constants and the fp32 hyperparameters
+   * it applies (the update kernel reads all of its scalars from here) */
+  double inv_bc2_sqrt; /* 1 / bc2_sqrt in float64 (correctly rounded)       */
   float step_size;     /* lr / (1 - beta1^t)                                */
   float bc2_sqrt;      /* sqrt(1 - beta2^t)                                 */
   float decay;         /* 1 - lr * weight_decay                             */
-  float one_minus_beta1;
-  float one_minus_beta2;
-  uint32_t reserved[3];
+  float beta1;         /* the update forms 1 - beta1 and 1 - beta2 in fp32  */
+  float beta2;
+  float eps;
 } zds_step_scalars;
 
 /* ---------------------------------------------------------------------------
@@ -251,8 +264,12 @@ zds_status zds_overflow_and_norm(const void *grads, zds_dtype dtype, int64_t n,
  * once to fp32. If scalars_dev->overflow is set every element is left
  * untouched (the step is skipped on the device; no host sync).
  * The step constants are derived once per call by a single-wave kernel and
- * stored in scalars_dev (step_size .. one_minus_beta2); the update kernel
- * reads them from there.
+ * stored in scalars_dev (inv_bc2_sqrt .. eps); the update kernel reads them
+ * from there. The division sqrt(v)/sqrt(1-b2^t) is carried out
+ * as float64(sqrt(v)) * inv_bc2_sqrt rounded to fp32, which is the correctly
+ * rounded quotient for every input (the float64 product is within 2^-52 of
+ * it, relatively, and the quotient of two fp32 numbers is never that close
+ * to a point halfway between two fp32 numbers).
  *   grads       device, n elements of grad_dtype (16-bit, or the fp32 accumulator)
  *   master, exp_avg, exp_avg_sq   device fp32, n elements, updated in place
  *   params_out  device, n elements of param_dtype (FP16/BF16), write-only;
@@ -365,7 +382,8 @@ zds_status zds_cpu_adam_step(const zds_adamw_hparams *hp, const void *grads, zds
  * separate export step that resuming does not need ([algomooc] 训练与恢复边界
  * and the checkpoint paragraph of the spoken answer).
  * A rank's file holds its fp32 master / exp_avg / exp_avg_sq shard, its step
- * state, the tensor table and a 64-bit hash per section; a save goes to
+ * state, the tensor table, a 64-bit hash per section and one over the header
+ * (meta, step state, section hashes); a save goes to
  * "<path>.tmp" and is renamed over <path> only once complete. The save does
  * not fsync: the rename protects <path> against a crash of the process, not
  * of the machine (a load then finds a torn file by its hashes and fails with
@@ -373,10 +391,15 @@ zds_status zds_cpu_adam_step(const zds_adamw_hparams *hp, const void *grads, zds
  * file and its directory after the call.
  * ------------------------------------------------------------------------- */
 
-#define ZDS_CHECKPOINT_FORMAT 1
+#define ZDS_CHECKPOINT_FORMAT 2
 
 /* Where the arrays and the step state of a save / load live. */
-typedef enum zds_location { ZDS_ON_DEVICE = 0, ZDS_ON_HOST = 1 } zds_location;
+typedef enum zds_location {
+  ZDS_ON_DEVICE = 0,
+  ZDS_ON_HOST = 1,
+  ZDS_LOCATION_RANGE_MIN_ = -2147483647 - 1,
+  ZDS_LOCATION_RANGE_MAX_ = 2147483647
+} zds_location;
 
 /* The partition a shard belongs to. lo, hi and flat_total must be what
  * zds_flat_layout and zds_shard_range give for the tensor table, world,
@@ -419,8 +442,12 @@ zds_status zds_checkpoint_read_meta(const char *path, zds_checkpoint_meta *meta,
  * exp_avg_sq and the step state, in device or host memory as `loc` says. The
  * file's meta must equal *expect field by field and its tensor table must
  * equal numel (EINVAL otherwise: a different world size, rank, stage,
- * offload setting or model); every section is checked against its hash (EIO
- * on a mismatch; the arrays may then hold part of the file). Synchronous;
+ * offload setting or model); the header and every section are checked
+ * against their hashes (EIO on a mismatch). The arrays are filled piece by
+ * piece as the file is read and its hashes are only known at the end, so
+ * after EIO from a section hash they hold an undefined mix of their previous
+ * contents and the file's; the step state is written only after every check
+ * has passed. Synchronous;
  * the transfer runs on up to 8 host threads with their own pinned buffers
  * and streams. */
 zds_status zds_checkpoint_load(const char *path, const zds_checkpoint_meta *expect, const int64_t *numel,

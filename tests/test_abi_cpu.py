@@ -30,14 +30,15 @@ def test_exports_every_declared_function():
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(zds._SIGS), set(names) ^ set(zds._SIGS)
-    assert zds.zds_abi_version() == 2
+    assert zds.zds_abi_version() == 3
 
 
 def test_struct_layouts():
     assert ctypes.sizeof(zds.StepState) == 64
     assert zds.StepState.t.offset == 32 and zds.StepState.beta1_pow.offset == 40
     assert ctypes.sizeof(zds.StepScalars) == 64 and zds.StepScalars.sumsq.offset == 8
-    assert zds.StepScalars.step_size.offset == 32
+    assert zds.StepScalars.inv_bc2_sqrt.offset == 32 and zds.StepScalars.step_size.offset == 40
+    assert zds.StepScalars.eps.offset == 60
 
 
 @pytest.mark.parametrize("seed", range(20))
@@ -160,3 +161,34 @@ def test_argument_errors():
         units = -(-n // 2048)
         assert units * 8 <= zds.lib.zds_workspace_bytes(n) <= units * 8 * 1.001 + 64, n
     assert zds.lib.zds_workspace_bytes(1 << 35) == zds.lib.zds_workspace_bytes(1 << 36)
+
+
+def test_reciprocal_product_gives_the_correctly_rounded_quotient():
+    """The AdamW kernels divide sqrt(v) by the per-step fp32 constant
+    bc2 = sqrt(1 - beta2^t) as fp32(float64(a) * (1 / float64(bc2))); the
+    claim is that this is the IEEE fp32 quotient for every a. Checked here for
+    every fp32 significand in one binade and a million random a over all
+    exponents a square root can have, against numpy's IEEE fp32 division, for
+    bc2 of the first 8 steps of two beta2 values (the step constants the
+    library derives) and random values in (0, 1]."""
+    rng = np.random.default_rng(11)
+    bs = []
+    for b2 in (0.999, 0.95):
+        hp = zds.hparams(beta2=b2)
+        s = zds.zds_step_state_init_host(zds.scaler_config())
+        for _ in range(8):
+            bs.append(np.float32(zds.zds_adam_constants_host(hp, s)["bc2_sqrt"]))
+            zds.zds_loss_scaler_update_host(s, 0, hp)
+    bs += [np.float32(x) for x in rng.uniform(1e-3, 1.0, 8)]
+    binade = (np.arange(1 << 23, dtype=np.uint32) | np.uint32(0x3F800000)).view(np.float32)
+    # sqrt(v) of an fp32 v: 0 or at least 2^-74.5, below 2^64
+    rnd = np.sqrt(rng.uniform(0, 1, 1 << 20).astype(np.float32) *
+                  np.exp2(rng.integers(-149, 128, 1 << 20)).astype(np.float32)).astype(np.float32)
+    edge = np.array([0.0, np.sqrt(np.float32(1.4e-45)), 1.0, np.inf, np.nan], np.float32)
+    for b in bs:
+        r = 1.0 / np.float64(b)
+        for a in (binade, rnd, edge):
+            got = (a.astype(np.float64) * r).astype(np.float32)
+            want = a / b
+            assert np.array_equal(got.view(np.uint32), want.view(np.uint32)) or \
+                np.array_equal(got, want, equal_nan=True), float(b)

@@ -148,7 +148,8 @@ def _flip(path, offset):
         f.write(bytes([b[0] ^ 0x10]))
 
 
-@pytest.mark.parametrize("section", ["table", "master", "exp_avg", "exp_avg_sq", "magic", "format", "truncate"])
+@pytest.mark.parametrize("section", ["table", "master", "exp_avg", "exp_avg_sq", "magic", "format", "truncate",
+                                     "meta", "state_scale", "state_t", "length", "section_hash", "header_hash"])
 def test_corruption_is_detected(section, tmp_path):
     numels, align, world, st, ranks = _run(5, world=2)
     paths = _save_all(tmp_path, numels, st, ranks)
@@ -157,7 +158,11 @@ def test_corruption_is_detected(section, tmp_path):
     p = paths[0]
     where = {"table": 256 + 8 * (T // 2), "master": 256 + 8 * T + 4 * (n // 3),
              "exp_avg": 256 + 8 * T + 4 * n + 5, "exp_avg_sq": 256 + 8 * T + 8 * n + 4 * n - 1,
-             "magic": 3, "format": 8}
+             "magic": 3, "format": 8,
+             # header: meta at 16, step state at 64 (scale, then t at +32), n at 128, section
+             # hashes at 136, the header's own hash at 168
+             "meta": 16 + 4 * 3, "state_scale": 64 + 2, "state_t": 64 + 32, "length": 128 + 7,
+             "section_hash": 136 + 8 + 3, "header_hash": 168 + 5}
     if section == "truncate":
         with open(p, "r+b") as f:
             f.truncate(os.path.getsize(p) - 4)

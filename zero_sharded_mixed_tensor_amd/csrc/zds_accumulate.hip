@@ -23,20 +23,12 @@
 #include "zds_device.h"
 #include "zds_internal.h"
 
-#ifndef ZDS_ACC_BLOCK
-#define ZDS_ACC_BLOCK 256
-#endif
-#ifndef ZDS_ACC_WAVES_PER_CU
-#define ZDS_ACC_WAVES_PER_CU 32
-#endif
-// 1: one block per chunk; 0: at most ZDS_ACC_WAVES_PER_CU waves per CU
-// striding over the chunks.
-#ifndef ZDS_ACC_ONESHOT
-#define ZDS_ACC_ONESHOT 1
-#endif
-
-
 namespace zds {
+
+// Threads per block. The grid has one block per work unit (a resident-size
+// grid striding over the units measured slower), capped below 2^32
+// work-items per dispatch with a loop beyond.
+constexpr int kAccBlock = 256;
 
 struct AccArgs {
   const int64_t *table;
@@ -50,12 +42,10 @@ struct AccArgs {
 // Work units per chunk: the fp32 modes move more bytes per element, so a
 // block takes a quarter chunk there (one quad per lane) and the whole chunk
 // in copy mode.
-#ifndef ZDS_ACC_FP32_PARTS
-#define ZDS_ACC_FP32_PARTS 4
-#endif
+constexpr int kFp32Parts = 4;
 template <int MODE>
-constexpr int parts_per_chunk() { return MODE == ZDS_COPY ? 1 : ZDS_ACC_FP32_PARTS; }
-static_assert(kAccumChunk % (8 * ZDS_ACC_FP32_PARTS) == 0, "a unit holds whole vector accesses in every mode");
+constexpr int parts_per_chunk() { return MODE == ZDS_COPY ? 1 : kFp32Parts; }
+static_assert(kAccumChunk % (8 * kFp32Parts) == 0, "a unit holds whole vector accesses in every mode");
 
 // One work unit: where it reads and writes, and whether the vector path
 // applies (both ends 16-byte aligned, or 8-byte for 16-bit sources of the
@@ -103,10 +93,10 @@ __device__ __forceinline__ Piece unit_piece(const AccArgs &a, int64_t u) {
 // (SD -> fp32). Every vector load of a block iteration is issued before its
 // first store.
 template <int SD, int MODE, bool NORM>
-__global__ void __launch_bounds__(ZDS_ACC_BLOCK) accumulate_kernel(AccArgs a) {
+__global__ void __launch_bounds__(kAccBlock) accumulate_kernel(AccArgs a) {
   constexpr int P = parts_per_chunk<MODE>();
   constexpr int PER = MODE == ZDS_COPY ? 8 : 4;                                     // elements per access
-  constexpr int UPT = (kAccumChunk / P / PER + ZDS_ACC_BLOCK - 1) / ZDS_ACC_BLOCK;  // accesses per thread
+  constexpr int UPT = (kAccumChunk / P / PER + kAccBlock - 1) / kAccBlock;  // accesses per thread
   const int64_t units = a.total_chunks * P;
   double ss = 0.0;
   for (int64_t u = blockIdx.x; u < units; u += gridDim.x) {  // uniform per block
@@ -118,12 +108,12 @@ __global__ void __launch_bounds__(ZDS_ACC_BLOCK) accumulate_kernel(AccArgs a) {
       u32x4 w[UPT];
 #pragma unroll
       for (int r = 0; r < UPT; ++r) {
-        const int64_t i = threadIdx.x + r * ZDS_ACC_BLOCK;
+        const int64_t i = threadIdx.x + r * kAccBlock;
         if (i < groups) w[r] = ld_stream(s4 + i);
       }
 #pragma unroll
       for (int r = 0; r < UPT; ++r) {
-        const int64_t i = threadIdx.x + r * ZDS_ACC_BLOCK;
+        const int64_t i = threadIdx.x + r * kAccBlock;
         if (i < groups) {
           st_stream(d4 + i, w[r]);
           if (NORM) {
@@ -137,7 +127,7 @@ __global__ void __launch_bounds__(ZDS_ACC_BLOCK) accumulate_kernel(AccArgs a) {
       // the tail of a vector piece, or a whole unaligned one
       const uint16_t *s16 = reinterpret_cast<const uint16_t *>(pc.src);
       uint16_t *d16 = static_cast<uint16_t *>(a.dst) + pc.d0;
-      for (int64_t j = (groups << 3) + threadIdx.x; j < pc.cnt; j += ZDS_ACC_BLOCK) {
+      for (int64_t j = (groups << 3) + threadIdx.x; j < pc.cnt; j += kAccBlock) {
         d16[j] = s16[j];
         if (NORM) ss = sq_add(widen1<SD>(s16, j), ss);
       }
@@ -147,7 +137,7 @@ __global__ void __launch_bounds__(ZDS_ACC_BLOCK) accumulate_kernel(AccArgs a) {
       float x[UPT][4], y[UPT][4];
 #pragma unroll
       for (int r = 0; r < UPT; ++r) {
-        const int64_t q = threadIdx.x + r * ZDS_ACC_BLOCK;
+        const int64_t q = threadIdx.x + r * kAccBlock;
         if (q < quads) {
           load_quad<SD>(pc.src, q, x[r]);
           if (MODE == ZDS_ACCUMULATE) load_quad<ZDS_FP32>(d32, q, y[r]);
@@ -155,7 +145,7 @@ __global__ void __launch_bounds__(ZDS_ACC_BLOCK) accumulate_kernel(AccArgs a) {
       }
 #pragma unroll
       for (int r = 0; r < UPT; ++r) {
-        const int64_t q = threadIdx.x + r * ZDS_ACC_BLOCK;
+        const int64_t q = threadIdx.x + r * kAccBlock;
         if (q < quads) {
           if (MODE == ZDS_ACCUMULATE) {
 #pragma unroll
@@ -169,7 +159,7 @@ __global__ void __launch_bounds__(ZDS_ACC_BLOCK) accumulate_kernel(AccArgs a) {
         }
       }
       // the tail of a vector piece, or a whole unaligned one
-      for (int64_t j = (quads << 2) + threadIdx.x; j < pc.cnt; j += ZDS_ACC_BLOCK) {
+      for (int64_t j = (quads << 2) + threadIdx.x; j < pc.cnt; j += kAccBlock) {
         const float v = widen1<SD>(pc.src, j);
         const float r = MODE == ZDS_ACCUMULATE ? d32[j] + v : v;
         d32[j] = r;
@@ -178,22 +168,20 @@ __global__ void __launch_bounds__(ZDS_ACC_BLOCK) accumulate_kernel(AccArgs a) {
     }
   }
   if (NORM) {
-    const double b = block_sum<ZDS_ACC_BLOCK>(ss);
+    const double b = block_sum<kAccBlock>(ss);
     if (threadIdx.x == 0) a.partials[blockIdx.x] = b;
   }
 }
 
 template <int SD, int MODE, bool NORM>
 static void go(int64_t grid, hipStream_t s, const AccArgs &a) {
-  hipLaunchKernelGGL((accumulate_kernel<SD, MODE, NORM>), dim3(static_cast<uint32_t>(grid)), dim3(ZDS_ACC_BLOCK),
+  hipLaunchKernelGGL((accumulate_kernel<SD, MODE, NORM>), dim3(static_cast<uint32_t>(grid)), dim3(kAccBlock),
                      0, s, a);
 }
 
 int64_t accumulate_grid(int64_t total_chunks, zds_accum_mode mode) {
-  const int64_t iters = total_chunks * (mode == ZDS_COPY ? parts_per_chunk<ZDS_COPY>() : parts_per_chunk<ZDS_OVERWRITE>());
-  int64_t grid = static_cast<int64_t>(device_cu_count()) * ZDS_ACC_WAVES_PER_CU * 64 / ZDS_ACC_BLOCK;
-  if (ZDS_ACC_ONESHOT || grid > iters) grid = iters;
-  if (grid > max_blocks(ZDS_ACC_BLOCK)) grid = max_blocks(ZDS_ACC_BLOCK);
+  int64_t grid = total_chunks * (mode == ZDS_COPY ? parts_per_chunk<ZDS_COPY>() : parts_per_chunk<ZDS_OVERWRITE>());
+  if (grid > max_blocks(kAccBlock)) grid = max_blocks(kAccBlock);
   if (grid < 1) grid = 1;
   return grid;
 }

@@ -32,6 +32,7 @@
 #include <atomic>
 #include <cerrno>
 #include <cstdio>
+#include <cstddef>
 #include <cstring>
 #include <mutex>
 #include <string>
@@ -49,12 +50,10 @@ constexpr char kMagic[8] = {'Z', 'D', 'S', 'C', 'K', 'P', 'T', '1'};
 constexpr uint32_t kHeaderBytes = 256;
 constexpr size_t kPiece = size_t(32) << 20;  // bytes per hashed and transferred piece
 constexpr int kMaxWorkers = 8;
-// 1: a save writes through a shared mapping of the preallocated file; 0:
+// A save writes through a shared mapping of the preallocated file, not
 // through pwrite (a 10.1 GB rank file saved to /tmp: 7.3-9.8 GB/s mapped;
-// 10.7 GB/s for a first pwrite save, 3.4-4.6 for the next ones).
-#ifndef ZDS_CKPT_MMAP
-#define ZDS_CKPT_MMAP 1
-#endif
+// 10.7 GB/s for a first pwrite save, 3.4-4.6 for the next ones); it falls
+// back to pwrite where the file cannot be mapped.
 
 struct Header {
   char magic[8];
@@ -63,9 +62,11 @@ struct Header {
   zds_checkpoint_meta meta;
   zds_step_state state;
   int64_t n;
-  uint64_t hash[4];  // tensor table, master, exp_avg, exp_avg_sq
+  uint64_t hash[4];   // tensor table, master, exp_avg, exp_avg_sq
+  uint64_t head_hash; // every field above (the step state included)
 };
 static_assert(sizeof(Header) <= kHeaderBytes, "the header fits its slot");
+static_assert(offsetof(Header, head_hash) == 168, "no padding before the header's own hash");
 
 // 64-bit hash of a byte stream: four lanes over 8-byte words with
 // multiply-rotate mixing, folded at the end.
@@ -279,6 +280,8 @@ zds_status read_head(int fd, const char *path, Header *hd, std::vector<int64_t> 
   if (hd->format != ZDS_CHECKPOINT_FORMAT || hd->header_bytes != kHeaderBytes)
     return fail(ZDS_EIO, "%s: %s has format %u; this library reads format %d", fn, path, hd->format,
                 ZDS_CHECKPOINT_FORMAT);
+  if (hash_of(hd, offsetof(Header, head_hash)) != hd->head_hash)
+    return fail(ZDS_EIO, "%s: %s is corrupt (the header, step state included, does not match its hash)", fn, path);
   const int32_t T = hd->meta.num_tensors;
   if (T < 0 || T > (1 << 24)) return fail(ZDS_EIO, "%s: %s has a bad tensor count %d", fn, path, T);
   numel->assign(static_cast<size_t>(T), 0);
@@ -354,7 +357,7 @@ extern "C" zds_status zds_checkpoint_save(const char *path, const zds_checkpoint
     // reserve the blocks first, so a full disk is an error here and not a
     // fault in the mapping
     char *map = nullptr;
-    if (st == ZDS_OK && n > 0 && ZDS_CKPT_MMAP) {
+    if (st == ZDS_OK && n > 0) {
       const int rc = ::posix_fallocate(out.fd, 0, static_cast<off_t>(file_bytes));
       if (rc != 0) {
         st = fail(ZDS_EIO, "%s: cannot reserve %zu bytes for %s (%s)", fn, file_bytes, tmp.c_str(), std::strerror(rc));
@@ -369,6 +372,7 @@ extern "C" zds_status zds_checkpoint_save(const char *path, const zds_checkpoint
     if (map && ::munmap(map, file_bytes) != 0 && st == ZDS_OK) st = fail(ZDS_EIO, "%s: munmap failed", fn);
     if (st == ZDS_OK) {
       for (int k = 0; k < 3; ++k) hd.hash[k + 1] = fold(dig[k]);
+      hd.head_hash = hash_of(&hd, offsetof(Header, head_hash));
       unsigned char head[kHeaderBytes] = {};
       std::memcpy(head, &hd, sizeof hd);
       if (!pwrite_all(out.fd, head, kHeaderBytes, 0)) st = fail(ZDS_EIO, "%s: header write failed", fn);
@@ -404,8 +408,8 @@ extern "C" zds_status zds_checkpoint_read_meta(const char *path, zds_checkpoint_
   *meta = hd.meta;
   if (state) *state = hd.state;
   const int32_t T = hd.meta.num_tensors;
-  if (numel_out)
-    std::memcpy(numel_out, numel.data(), sizeof(int64_t) * static_cast<size_t>(T < max_tensors ? T : max_tensors));
+  const int32_t copy = T < max_tensors ? T : max_tensors;
+  if (numel_out && copy > 0) std::memcpy(numel_out, numel.data(), sizeof(int64_t) * static_cast<size_t>(copy));
   if (numel_out && T > max_tensors)
     return fail(ZDS_EINVAL, "%s: %s has %d tensors, room for %d", fn, path, T, max_tensors);
   return ZDS_OK;

@@ -63,56 +63,33 @@ __device__ __forceinline__ uint16_t narrow1(float a) {
   return static_cast<uint16_t>(pack2<D>(a, 0.0f) & 0xffffu);
 }
 
-// Streaming 16-byte loads and stores: every byte of the hot arrays is touched
-// once per call, so by default they carry the non-temporal hint.
-#ifndef ZDS_NT_LOADS
-#define ZDS_NT_LOADS 1
-#endif
-#ifndef ZDS_NT_STORES
-#define ZDS_NT_STORES 1
-#endif
+// Streaming loads and stores: every byte of the hot arrays is touched once
+// per call, so they carry the non-temporal hint. Loads are the compiler's
+// non-temporal loads ("nt"; the policies "sc1 nt" and "sc0 sc1 nt" measured
+// no different). The 16- and 8-byte stores use the cache policy
+// "sc0 sc1 nt" (system scope, written through), which has no builtin, so
+// they are one vector global store in inline assembly; other sizes use the
+// compiler's non-temporal store. A store of more than 8 bytes reads its data
+// registers one cycle late: a VALU write to them right after the store needs
+// one wait state in between, which the compiler's hazard pass does not insert
+// for a store inside inline assembly, so the 16-byte form carries its own
+// s_nop. Measured on the 7B shard, interleaved A/B, store policies "nt" /
+// "sc1 nt" / "sc0 sc1 nt": AdamW 6,282 / 6,297 / 6,301 GB/s, flatten + norm
+// 5,997 / 6,014 / 6,040 GB/s, a plain copy 6,524 / 6,627 / 6,631; plain
+// (write-back) stores: AdamW 5,517 GB/s against 6,215.
 template <typename T>
 __device__ __forceinline__ T ld_stream(const T *p) {
-#if ZDS_NT_LOADS
   return __builtin_nontemporal_load(p);
-#else
-  return *p;
-#endif
 }
-// Store cache policy of the streaming 16- and 8-byte stores: 0 = the
-// compiler's non-temporal store ("nt"); 1 = "sc1 nt"; 2 = "sc0 sc1 nt"
-// (system scope, written through). The scope bits have no builtin, so 1 and
-// 2 use a vector global store in inline assembly. A store of more than 8
-// bytes reads its data registers one cycle late: a VALU write to them right
-// after the store needs one wait state in between, which the compiler's
-// hazard pass does not insert for a store inside inline assembly, so the
-// 16-byte form carries its own s_nop. Measured on the 7B shard,
-// interleaved A/B: AdamW 6,282 / 6,297 / 6,301 GB/s, flatten + norm
-// 5,997 / 6,014 / 6,040 GB/s; a plain copy 6,524 / 6,627 / 6,631.
-#ifndef ZDS_ST_POLICY
-#define ZDS_ST_POLICY 2
-#endif
-#if ZDS_ST_POLICY == 1
-#define ZDS_ST_BITS "sc1 nt"
-#elif ZDS_ST_POLICY == 2
-#define ZDS_ST_BITS "sc0 sc1 nt"
-#endif
 template <typename T>
 __device__ __forceinline__ void st_stream(T *p, T v) {
-#if ZDS_ST_POLICY != 0
   if constexpr (sizeof(T) == 16) {
-    asm volatile("global_store_dwordx4 %0, %1, off " ZDS_ST_BITS "\n\ts_nop 0" : : "v"(p), "v"(v) : "memory");
-    return;
+    asm volatile("global_store_dwordx4 %0, %1, off sc0 sc1 nt\n\ts_nop 0" : : "v"(p), "v"(v) : "memory");
   } else if constexpr (sizeof(T) == 8) {
-    asm volatile("global_store_dwordx2 %0, %1, off " ZDS_ST_BITS : : "v"(p), "v"(v) : "memory");
-    return;
+    asm volatile("global_store_dwordx2 %0, %1, off sc0 sc1 nt" : : "v"(p), "v"(v) : "memory");
+  } else {
+    __builtin_nontemporal_store(v, p);
   }
-#endif
-#if ZDS_NT_STORES
-  __builtin_nontemporal_store(v, p);
-#else
-  *p = v;
-#endif
 }
 
 // 8 consecutive 16-bit elements (one 16-byte access) at group index `group`,

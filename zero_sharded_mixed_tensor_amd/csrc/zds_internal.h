@@ -88,9 +88,6 @@ constexpr int64_t max_blocks(int threads_per_block) {
 }
 
 // Chunk size (elements) of the accumulate kernel's work items.
-#ifndef ZDS_ACC_CHUNK
-#define ZDS_ACC_CHUNK 4096
-#endif
-constexpr int64_t kAccumChunk = ZDS_ACC_CHUNK;
+constexpr int64_t kAccumChunk = 4096;
 
 }  // namespace zds

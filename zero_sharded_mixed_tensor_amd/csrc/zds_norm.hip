@@ -11,7 +11,7 @@
 // (quad_perm and row_ror) inside each 16-lane row and readlane across the four
 // rows; waves meet in LDS; one partial per block. Stage 2 is one block that
 // adds the partials in index order and derives the scalars. Each block of
-// stage 1 reads one contiguous unit of ZDS_NORM_UNIT_BYTES (every load of
+// stage 1 reads one contiguous unit of kNormUnitBytes (every load of
 // a whole unit issued before the sums, a unit per block as long as the grid
 // allows), and its partial is that unit's sum in a fixed order, so the
 // summation order, and the result, are the same on every call. (A grid of at
@@ -26,18 +26,13 @@
 #include "zds_device.h"
 #include "zds_internal.h"
 
-#ifndef ZDS_NORM_BLOCK
-#define ZDS_NORM_BLOCK 256
-#endif
-// Bytes per block in the vector paths: 2 accesses of 16 bytes per lane
-// (4096 16-bit or 2048 fp32 elements).
-#ifndef ZDS_NORM_UNIT_BYTES
-#define ZDS_NORM_UNIT_BYTES 8192
-#endif
-
 namespace zds {
 
-static_assert(ZDS_NORM_BLOCK % 64 == 0, "block is whole waves");
+constexpr int kNormBlock = 256;
+// Bytes per block in the vector paths: 2 accesses of 16 bytes per lane
+// (4096 16-bit or 2048 fp32 elements).
+constexpr int64_t kNormUnitBytes = 8192;
+static_assert(kNormBlock % 64 == 0, "block is whole waves");
 
 template <int D>
 __device__ __forceinline__ double sq_acc(float x, double acc) {
@@ -59,7 +54,7 @@ __device__ __forceinline__ void unit_sumsq(const void *x, int64_t base, int64_t 
   float v[UPT][PER];
 #pragma unroll
   for (int r = 0; r < UPT; ++r) {
-    const int64_t i = base + r * ZDS_NORM_BLOCK;
+    const int64_t i = base + r * kNormBlock;
     if (FULL || i < groups) {
       if constexpr (D == ZDS_FP32) load_quad<D>(x, i, v[r]);
       else load8<D>(x, i, v[r]);
@@ -81,21 +76,21 @@ __device__ __forceinline__ void unit_sumsq(const void *x, int64_t base, int64_t 
 }
 
 template <int D>
-constexpr int64_t norm_unit() { return ZDS_NORM_UNIT_BYTES / (D == ZDS_FP32 ? 4 : 2); }
+constexpr int64_t norm_unit() { return kNormUnitBytes / (D == ZDS_FP32 ? 4 : 2); }
 
 template <int D, bool VEC>
-__global__ void __launch_bounds__(ZDS_NORM_BLOCK) norm_stage1(const void *x, int64_t n, double *partials) {
+__global__ void __launch_bounds__(kNormBlock) norm_stage1(const void *x, int64_t n, double *partials) {
   double acc0 = 0.0, acc1 = 0.0;
   if constexpr (VEC) {
     // lane-contiguous 16-byte accesses: fp32 quads or 8 16-bit elements
     constexpr int PER = D == ZDS_FP32 ? 4 : 8;
-    constexpr int UPT = static_cast<int>(norm_unit<D>() / PER / ZDS_NORM_BLOCK);
-    static_assert(UPT >= 1 && UPT * PER * ZDS_NORM_BLOCK == norm_unit<D>(), "a unit is whole accesses");
+    constexpr int UPT = static_cast<int>(norm_unit<D>() / PER / kNormBlock);
+    static_assert(UPT >= 1 && UPT * PER * kNormBlock == norm_unit<D>(), "a unit is whole accesses");
     const int64_t groups = n / PER;
-    const int64_t units = (groups + UPT * ZDS_NORM_BLOCK - 1) / (UPT * ZDS_NORM_BLOCK);
+    const int64_t units = (groups + UPT * kNormBlock - 1) / (UPT * kNormBlock);
     for (int64_t u = blockIdx.x; u < units; u += gridDim.x) {  // uniform per block
-      const int64_t first = u * UPT * ZDS_NORM_BLOCK;
-      if (first + UPT * ZDS_NORM_BLOCK <= groups)
+      const int64_t first = u * UPT * kNormBlock;
+      if (first + UPT * kNormBlock <= groups)
         unit_sumsq<D, UPT, true>(x, first + threadIdx.x, groups, acc0, acc1);
       else
         unit_sumsq<D, UPT, false>(x, first + threadIdx.x, groups, acc0, acc1);
@@ -103,21 +98,21 @@ __global__ void __launch_bounds__(ZDS_NORM_BLOCK) norm_stage1(const void *x, int
     const int64_t done = groups * PER;
     if (blockIdx.x == 0 && done + threadIdx.x < n) acc0 = sq_acc<D>(widen1<D>(x, done + threadIdx.x), acc0);
   } else {
-    const int64_t stride = static_cast<int64_t>(gridDim.x) * ZDS_NORM_BLOCK;
-    for (int64_t e = static_cast<int64_t>(blockIdx.x) * ZDS_NORM_BLOCK + threadIdx.x; e < n; e += stride)
+    const int64_t stride = static_cast<int64_t>(gridDim.x) * kNormBlock;
+    for (int64_t e = static_cast<int64_t>(blockIdx.x) * kNormBlock + threadIdx.x; e < n; e += stride)
       acc0 = sq_acc<D>(widen1<D>(x, e), acc0);
   }
-  const double b = block_sum<ZDS_NORM_BLOCK>(acc0 + acc1);
+  const double b = block_sum<kNormBlock>(acc0 + acc1);
   if (threadIdx.x == 0) partials[blockIdx.x] = b;
 }
 
-__global__ void __launch_bounds__(ZDS_NORM_BLOCK) norm_stage2(const double *partials, int64_t nparts,
+__global__ void __launch_bounds__(kNormBlock) norm_stage2(const double *partials, int64_t nparts,
                                                                const zds_step_state *state,
                                                                int32_t accum_steps, float max_norm,
                                                                zds_step_scalars *out) {
   double acc = 0.0;
-  for (int64_t i = threadIdx.x; i < nparts; i += ZDS_NORM_BLOCK) acc += partials[i];
-  const double total = block_sum<ZDS_NORM_BLOCK>(acc);
+  for (int64_t i = threadIdx.x; i < nparts; i += kNormBlock) acc += partials[i];
+  const double total = block_sum<kNormBlock>(acc);
   if (threadIdx.x == 0) {
     zds_step_scalars s = {};
     clip_scalars(total, state->scale, accum_steps, max_norm, s);
@@ -127,7 +122,7 @@ __global__ void __launch_bounds__(ZDS_NORM_BLOCK) norm_stage2(const double *part
 
 static int grid_for(int64_t n, int64_t unit) {
   int64_t g = (n + unit - 1) / unit;
-  if (g > max_blocks(ZDS_NORM_BLOCK)) g = max_blocks(ZDS_NORM_BLOCK);
+  if (g > max_blocks(kNormBlock)) g = max_blocks(kNormBlock);
   if (g < 1) g = 1;
   return static_cast<int>(g);
 }
@@ -139,9 +134,9 @@ template <int D>
 static int launch_d(bool vec, hipStream_t s, const void *x, int64_t n, double *partials) {
   const int grid = grid_for(n, norm_unit<D>());
   if (vec)
-    hipLaunchKernelGGL((norm_stage1<D, true>), dim3(grid), dim3(ZDS_NORM_BLOCK), 0, s, x, n, partials);
+    hipLaunchKernelGGL((norm_stage1<D, true>), dim3(grid), dim3(kNormBlock), 0, s, x, n, partials);
   else
-    hipLaunchKernelGGL((norm_stage1<D, false>), dim3(grid), dim3(ZDS_NORM_BLOCK), 0, s, x, n, partials);
+    hipLaunchKernelGGL((norm_stage1<D, false>), dim3(grid), dim3(kNormBlock), 0, s, x, n, partials);
   return grid;
 }
 
@@ -161,17 +156,17 @@ zds_status launch_norm(const void *grads, zds_dtype dtype, int64_t n, int32_t ac
 }
 
 // Block b adds partials [b*kReduceSpan, (b+1)*kReduceSpan) in a fixed order.
-constexpr int64_t kReduceSpan = 8 * ZDS_NORM_BLOCK;
+constexpr int64_t kReduceSpan = 8 * kNormBlock;
 
-__global__ void __launch_bounds__(ZDS_NORM_BLOCK) norm_reduce(const double *in, int64_t n, double *out) {
+__global__ void __launch_bounds__(kNormBlock) norm_reduce(const double *in, int64_t n, double *out) {
   const int64_t base = static_cast<int64_t>(blockIdx.x) * kReduceSpan;
   double acc = 0.0;
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
-    const int64_t i = base + k * ZDS_NORM_BLOCK + threadIdx.x;
+    const int64_t i = base + k * kNormBlock + threadIdx.x;
     if (i < n) acc += in[i];
   }
-  const double b = block_sum<ZDS_NORM_BLOCK>(acc);
+  const double b = block_sum<kNormBlock>(acc);
   if (threadIdx.x == 0) out[blockIdx.x] = b;
 }
 
@@ -193,7 +188,7 @@ zds_status launch_norm_stage2(double *partials, int64_t nparts, const zds_step_s
   int64_t k = nparts;
   while (k > kReduceSpan) {
     const int64_t blocks = (k + kReduceSpan - 1) / kReduceSpan;
-    hipLaunchKernelGGL(norm_reduce, dim3(static_cast<uint32_t>(blocks)), dim3(ZDS_NORM_BLOCK), 0, stream, p, k,
+    hipLaunchKernelGGL(norm_reduce, dim3(static_cast<uint32_t>(blocks)), dim3(kNormBlock), 0, stream, p, k,
                        next);
     zds_status st = check_launch("overflow_and_norm partial reduction");
     if (st != ZDS_OK) return st;
@@ -201,7 +196,7 @@ zds_status launch_norm_stage2(double *partials, int64_t nparts, const zds_step_s
     next += blocks;
     k = blocks;
   }
-  hipLaunchKernelGGL(norm_stage2, dim3(1), dim3(ZDS_NORM_BLOCK), 0, stream, p, k, state, accum_steps, max_norm,
+  hipLaunchKernelGGL(norm_stage2, dim3(1), dim3(kNormBlock), 0, stream, p, k, state, accum_steps, max_norm,
                      out);
   return check_launch("overflow_and_norm stage 2");
 }

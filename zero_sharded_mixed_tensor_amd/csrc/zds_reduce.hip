@@ -24,21 +24,16 @@
 #include "zds_device.h"
 #include "zds_internal.h"
 
-// Consecutive tiles a block takes per grid step, without and with the norm
+namespace zds {
+
+// Consecutive tiles a block takes per grid step, with or without the norm
 // fused in. One: each block streams one tile and ends (8 peers into fp32,
 // library builds swapped between bench runs, three rounds on one box: 2.52
 // ms against 2.69-2.73 with 2 tiles; with the norm fused in 2.55-2.65 against
 // 2.73-2.82 with 2 tiles and 2.93-2.96 with 4). When each wave's peer loads
 // were still serialised by the compiler (below), 2 and 4 tiles per block had
-// measured best.
-#ifndef ZDS_REDUCE_TPB
-#define ZDS_REDUCE_TPB 1
-#endif
-#ifndef ZDS_REDUCE_NORM_TPB
-#define ZDS_REDUCE_NORM_TPB 1
-#endif
-
-namespace zds {
+// measured best. Blocks loop only past the grid cap.
+constexpr int kReduceTilesPerBlock = 1;
 
 struct ReduceArgs {
   const void *peers[kMaxPeers];
@@ -67,7 +62,7 @@ __global__ void __launch_bounds__(256) reduce_peers_kernel(ReduceArgs a) {
   const int N = a.npeers;
   const int64_t g8 = a.n >> 3;  // whole groups of 8 elements
   const int64_t ntiles = (g8 + 63) >> 6;
-  constexpr int TPB = NORM ? ZDS_REDUCE_NORM_TPB : ZDS_REDUCE_TPB;
+  constexpr int TPB = kReduceTilesPerBlock;
   double ss = 0.0;
   for (int64_t it = static_cast<int64_t>(blockIdx.x) * TPB; it < ntiles; it += static_cast<int64_t>(gridDim.x) * TPB)
   for (int64_t tile = it; tile < it + TPB && tile < ntiles; ++tile) {  // uniform per block
@@ -203,7 +198,7 @@ __global__ void __launch_bounds__(256) reduce_peers_scalar(ReduceArgs a) {
 // writes).
 static int64_t reduce_grid(int64_t n, bool vec, bool norm) {
   if (vec) {
-    const int tpb = norm ? ZDS_REDUCE_NORM_TPB : ZDS_REDUCE_TPB;
+    const int tpb = kReduceTilesPerBlock;
     int64_t g = (((n >> 3) + 63) / 64 + tpb - 1) / tpb;
     if (g < 1) g = 1;
     if (g > max_blocks(256)) g = max_blocks(256);

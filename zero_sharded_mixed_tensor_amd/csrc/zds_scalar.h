@@ -30,6 +30,7 @@ ZDS_HD inline bool aligned(const void *p, uintptr_t a) { return (reinterpret_cas
 
 struct AdamConsts {
   float b1, b2, omb1, omb2, eps, step_size, bc2_sqrt, decay;
+  double inv_bc2_sqrt;  // 1 / bc2_sqrt in float64, correctly rounded
 };
 
 // The fp32 scalars of the step that raises t by one. The hyperparameters are
@@ -49,6 +50,7 @@ ZDS_HD inline AdamConsts adam_constants(const zds_adamw_hparams &hp, double b1po
   c.step_size = static_cast<float>(static_cast<double>(hp.lr) / (1.0 - p1));
   c.bc2_sqrt = static_cast<float>(sqrt(1.0 - p2));
   c.decay = static_cast<float>(1.0 - static_cast<double>(hp.lr) * static_cast<double>(hp.weight_decay));
+  c.inv_bc2_sqrt = 1.0 / static_cast<double>(c.bc2_sqrt);
   return c;
 }
 

@@ -14,7 +14,9 @@ import os
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libzds.so")
+# ZDS_LIBRARY selects another build of the library (the host-sanitizer
+# build, for the CPU tests run under AddressSanitizer).
+LIB_PATH = os.environ.get("ZDS_LIBRARY") or os.path.join(_HERE, "libzds.so")
 
 ZDS_OK, ZDS_EINVAL, ZDS_EALIGN, ZDS_ENOMEM, ZDS_EHIP, ZDS_EIO = 0, 1, 2, 3, 4, 5
 ZDS_FP16, ZDS_BF16, ZDS_FP32 = 0, 1, 2
@@ -56,10 +58,9 @@ class StepScalars(ctypes.Structure):
     _fields_ = [("overflow", ctypes.c_uint32), ("accum_steps", ctypes.c_int32),
                 ("sumsq", ctypes.c_double), ("norm", ctypes.c_float),
                 ("clip_coef", ctypes.c_float), ("grad_scale", ctypes.c_float),
-                ("scale_used", ctypes.c_float), ("step_size", ctypes.c_float),
-                ("bc2_sqrt", ctypes.c_float), ("decay", ctypes.c_float),
-                ("one_minus_beta1", ctypes.c_float), ("one_minus_beta2", ctypes.c_float),
-                ("reserved", ctypes.c_uint32 * 3)]
+                ("scale_used", ctypes.c_float), ("inv_bc2_sqrt", ctypes.c_double),
+                ("step_size", ctypes.c_float), ("bc2_sqrt", ctypes.c_float), ("decay", ctypes.c_float),
+                ("beta1", ctypes.c_float), ("beta2", ctypes.c_float), ("eps", ctypes.c_float)]
 
 
 class CheckpointMeta(ctypes.Structure):
