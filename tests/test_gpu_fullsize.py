@@ -5,16 +5,18 @@ that hold at any size.
 * Every table entry of the flat bucket is compared with its source tensor
   over its whole length on the device (the copy moves bits, so equality is
   exact).
-* Sampled elements (65,536 seeded positions plus the first and last element
-  of every table entry): the oracle recomputes the accumulated grad, the
-  AdamW update and the cast from the gathered pre-step inputs and its own
-  clip scalars; master/m/v within 2 ulp, 16-bit params within 1 ulp.
-* The norm: at the 7B Stage-1 shard the oracle sums x^2 over all 842M
-  elements on the host; at the whole-7B and 65B sizes (6.7B and 8.2B
-  elements) the sum is taken by torch in float64 on the device, chunk by
-  chunk, and the GPU's sum must agree within 1e-12 relative. Either way the
-  oracle derives the clip scalars itself and the GPU's grad_scale must equal
-  them.
+* Whole arrays at the Stage-1 shards (7B, 7B with 16 accumulated
+  micro-batches, 65B) and at the whole 7B model's last step: the oracle
+  recomputes every element of the accumulated grad (bit-exact), the AdamW
+  update and the cast from the pre-step state (device copies) and its own
+  clip scalars, on host threads chunk by chunk; master/m/v within 2 ulp,
+  16-bit params within 1 ulp. The next rows at full size use sampled
+  elements (65,536 seeded positions plus the first and last element of
+  every table entry).
+* The norm: the oracle's overflow flag and sum of squares over the whole
+  flat buffer, chunk by chunk on host threads; the GPU's sum must agree
+  within 1e-12 relative, the oracle derives the clip scalars itself and the
+  GPU's grad_scale must equal them.
 * Flags, skips and the loss-scale trajectory are compared exactly.
 The Stage-1 shards run the bench's step (the norm fused into the flatten or
 the last accumulate call); the whole-7B run uses the separate norm pass.
@@ -76,15 +78,6 @@ def _check_copy(bucket, srcs, ents):
         assert torch.equal(bucket[d:d + ln], srcs[t][s:s + ln]), "entry %d" % t
 
 
-def _torch_sumsq(x, chunk=1 << 27):
-    """float64 sum of squares on the device, chunk partials added in order."""
-    tot = 0.0
-    for a in range(0, x.numel(), chunk):
-        xc = x[a:a + chunk].double()
-        tot += float(torch.dot(xc, xc))
-    return tot
-
-
 def _setup_shard(tensors, world, rank, gdt, sigma, prior, seed):
     numels = [n for _, n in tensors]
     _, total = zds.zds_flat_layout(numels, 64)
@@ -121,6 +114,72 @@ def _compare_samples(tag, idx, master, m, v, out, want):
     assert_p16_close(tag + " params", _h16(out[idx]), oOUT, 1)
 
 
+CHUNK = 1 << 24
+POOL = 16
+
+
+def _host(t):
+    """Device tensor -> numpy (16-bit types as their bit patterns)."""
+    if t.dtype in (torch.float16, torch.bfloat16):
+        return _h16(t)
+    return t.cpu().numpy()
+
+
+def _bounded(ex, futs, fn, *args, limit=2 * POOL):
+    futs.append(ex.submit(fn, *args))
+    while len(futs) > limit:
+        futs.pop(0).result()
+
+
+def _oracle_flag_and_sumsq(x, dtype):
+    """The oracle's overflow flag and sum of squares of a whole device array,
+    taken chunk by chunk on the host (threads; numpy releases the GIL in its
+    array loops), the chunk sums added in chunk order."""
+    from concurrent.futures import ThreadPoolExecutor
+    n = x.numel()
+    with ThreadPoolExecutor(POOL) as ex:
+        futs = [ex.submit(lambda h: (O.overflow_flag(h, dtype), O.sum_of_squares(h, dtype)), _host(x[a:a + CHUNK]))
+                for a in range(0, n, CHUNK)]
+        parts = [f.result() for f in futs]
+    ovf = int(any(f for f, _ in parts))
+    total = 0.0
+    for _, t in parts:
+        total += t
+    return ovf, total
+
+
+def _cmp_chunk(tag, a, xh, gdt, gs, c, p0, m0, v0, pg, mg, vg, og, pdt):
+    p, m, v = O.adamw_update(xh, gdt, gs, p0, m0, v0, c)
+    assert_state_close("%s master [%d:]" % (tag, a), pg, p, 2)
+    assert_state_close("%s exp_avg [%d:]" % (tag, a), mg, m, 2)
+    assert_state_close("%s exp_avg_sq [%d:]" % (tag, a), vg, v, 2)
+    if og is not None:
+        assert_p16_close("%s params [%d:]" % (tag, a), og, O.narrow(p, pdt), 1)
+
+
+def _compare_whole(tag, x, gdt, osc, ost, pre, master, m, v, out, pdt):
+    """Every element of master / m / v / the 16-bit params against the
+    oracle's update of the pre-step state `pre` (device copies of master, m,
+    v) with the grads x and the oracle's grad factor, in CHUNK-element pieces
+    on host threads."""
+    from concurrent.futures import ThreadPoolExecutor
+    c = O.adamw_constants(O.AdamW(), ost.beta1_pow, ost.beta2_pow)
+    n = master.numel()
+    P0, M0, V0 = pre
+    futs = []
+    with ThreadPoolExecutor(POOL) as ex:
+        for k, a in enumerate(range(0, n, CHUNK)):
+            b = min(n, a + CHUNK)
+            args = (tag, a, _host(x[a:b]), gdt, osc["grad_scale"], c, P0[a:b].cpu().numpy(), M0[a:b].cpu().numpy(),
+                    V0[a:b].cpu().numpy(), master[a:b].cpu().numpy(), m[a:b].cpu().numpy(), v[a:b].cpu().numpy(),
+                    None if out is None else _h16(out[a:b]), pdt)
+            _bounded(ex, futs, _cmp_chunk, *args)
+            if k % 64 == 63:
+                say("  %s: %d of %d elements compared" % (tag, b, n))
+        for f in futs:
+            f.result()
+
+
 def _compare_scalars(sc, osc):
     assert sc.overflow == osc["overflow"]
     if osc["overflow"]:
@@ -139,7 +198,10 @@ def _oracle_scalars(sumsq, scale, k, max_norm, overflow):
 
 def test_llama7b_stage1_shard_bf16():
     """842,301,440-param Stage-1 shard (rank 0 of 8, 33 entries), bf16 grads
-    N(0, 2e-3), static scale 1, clip 1.0, prior moments, one step."""
+    N(0, 2e-3), static scale 1, clip 1.0, prior moments, one step. Every
+    element of the flat bucket, master, m, v and the bf16 params is checked:
+    the oracle's flag, sum and clip scalars over the whole bucket, then the
+    oracle's update of the whole pre-step state."""
     say("full size: Llama-7B Stage-1 shard, bf16")
     numels, plan, ents, n, srcs, master, m, v = _setup_shard(llama_7b_tensors(), 8, 0, "bf16", 2e-3, True, 21)
     draw_sources_(srcs, 2e-3, 1.0, 21, 0)
@@ -147,72 +209,79 @@ def test_llama7b_stage1_shard_bf16():
     out = torch.empty(n, dtype=torch.bfloat16, device="cuda")
     st = ShardStep(n, zds.hparams(), zds.scaler_config(dynamic=False, static_scale=1.0), max_norm=1.0,
                    t0=1, beta1_pow0=B1, beta2_pow0=B2)
-    idx = _sample_index(n, ents)
-    P0, M0, V0 = master[idx].cpu().numpy(), m[idx].cpu().numpy(), v[idx].cpu().numpy()
+    pre = (master.clone(), m.clone(), v.clone())
     # the bench's step: flatten with the norm fused in, then Adam and the scaler
     st.accumulate_norm(plan, srcs, bucket, zds.ZDS_COPY, zds.new_plan_workspace(plan))
     st.adam(bucket, master, m, v, out)
     st.scaler()
     torch.cuda.synchronize()
     _check_copy(bucket, srcs, ents)
-    g_host = _h16(bucket)
-    osum = O.sum_of_squares(g_host, "bf16")
+    ovf, osum = _oracle_flag_and_sumsq(bucket, "bf16")
     sc = st.read_scalars()
-    osc = _oracle_scalars(osum, 1.0, 1, 1.0, O.overflow_flag(g_host, "bf16"))
+    osc = _oracle_scalars(osum, 1.0, 1, 1.0, ovf)
     _compare_scalars(sc, osc)
     assert osc["coef"] < 1.0
     ost = O.scaler_init(dynamic=False, static_scale=1.0, t=1, beta1_pow=B1, beta2_pow=B2)
-    want = _oracle_update(g_host[idx.cpu().numpy()], "bf16", osc, ost, P0, M0, V0, "bf16")
-    _compare_samples("7B shard", idx, master, m, v, out, want)
+    _compare_whole("7B shard", bucket, "bf16", osc, ost, pre, master, m, v, out, "bf16")
     s = st.read_state()
     assert s.t == 2 and s.last_skip == 0
     plan.close()
 
 
+def _oracle_accumulate_whole(srcs, ents, acc_h, overwrite):
+    """The oracle's flatten into fp32 over the plan's entries, on host copies
+    of the sources, cut into CHUNK-element pieces of entries on threads (each
+    piece writes its own part of acc_h)."""
+    from concurrent.futures import ThreadPoolExecutor
+    host = {t: _h16(srcs[t][s:s + ln]) for t, s, ln, _ in ents}
+    pieces = []
+    for t, s, ln, d in ents:
+        for o in range(0, ln, CHUNK):
+            k = min(CHUNK, ln - o)
+            pieces.append([(t, o, k, d + o)])
+    with ThreadPoolExecutor(POOL) as ex:
+        for f in [ex.submit(O.flatten_accumulate, host, "fp16", pc, acc_h, overwrite) for pc in pieces]:
+            f.result()
+
+
 def test_llama7b_stage1_shard_accumulate16():
     """Same shard: 16 micro-batches of fp16 grads N(0, 1e-3) x 2^14
-    accumulated into fp32, overflow check, clip 1.0, AdamW, fp16 params."""
+    accumulated into fp32, overflow check, clip 1.0, AdamW, fp16 params.
+    Every element: the fp32 accumulator bit for bit against the oracle's
+    accumulation of all 16 micro-batches, the oracle's scalars over it, then
+    master, m, v and the fp16 params against the oracle's update."""
     say("full size: Llama-7B Stage-1 shard, 16 micro-batches")
     numels, plan, ents, n, srcs, master, m, v = _setup_shard(llama_7b_tensors(), 8, 0, "fp16", 1e-3, True, 31)
     acc = torch.empty(n, dtype=torch.float32, device="cuda")
     out = torch.empty(n, dtype=torch.float16, device="cuda")
     st = ShardStep(n, zds.hparams(), zds.scaler_config(initial_scale_power=14), max_norm=1.0, accum_steps=16,
                    t0=1, beta1_pow0=B1, beta2_pow0=B2)
-    idx = _sample_index(n, ents)
-    idx_h = idx.cpu().numpy()
-    P0, M0, V0 = master[idx].cpu().numpy(), m[idx].cpu().numpy(), v[idx].cpu().numpy()
-    # flat index -> (tensor, offset) for gathering the sampled sources
-    owner = np.empty(len(idx_h), np.int64)
-    off = np.empty(len(idx_h), np.int64)
-    for t, s, ln, d in ents:
-        sel = (idx_h >= d) & (idx_h < d + ln)
-        owner[sel] = t
-        off[sel] = idx_h[sel] - d + s
-    wacc = np.zeros(len(idx_h), np.float32)
+    pre = (master.clone(), m.clone(), v.clone())
+    # entries relative to each tensor's host copy of its entry range
+    host_ents = [(t, 0, ln, d) for t, s, ln, d in ents]
+    acc_h = np.full(n, np.float32(np.nan))
     for k in range(16):
         draw_sources_(srcs, 1e-3, 2.0 ** 14, 31, k)
-        xs = np.empty(len(idx_h), np.uint16)
-        for t in np.unique(owner):
-            sel = owner == t
-            xs[sel] = _h16(srcs[t][torch.from_numpy(off[sel]).cuda()])
-        wacc = wacc + O.widen(xs, "fp16") if k else O.widen(xs, "fp16").copy()
         if k < 15:
             zds.zds_grad_accumulate(plan, srcs, acc, zds.ZDS_OVERWRITE if k == 0 else zds.ZDS_ACCUMULATE)
         else:  # the last micro-batch with the norm fused in, as the bench runs it
             st.accumulate_norm(plan, srcs, acc, zds.ZDS_ACCUMULATE, zds.new_plan_workspace(plan))
+        view = {t: srcs[t][s:s + ln] for t, s, ln, _ in ents}
+        _oracle_accumulate_whole(view, host_ents, acc_h, overwrite=(k == 0))
+        say("  micro-batch %d accumulated" % k)
     torch.cuda.synchronize()
-    assert (acc[idx].cpu().numpy().view(np.uint32) == wacc.view(np.uint32)).all()
+    for a in range(0, n, CHUNK):
+        got = acc[a:a + CHUNK].cpu().numpy()
+        assert (got.view(np.uint32) == acc_h[a:a + CHUNK].view(np.uint32)).all(), a
     st.adam(acc, master, m, v, out)
     st.scaler()
     torch.cuda.synchronize()
-    acc_h = acc.cpu().numpy()
-    osc = _oracle_scalars(O.sum_of_squares(acc_h, "fp32"), 2.0 ** 14, 16, 1.0, O.overflow_flag(acc_h, "fp32"))
-    del acc_h
+    ovf, osum = _oracle_flag_and_sumsq(acc, "fp32")
+    osc = _oracle_scalars(osum, 2.0 ** 14, 16, 1.0, ovf)
     _compare_scalars(st.read_scalars(), osc)
     assert osc["coef"] < 1.0
     ost = O.scaler_init(initial_scale_power=14, t=1, beta1_pow=B1, beta2_pow=B2)
-    want = _oracle_update(wacc, "fp32", osc, ost, P0, M0, V0, "fp16")
-    _compare_samples("7B accum16", idx, master, m, v, out, want)
+    _compare_whole("7B accum16", acc, "fp32", osc, ost, pre, master, m, v, out, "fp16")
     plan.close()
 
 
@@ -220,7 +289,10 @@ def test_llama7b_whole_1024_tensors_twenty_steps():
     """All 6,738,411,520 params as 1,024 tensors, fp16 grads N(0, 1e-3) x S,
     copied into a flat bucket each step; 20 steps, dynamic scale from 2^16,
     window 1000; overflow schedule: Bernoulli(0.001) per step plus one forced
-    overflow at a seeded step in [2, 19], inf and NaN alternately."""
+    overflow at a seeded step in [2, 19], inf and NaN alternately. Every
+    step: the oracle's flag and sum of squares over the whole bucket, the
+    scale trajectory, and sampled state against the free-running oracle; the
+    last step: every element against the oracle's update."""
     say("full size: whole Llama-7B, 1024 tensors, 20 steps")
     tensors = llama_7b_split_1024()
     numels, plan, ents, n, srcs, master, m, v = _setup_shard(tensors, 1, 0, "fp16", 1e-3, False, 41)
@@ -244,10 +316,10 @@ def test_llama7b_whole_1024_tensors_twenty_steps():
             srcs[t][int(sched.integers(0, numels[t]))] = float("inf") if nov % 2 == 0 else float("nan")
             nov += 1
         zds.zds_grad_accumulate(plan, srcs, bucket, zds.ZDS_COPY)
+        pre = (master.clone(), m.clone(), v.clone()) if k == 20 else None
         st.step(bucket, master, m, v, out)
         g = _h16(bucket[idx])
-        ovf = int(not bool(torch.isfinite(bucket).all()))
-        ssum = _torch_sumsq(bucket)
+        ovf, ssum = _oracle_flag_and_sumsq(bucket, "fp16")
         osc = _oracle_scalars(ssum, ost.scale, 1, 1.0, ovf)
         torch.cuda.synchronize()
         if k in (1, 2, forced, 20):
@@ -258,6 +330,12 @@ def test_llama7b_whole_1024_tensors_twenty_steps():
             assert abs(sc.sumsq - ssum) <= 1e-12 * ssum
             assert sc.grad_scale == osc["grad_scale"]
             oP, oM, oV, oOUT = _oracle_update(g, "fp16", osc, ost, oP, oM, oV, "fp16")
+        if pre is not None:
+            # the last step over every element: the oracle's update of the
+            # whole pre-step state (teacher-forced; the samples run free)
+            assert not ovf
+            _compare_whole("whole 7B step 20", bucket, "fp16", osc, ost, pre, master, m, v, out, "fp16")
+            del pre
         ost = O.scaler_update(ost, ovf, 0.9, 0.999)
         s = st.read_state()
         assert (s.scale, s.t, s.last_skip) == (np.float32(ost.scale), ost.t, ost.last_skip), k
@@ -274,7 +352,10 @@ def test_llama7b_whole_1024_tensors_twenty_steps():
 
 def test_llama65b_stage1_shard_bf16():
     """8,160,706,560-param Stage-1 shard of the 65B shape (rank 0 of 8, 88
-    entries), bf16 grads N(0, 1e-3), static scale 1, clip 1.0, prior moments."""
+    entries), bf16 grads N(0, 1e-3), static scale 1, clip 1.0, prior moments.
+    Every element: the oracle's flag, sum and clip scalars over the whole
+    bucket, then master, m, v and the bf16 params against the oracle's
+    update of the pre-step state."""
     say("full size: 65B Stage-1 shard, bf16")
     numels, plan, ents, n, srcs, master, m, v = _setup_shard(llama_65b_tensors(), 8, 0, "bf16", 1e-3, True, 51)
     assert len(ents) == 88 and n == 8_160_706_560
@@ -283,20 +364,21 @@ def test_llama65b_stage1_shard_bf16():
     out = torch.empty(n, dtype=torch.bfloat16, device="cuda")
     st = ShardStep(n, zds.hparams(), zds.scaler_config(dynamic=False, static_scale=1.0), max_norm=1.0,
                    t0=1, beta1_pow0=B1, beta2_pow0=B2)
-    idx = _sample_index(n, ents)
-    P0, M0, V0 = master[idx].cpu().numpy(), m[idx].cpu().numpy(), v[idx].cpu().numpy()
     st.accumulate_norm(plan, srcs, bucket, zds.ZDS_COPY, zds.new_plan_workspace(plan))
-    st.adam(bucket, master, m, v, out)
-    st.scaler()
-    ssum = _torch_sumsq(bucket)
     torch.cuda.synchronize()
     _check_copy(bucket, srcs, ents)
-    osc = _oracle_scalars(ssum, 1.0, 1, 1.0, 0)
+    del srcs  # room for the pre-step copies of the state
+    torch.cuda.empty_cache()
+    pre = (master.clone(), m.clone(), v.clone())
+    st.adam(bucket, master, m, v, out)
+    st.scaler()
+    torch.cuda.synchronize()
+    ovf, ssum = _oracle_flag_and_sumsq(bucket, "bf16")
+    osc = _oracle_scalars(ssum, 1.0, 1, 1.0, ovf)
     _compare_scalars(st.read_scalars(), osc)
     assert osc["coef"] < 1.0
     ost = O.scaler_init(dynamic=False, static_scale=1.0, t=1, beta1_pow=B1, beta2_pow=B2)
-    want = _oracle_update(_h16(bucket[idx]), "bf16", osc, ost, P0, M0, V0, "bf16")
-    _compare_samples("65B shard", idx, master, m, v, out, want)
+    _compare_whole("65B shard", bucket, "bf16", osc, ost, pre, master, m, v, out, "bf16")
     plan.close()
 
 
@@ -548,9 +630,9 @@ def test_adam_step_beyond_the_grid_cap(offset16):
     st = ShardStep(n, zds.hparams(), zds.scaler_config(dynamic=False, static_scale=1.0), max_norm=1.0,
                    t0=1, beta1_pow0=B1, beta2_pow0=B2)
     st.step(grads, master, m, v, out)
-    ssum = _torch_sumsq(grads)
     torch.cuda.synchronize()
-    osc = _oracle_scalars(ssum, 1.0, 1, 1.0, 0)
+    ovf, ssum = _oracle_flag_and_sumsq(grads, "bf16")
+    osc = _oracle_scalars(ssum, 1.0, 1, 1.0, ovf)
     _compare_scalars(st.read_scalars(), osc)
     ost = O.scaler_init(dynamic=False, static_scale=1.0, t=1, beta1_pow=B1, beta2_pow=B2)
     want = _oracle_update(g_idx, "bf16", osc, ost, P0, M0, V0, "bf16")
@@ -579,8 +661,9 @@ def test_accumulate_beyond_the_grid_cap():
     st = ShardStep(total, zds.hparams(), zds.scaler_config(dynamic=False, static_scale=1.0), max_norm=1.0,
                    accum_steps=2, t0=1, beta1_pow0=B1, beta2_pow0=B2)
     st.accumulate_norm(plan, [b], acc, zds.ZDS_ACCUMULATE, zds.new_plan_workspace(plan))
-    ssum = _torch_sumsq(acc)
     torch.cuda.synchronize()
+    ovf, ssum = _oracle_flag_and_sumsq(acc, "fp32")
+    assert ovf == 0
     wrap = 8_388_607 * 1024
     rng = np.random.default_rng(143)
     idx = np.unique(np.concatenate([rng.integers(0, n, 65536), np.arange(0, 64), np.arange(n - 2100, n),
@@ -607,8 +690,8 @@ def test_norm_beyond_the_grid_cap():
     x = fill_normal_(torch.empty(n, dtype=torch.float32, device="cuda"), 1e-3, 151)
     st = ShardStep(n, zds.hparams(), zds.scaler_config(dynamic=False, static_scale=1.0), max_norm=1.0)
     st.norm(x)
-    ssum = _torch_sumsq(x)
     torch.cuda.synchronize()
-    osc = _oracle_scalars(ssum, 1.0, 1, 1.0, 0)
+    ovf, ssum = _oracle_flag_and_sumsq(x, "fp32")
+    osc = _oracle_scalars(ssum, 1.0, 1, 1.0, ovf)
     _compare_scalars(st.read_scalars(), osc)
     assert osc["coef"] < 1.0
