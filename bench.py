@@ -49,8 +49,11 @@ def _parse():
     ap.add_argument("--unfused", action="store_true",
                     help="separate overflow/norm pass instead of the one fused into the last "
                          "flatten/accumulate call")
-    ap.add_argument("--cpu-sample", type=int, default=1 << 24, help="oracle sample size (params)")
-    ap.add_argument("--cpu-repeats", type=int, default=2, help="minimum oracle passes over the sample")
+    ap.add_argument("--cpu-sample", type=int, default=None,
+                    help="oracle sample size in params (default: the whole shard, at most 2^30)")
+    ap.add_argument("--cpu-repeats", type=int, default=2, help="oracle passes over the sample")
+    ap.add_argument("--cpu-procs", type=int, default=None,
+                    help="oracle host processes (default: the CPUs of the affinity mask)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run torch's device copy of a known size (1 GiB read + 1 GiB write) "
                          "5 times, to calibrate HBM byte counters")
@@ -257,7 +260,11 @@ def run_gpu(args, w):
         g_ms = (time.perf_counter() - t_g) / args.steps * 1e3
         graph = {"ms_per_step": round(g_ms, 4), "params_per_s": round(n / (g_ms * 1e-3), 1),
                  "vs_eager": round(ms_per_step / g_ms, 3)}
-    return dict(n=n, entries=len(ents), elapsed=elapsed, ms_per_step=ms_per_step, kernels=kern, fused=fused,
+    # params counted in params/s: the shard's elements that belong to a
+    # tensor (the flat layout's alignment padding is moved but not counted)
+    n_real = n if w["mode"] == "intake" else sum(e[2] for e in ents)
+    return dict(n=n, n_real=n_real, entries=len(ents), elapsed=elapsed, ms_per_step=ms_per_step, kernels=kern,
+                fused=fused,
                 graph=graph,
                 adam_gbs=achieved, step_gbs=step_bytes / (elapsed / args.steps) / 1e9,
                 step_bytes_per_param=bpp["accum_total"] + bpp["norm"] + bpp["adam"],
@@ -464,58 +471,125 @@ def run_checkpoint(args, w):
 
 # ------------------------------------------------------------------ CPU oracle part
 
-def run_cpu_baseline(w, sample, repeats, min_seconds=10.0):
-    """Time the oracle's step for the workload (the flatten copy, or the K
-    micro-batch accumulation, or the intake of the peers' slices; then
-    overflow + norm, AdamW + cast, scaler update) on the first `sample` params
-    of the same workload, at least `repeats` times and for at least
-    `min_seconds`, with inputs generated before timing. Single process:
-    NumPy's elementwise kernels use one thread."""
+def _oracle_worker(conn, w, n, c0, c1, chunk):
+    """One host process of the CPU baseline: generates its share of the
+    workload's inputs (chunks c0 .. c1-1 of `chunk` params; not timed), then
+    on each "go" runs the oracle's step on them in two phases, the global
+    norm being combined by the parent in between (the scalars of row a2 are
+    global over the shard)."""
     import numpy as np
     import oracle as O
     from workloads import draw_grads, draw_master, draw_prior_moments
 
-    n = sample
-    g = draw_grads(n, w["gdt"], w["sigma"], 1.0 if w["scale"] is None else 2.0 ** w["scale"], 1, 2, 0)
-    master = draw_master(n, 0.02, 1, 2)
-    if w["prior"]:
-        m, v = draw_prior_moments(n, w["sigma"], 1, 2)
-        st = O.scaler_init(dynamic=w["scale"] is not None, initial_scale_power=w["scale"] or 0,
-                           static_scale=1.0, t=1, beta1_pow=float(np.float32(0.9)),
-                           beta2_pow=float(np.float32(0.999)))
-    else:
-        m = np.zeros(n, np.float32)
-        v = np.zeros(n, np.float32)
-        st = O.scaler_init(dynamic=w["scale"] is not None, initial_scale_power=w["scale"] or 0,
-                           static_scale=1.0)
-    ent = [(0, 0, n, 0)]
-    bucket = np.zeros(n, np.uint16)
-    acc = np.zeros(n, np.float32)
     scale = 1.0 if w["scale"] is None else 2.0 ** w["scale"]
-    extra = []
-    if w["mode"] == "intake":
-        extra = [draw_grads(n, w["gdt"], w["sigma"], scale, 2 + k, 2, 0) for k in range(w["peers"] - 1)]
-    elif w["mode"] == "accumulate":
-        extra = [draw_grads(n, w["gdt"], w["sigma"], scale, 2 + k, 2, 0) for k in range(w["accum"] - 1)]
-    t0 = time.perf_counter()
-    done = 0
-    while done < repeats or time.perf_counter() - t0 < min_seconds:
-        if w["mode"] == "intake":
-            x = O.reduce_peer_slices([g] + extra, w["gdt"], None, "fp32", accumulate=False)
-            r = O.optimizer_step(x, "fp32", master, m, v, st, O.AdamW(), 1.0, w["accum"], w["pdt"])
-        elif w["mode"] == "accumulate":
-            for k, src in enumerate([g] + extra):
-                O.flatten_accumulate([src], w["gdt"], ent, acc, overwrite=(k == 0))
-            r = O.optimizer_step(acc, "fp32", master, m, v, st, O.AdamW(), 1.0, w["accum"], w["pdt"])
+    nsrc = w["peers"] if w["mode"] == "intake" else (w["accum"] if w["mode"] == "accumulate" else 1)
+    parts = []
+    for c in range(c0, c1):
+        a = c * chunk
+        ln = min(chunk, n - a)
+        g = [draw_grads(ln, w["gdt"], w["sigma"], scale, 1 + k, 2, 0, offset=a) for k in range(nsrc)]
+        master = draw_master(ln, 0.02, 1, 2, offset=a)
+        if w["prior"]:
+            m, v = draw_prior_moments(ln, w["sigma"], 1, 2, offset=a)
         else:
-            O.flatten_copy([g], ent, bucket)
-            r = O.optimizer_step(bucket, w["gdt"], master, m, v, st, O.AdamW(), 1.0, 1, w["pdt"])
-        assert r[3] is not None
-        done += 1
-    dt = time.perf_counter() - t0
+            m, v = np.zeros(ln, np.float32), np.zeros(ln, np.float32)
+        parts.append((ln, g, master, m, v))
+    conn.send("ready")
+    xdt = w["gdt"] if w["mode"] == "copy" else "fp32"
+    while conn.recv() == "go":
+        xs, sums, ovf = [], [], 0
+        for ln, g, _, _, _ in parts:
+            ent = [(0, 0, ln, 0)]
+            if w["mode"] == "intake":
+                x = O.reduce_peer_slices(g, w["gdt"], None, "fp32", accumulate=False)
+            elif w["mode"] == "accumulate":
+                x = np.empty(ln, np.float32)
+                for k, src in enumerate(g):
+                    O.flatten_accumulate([src], w["gdt"], ent, x, overwrite=(k == 0))
+            else:
+                x = O.flatten_copy(g, ent, np.empty(ln, np.uint16))
+            sums.append(O.sum_of_squares(x, xdt))
+            ovf |= O.overflow_flag(x, xdt)
+            xs.append(x)
+        conn.send((sums, ovf))
+        gs, consts = conn.recv()
+        if gs is not None:
+            for x, (_, _, master, m, v) in zip(xs, parts):
+                p, _, _ = O.adamw_update(x, xdt, gs, master, m, v, consts)
+                O.narrow(p, w["pdt"])
+        conn.send("done")
+
+
+def run_cpu_baseline(w, sample=None, repeats=2, procs=None, chunk=1 << 24):
+    """The oracle's whole step (the flatten copy, or the K micro-batch
+    accumulation, or the intake of the peers' slices; then overflow + norm,
+    AdamW + cast, scaler update) over `sample` params of the workload's shard
+    (default: the whole shard up to 2^30 params), in `chunk`-param pieces
+    spread over `procs` host processes (default: the CPUs of this process's
+    affinity mask). Inputs are generated before timing, each process its own
+    pieces; only the compute is timed (wall clock, `repeats` passes). Must
+    run before this process touches the GPU: the workers are forked."""
+    import multiprocessing as mp
+    import oracle as O
+
+    numels = [t for _, t in w["tensors"]]
+    _, total = O.flat_layout(numels, 64)
+    lo, hi = O.shard_range(total, w["world"], w["rank"], 64)
+    n = min(hi - lo, sample or (1 << 30))
+    nchunks = (n + chunk - 1) // chunk
+    procs = max(1, min(procs or len(os.sched_getaffinity(0)), nchunks))
+    ctx = mp.get_context("fork")
+    workers, conns = [], []
+    for i in range(procs):
+        c0, c1 = nchunks * i // procs, nchunks * (i + 1) // procs
+        a, b = ctx.Pipe()
+        pr = ctx.Process(target=_oracle_worker, args=(b, w, n, c0, c1, chunk), daemon=True)
+        pr.start()
+        workers.append(pr)
+        conns.append(a)
+    try:
+        for c in conns:
+            if c.recv() != "ready":
+                raise RuntimeError("oracle worker failed")
+        st = O.scaler_init(dynamic=w["scale"] is not None, initial_scale_power=w["scale"] or 0,
+                           static_scale=1.0, t=1 if w["prior"] else 0,
+                           beta1_pow=float(O.np.float32(0.9)) if w["prior"] else 1.0,
+                           beta2_pow=float(O.np.float32(0.999)) if w["prior"] else 1.0)
+        times = []
+        for _ in range(repeats):
+            t0 = time.perf_counter()
+            for c in conns:
+                c.send("go")
+            sumsq, ovf = 0.0, 0
+            for c in conns:                      # partials in chunk order
+                s, o = c.recv()
+                for x in s:
+                    sumsq += x
+                ovf |= o
+            if ovf:
+                gs, consts = None, None
+            else:
+                _, _, gs = O.clip_scalars(sumsq, st.scale, w["accum"], 1.0)
+                consts = O.adamw_constants(O.AdamW(), st.beta1_pow, st.beta2_pow)
+            for c in conns:
+                c.send((gs, consts))
+            for c in conns:
+                if c.recv() != "done":
+                    raise RuntimeError("oracle worker failed")
+            O.scaler_update(st, ovf, O.AdamW().beta1, O.AdamW().beta2)
+            times.append(time.perf_counter() - t0)
+        for c in conns:
+            c.send("stop")
+    finally:
+        for pr in workers:
+            pr.join(timeout=60)
+            if pr.is_alive():
+                pr.kill()
+    dt = sum(times)
     what = {"intake": "intake of %d peers' slices" % w.get("peers", 0),
             "accumulate": "accumulation of %d micro-batches" % w["accum"]}.get(w["mode"], "copy")
-    return dict(value=n * done / dt, seconds=dt, n=n, repeats=done, what=what)
+    return dict(value=n * repeats / dt, seconds=dt, n=n, shard=hi - lo, repeats=repeats, procs=procs,
+                chunk=chunk, what=what)
 
 
 def run_cpu_baseline_onebit(w, sample, repeats, min_seconds=10.0):
@@ -579,7 +653,7 @@ def main():
         if args.copy_calibration:
             out["copy_calibration"] = _copy_calibration()
         if not args.no_cpu_baseline:
-            c = run_cpu_baseline_onebit(w, min(args.cpu_sample, 1 << 18), args.cpu_repeats)
+            c = run_cpu_baseline_onebit(w, min(args.cpu_sample or (1 << 18), 1 << 18), args.cpu_repeats)
             out["cpu_baseline"] = {
                 "value": round(c["value"], 1), "unit": "elements/s", "cores": 1, "kind": "oracle",
                 "sample": "%d passes of the oracle's encode (with error feedback) and %d-peer decode over %d "
@@ -589,10 +663,14 @@ def main():
     if w.get("checkpoint"):
         print(json.dumps(run_checkpoint(args, w)), flush=True)
         return 0
+    # the CPU baseline first: its workers are forked, which must happen
+    # before this process initialises the GPU
+    cpu = None if args.no_cpu_baseline else run_cpu_baseline(w, args.cpu_sample, args.cpu_repeats,
+                                                             args.cpu_procs)
     r = run_gpu(args, w)
     out = {
         "metric": METRIC,
-        "value": round(r["n"] * args.steps / r["elapsed"], 1),
+        "value": round(r["n_real"] * args.steps / r["elapsed"], 1),
         "unit": "params/s",
         "n_gpus": 1,
         "steps": args.steps,
@@ -605,7 +683,8 @@ def main():
         "data": "synthetic",
         "config": {
             "workload": args.workload,
-            "params": r["n"],
+            "params": r["n_real"],
+            "elements": r["n"],
             "table_entries": r["entries"],
             "grad_dtype": w["gdt"],
             "param_dtype": w["pdt"],
@@ -633,16 +712,18 @@ def main():
     }
     if args.copy_calibration:
         out["copy_calibration"] = _copy_calibration()
-    if not args.no_cpu_baseline:
-        c = run_cpu_baseline(w, args.cpu_sample, args.cpu_repeats)
+    if cpu is not None:
         out["cpu_baseline"] = {
-            "value": round(c["value"], 1),
+            "value": round(cpu["value"], 1),
             "unit": "params/s",
-            "cores": 1,
+            "cores": cpu["procs"],
             "kind": "oracle",
-            "sample": "%d passes of one whole oracle step (%s, overflow+norm, AdamW, cast, scaler) "
-                      "over the first %d params of the same workload, %.1f s"
-                      % (c["repeats"], c["what"], c["n"], c["seconds"]),
+            "sample": "%d passes of one whole oracle step (%s, overflow+norm, AdamW, cast, scaler) over "
+                      "%s (%d params) in %d-param pieces on %d host processes, %.2f s of compute "
+                      "(inputs generated before timing)"
+                      % (cpu["repeats"], cpu["what"],
+                         "the whole shard" if cpu["n"] == cpu["shard"] else "the first %d params of the shard"
+                         % cpu["n"], cpu["n"], cpu["chunk"], cpu["procs"], cpu["seconds"]),
         }
     print(json.dumps(out), flush=True)
     return 0

@@ -113,7 +113,10 @@ def test_cpu_baselines_time_the_workloads_own_oracle_step(workload):
     if w.get("onebit"):
         c = bench.run_cpu_baseline_onebit(w, 4096, 1, min_seconds=0.0)
     else:
-        c = bench.run_cpu_baseline(w, 4096, 1, min_seconds=0.0)
+        # several processes over pieces with a ragged last one
+        c = bench.run_cpu_baseline(w, 4096 + 1000, 1, procs=3, chunk=1024)
         assert c["what"] == {"llama7b_s1": "copy", "llama7b_s1_accum16": "accumulation of 16 micro-batches",
                              "llama7b_s2_intake8": "intake of 8 peers' slices"}[workload]
+        assert c["procs"] == 3 and c["n"] == 5096 and c["shard"] == 842301440
+        c["n"] -= 1000
     assert c["repeats"] == 1 and c["n"] == 4096 and c["value"] > 0
