@@ -253,6 +253,23 @@ zds_status zds_overflow_and_norm(const void *grads, zds_dtype dtype, int64_t n,
                                  const zds_step_state *state_dev, zds_step_scalars *out_dev,
                                  void *ws, size_t ws_bytes, void *stream);
 
+/* Row a2 for callers that cannot allocate (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc): zds_overflow_and_norm
+ * with the same kernels and results, its partial sums kept in a fixed 4 MiB
+ * device array of the library instead of a caller workspace. The array
+ * exists once per GPU and stays allocated until the process ends; the first
+ * call on a device resolves its address there (no stream operation). Calls
+ * on one GPU share it, so calls that overlap in time on one GPU (different
+ * streams, or host threads) race and must not be issued; calls in order on
+ * one stream are safe (nothing needs clearing between calls: every partial
+ * is written before it is read). Arguments as for zds_overflow_and_norm
+ * without ws / ws_bytes; n may be at most 1,073,217,536 (the largest n whose
+ * partial sums fit the array; EINVAL beyond). Allocates nothing. */
+zds_status zds_overflow_and_norm_noalloc(const void *grads, zds_dtype dtype, int64_t n,
+                                         int32_t accum_steps, float max_norm,
+                                         const zds_step_state *state_dev, zds_step_scalars *out_dev,
+                                         void *stream);
+
 /* Row a4. Fused AdamW on the fp32 master shard with unscale/clip and the cast
  * back to 16 bits ([csdn] §2.2 and [aiqz] 混合精度: the update runs on the
  * fp32 master copy; [csdn] §3.2 AdamW; [aiqz] Python 演示: the moment

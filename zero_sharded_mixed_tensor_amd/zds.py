@@ -98,6 +98,7 @@ _SIGS = {
                                         _P, _P, _P, ctypes.c_size_t, _P]),
     "zds_overflow_and_norm": (_I32, [_P, _I32, _I64, _I32, ctypes.c_float, _P, _P, _P,
                                      ctypes.c_size_t, _P]),
+    "zds_overflow_and_norm_noalloc": (_I32, [_P, _I32, _I64, _I32, ctypes.c_float, _P, _P, _P]),
     "zds_adam_step": (_I32, [ctypes.POINTER(AdamWHparams), _P, _I32, _P, _P, _P, _P, _I32, _I64,
                              _P, _P, _P]),
     "zds_cpu_adam_step": (_I32, [ctypes.POINTER(AdamWHparams), _P, _I32, _P, _P, _P, _P, _I32, _I64,
@@ -405,6 +406,14 @@ def zds_overflow_and_norm(grads, accum_steps, max_norm, state, scalars, ws, stre
                                      max_norm, _dev_ptr(state, "state"), _dev_ptr(scalars, "scalars"),
                                      _dev_ptr(ws, "workspace"), ws.numel() * ws.element_size(),
                                      _stream(stream)))
+
+
+def zds_overflow_and_norm_noalloc(grads, accum_steps, max_norm, state, scalars, stream=None, n=None):
+    n = grads.numel() if n is None else n
+    _need(grads, n, "grads")
+    _check(lib.zds_overflow_and_norm_noalloc(_dev_ptr(grads, "grads"), dtype_code(grads), n, accum_steps,
+                                             max_norm, _dev_ptr(state, "state"), _dev_ptr(scalars, "scalars"),
+                                             _stream(stream)))
 
 
 def zds_adam_step(hp, grads, master, exp_avg, exp_avg_sq, params_out, scalars, state, stream=None,
