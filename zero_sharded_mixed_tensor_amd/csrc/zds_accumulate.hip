@@ -14,8 +14,9 @@
 // range so each wave-level access is contiguous. Unaligned entries fall back
 // to element-wise moves. Bytes per element: copy 2+2, overwrite 2+4,
 // accumulate 2+4+4. A block takes a whole chunk in copy mode (2 accesses per
-// lane) and a quarter chunk in the fp32 modes (1 quad per lane), and issues
-// all of its vector loads before its first store. Measured on the 7B shard
+// lane), half a chunk in overwrite mode (2 quads per lane) and a quarter
+// chunk in accumulate mode (1 quad per lane), and issues all of its vector
+// loads before its first store. Measured on the 7B shard
 // against 8192-element chunks (whole / half): copy with the fused norm
 // 0.535 vs 0.543-0.564 ms, 16 accumulated micro-batches 20.5 vs 21.1-22.2 ms,
 // the whole 7B model's flatten 4.08-4.15 vs 4.36-4.45 ms. Small units pay
@@ -25,9 +26,9 @@
 
 namespace zds {
 
-// Threads per block. The grid has one block per work unit (a resident-size
-// grid striding over the units measured slower), capped below 2^32
-// work-items per dispatch with a loop beyond.
+// Threads per block by mode. The grid has one block per work unit (a
+// resident-size grid striding over the units measured slower), capped below
+// 2^32 work-items per dispatch with a loop beyond.
 constexpr int kAccBlock = 256;
 
 struct AccArgs {
@@ -39,13 +40,20 @@ struct AccArgs {
   double *partials;  // NORM: one sum of squares per block
 };
 
-// Work units per chunk: the fp32 modes move more bytes per element, so a
-// block takes a quarter chunk there (one quad per lane) and the whole chunk
-// in copy mode.
-constexpr int kFp32Parts = 4;
+// Work units per chunk. Copy mode takes a whole chunk per block (2 accesses
+// of 8 elements per lane); accumulate a quarter chunk (one quad per lane: a
+// 16-bit load, an fp32 load and an fp32 store); overwrite half a chunk (two
+// quads per lane: its block moves only 6 B per element, and with a quarter
+// chunk the two rounds of table lookups at each block's start cost 15 %).
+// Measured on the 7B shard, fp16 sources, library builds swapped, two
+// rounds: overwrite 0.90 ms (5,610 GB/s) with a quarter chunk, 0.80 ms
+// (6,330 GB/s) with half a chunk, 0.84 with a whole chunk (4 quads per
+// lane), 0.90-0.93 with 512- or 1024-thread blocks at one quad per lane;
+// accumulate 1.30 ms (6,480 GB/s) with a quarter chunk against 1.37 / 1.44
+// with half / whole chunks.
 template <int MODE>
-constexpr int parts_per_chunk() { return MODE == ZDS_COPY ? 1 : kFp32Parts; }
-static_assert(kAccumChunk % (8 * kFp32Parts) == 0, "a unit holds whole vector accesses in every mode");
+constexpr int parts_per_chunk() { return MODE == ZDS_COPY ? 1 : (MODE == ZDS_OVERWRITE ? 2 : 4); }
+static_assert(kAccumChunk % (8 * 4) == 0, "a unit holds whole vector accesses in every mode");
 
 // One work unit: where it reads and writes, and whether the vector path
 // applies (both ends 16-byte aligned, or 8-byte for 16-bit sources of the
@@ -95,8 +103,9 @@ __device__ __forceinline__ Piece unit_piece(const AccArgs &a, int64_t u) {
 template <int SD, int MODE, bool NORM>
 __global__ void __launch_bounds__(kAccBlock) accumulate_kernel(AccArgs a) {
   constexpr int P = parts_per_chunk<MODE>();
-  constexpr int PER = MODE == ZDS_COPY ? 8 : 4;                                     // elements per access
-  constexpr int UPT = (kAccumChunk / P / PER + kAccBlock - 1) / kAccBlock;  // accesses per thread
+  constexpr int BLK = kAccBlock;
+  constexpr int PER = MODE == ZDS_COPY ? 8 : 4;                         // elements per access
+  constexpr int UPT = (kAccumChunk / P / PER + BLK - 1) / BLK;  // accesses per thread
   const int64_t units = a.total_chunks * P;
   double ss = 0.0;
   for (int64_t u = blockIdx.x; u < units; u += gridDim.x) {  // uniform per block
@@ -108,12 +117,12 @@ __global__ void __launch_bounds__(kAccBlock) accumulate_kernel(AccArgs a) {
       u32x4 w[UPT];
 #pragma unroll
       for (int r = 0; r < UPT; ++r) {
-        const int64_t i = threadIdx.x + r * kAccBlock;
+        const int64_t i = threadIdx.x + r * BLK;
         if (i < groups) w[r] = ld_stream(s4 + i);
       }
 #pragma unroll
       for (int r = 0; r < UPT; ++r) {
-        const int64_t i = threadIdx.x + r * kAccBlock;
+        const int64_t i = threadIdx.x + r * BLK;
         if (i < groups) {
           st_stream(d4 + i, w[r]);
           if (NORM) {
@@ -127,7 +136,7 @@ __global__ void __launch_bounds__(kAccBlock) accumulate_kernel(AccArgs a) {
       // the tail of a vector piece, or a whole unaligned one
       const uint16_t *s16 = reinterpret_cast<const uint16_t *>(pc.src);
       uint16_t *d16 = static_cast<uint16_t *>(a.dst) + pc.d0;
-      for (int64_t j = (groups << 3) + threadIdx.x; j < pc.cnt; j += kAccBlock) {
+      for (int64_t j = (groups << 3) + threadIdx.x; j < pc.cnt; j += BLK) {
         d16[j] = s16[j];
         if (NORM) ss = sq_add(widen1<SD>(s16, j), ss);
       }
@@ -137,7 +146,7 @@ __global__ void __launch_bounds__(kAccBlock) accumulate_kernel(AccArgs a) {
       float x[UPT][4], y[UPT][4];
 #pragma unroll
       for (int r = 0; r < UPT; ++r) {
-        const int64_t q = threadIdx.x + r * kAccBlock;
+        const int64_t q = threadIdx.x + r * BLK;
         if (q < quads) {
           load_quad<SD>(pc.src, q, x[r]);
           if (MODE == ZDS_ACCUMULATE) load_quad<ZDS_FP32>(d32, q, y[r]);
@@ -145,7 +154,7 @@ __global__ void __launch_bounds__(kAccBlock) accumulate_kernel(AccArgs a) {
       }
 #pragma unroll
       for (int r = 0; r < UPT; ++r) {
-        const int64_t q = threadIdx.x + r * kAccBlock;
+        const int64_t q = threadIdx.x + r * BLK;
         if (q < quads) {
           if (MODE == ZDS_ACCUMULATE) {
 #pragma unroll
@@ -159,7 +168,7 @@ __global__ void __launch_bounds__(kAccBlock) accumulate_kernel(AccArgs a) {
         }
       }
       // the tail of a vector piece, or a whole unaligned one
-      for (int64_t j = (quads << 2) + threadIdx.x; j < pc.cnt; j += kAccBlock) {
+      for (int64_t j = (quads << 2) + threadIdx.x; j < pc.cnt; j += BLK) {
         const float v = widen1<SD>(pc.src, j);
         const float r = MODE == ZDS_ACCUMULATE ? d32[j] + v : v;
         d32[j] = r;
@@ -168,7 +177,7 @@ __global__ void __launch_bounds__(kAccBlock) accumulate_kernel(AccArgs a) {
     }
   }
   if (NORM) {
-    const double b = block_sum<kAccBlock>(ss);
+    const double b = block_sum<BLK>(ss);
     if (threadIdx.x == 0) a.partials[blockIdx.x] = b;
   }
 }
@@ -180,7 +189,10 @@ static void go(int64_t grid, hipStream_t s, const AccArgs &a) {
 }
 
 int64_t accumulate_grid(int64_t total_chunks, zds_accum_mode mode) {
-  int64_t grid = total_chunks * (mode == ZDS_COPY ? parts_per_chunk<ZDS_COPY>() : parts_per_chunk<ZDS_OVERWRITE>());
+  const int parts = mode == ZDS_COPY ? parts_per_chunk<ZDS_COPY>()
+                                     : (mode == ZDS_OVERWRITE ? parts_per_chunk<ZDS_OVERWRITE>()
+                                                              : parts_per_chunk<ZDS_ACCUMULATE>());
+  int64_t grid = total_chunks * parts;
   if (grid > max_blocks(kAccBlock)) grid = max_blocks(kAccBlock);
   if (grid < 1) grid = 1;
   return grid;

@@ -348,8 +348,8 @@ extern "C" zds_status zds_grad_accumulate(zds_plan *plan, const void *const *src
 
 extern "C" size_t zds_plan_norm_workspace_bytes(const zds_plan *plan) {
   if (!plan) return 0;
-  // the fp32 modes launch the most blocks, hence write the most partials
-  return static_cast<size_t>(partials_workspace_doubles(accumulate_grid(plan->total_chunks, ZDS_OVERWRITE))) *
+  // the accumulate mode launches the most blocks, hence writes the most partials
+  return static_cast<size_t>(partials_workspace_doubles(accumulate_grid(plan->total_chunks, ZDS_ACCUMULATE))) *
          sizeof(double);
 }
 
