@@ -70,10 +70,13 @@ __device__ __forceinline__ uint16_t narrow1(float a) {
 // "sc0 sc1 nt" (system scope, written through), which has no builtin, so
 // they are one vector global store in inline assembly; other sizes use the
 // compiler's non-temporal store. A store of more than 8 bytes reads its data
-// registers one cycle late: a VALU write to them right after the store needs
-// one wait state in between, which the compiler's hazard pass does not insert
-// for a store inside inline assembly, so the 16-byte form carries its own
-// s_nop. Measured on the 7B shard, interleaved A/B, store policies "nt" /
+// registers late: on gfx950 a VALU write to them needs two wait states after
+// the store (the compiler pads a plain 16-byte store that way), which the
+// compiler's hazard pass does not insert for a store inside inline assembly,
+// so the 16-byte form carries its own s_nop 1. With one wait state only, a
+// decode variant whose compiler placed an address computation into the data
+// registers right after the store wrote wrong values.
+// Measured on the 7B shard, interleaved A/B, store policies "nt" /
 // "sc1 nt" / "sc0 sc1 nt": AdamW 6,282 / 6,297 / 6,301 GB/s, flatten + norm
 // 5,997 / 6,014 / 6,040 GB/s, a plain copy 6,524 / 6,627 / 6,631; plain
 // (write-back) stores: AdamW 5,517 GB/s against 6,215.
@@ -84,7 +87,7 @@ __device__ __forceinline__ T ld_stream(const T *p) {
 template <typename T>
 __device__ __forceinline__ void st_stream(T *p, T v) {
   if constexpr (sizeof(T) == 16) {
-    asm volatile("global_store_dwordx4 %0, %1, off sc0 sc1 nt\n\ts_nop 0" : : "v"(p), "v"(v) : "memory");
+    asm volatile("global_store_dwordx4 %0, %1, off sc0 sc1 nt\n\ts_nop 1" : : "v"(p), "v"(v) : "memory");
   } else if constexpr (sizeof(T) == 8) {
     asm volatile("global_store_dwordx2 %0, %1, off sc0 sc1 nt" : : "v"(p), "v"(v) : "memory");
   } else {
