@@ -291,6 +291,7 @@ zds_status zds_overflow_and_norm_noalloc(const void *grads, zds_dtype dtype, int
  *   master, exp_avg, exp_avg_sq   device fp32, n elements, updated in place
  *   params_out  device, n elements of param_dtype (FP16/BF16), write-only;
  *               NULL skips the cast.
+ *   n           below 2^40 (EINVAL otherwise; tile indices are 32-bit).
  * The state is read, not advanced: zds_loss_scaler_update commits t. */
 zds_status zds_adam_step(const zds_adamw_hparams *hp, const void *grads, zds_dtype grad_dtype,
                          float *master, float *exp_avg, float *exp_avg_sq, void *params_out,

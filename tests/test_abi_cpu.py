@@ -136,6 +136,9 @@ def test_argument_errors():
     # bad dtype, negative n, betas out of range: rejected before any launch
     assert lib.zds_adam_step(ctypes.byref(hp), None, 7, None, None, None, None, 0, 10, None, None, None) == zds.ZDS_EINVAL
     assert lib.zds_adam_step(ctypes.byref(hp), None, 0, None, None, None, None, 0, -1, None, None, None) == zds.ZDS_EINVAL
+    # n at or past 2^40 (the kernels' tile indices are 32-bit)
+    assert lib.zds_adam_step(ctypes.byref(hp), 16, 0, 32, 48, 64, None, 0, 1 << 40, 128, 192, None) == zds.ZDS_EINVAL
+    assert "2^40" in zds.zds_last_error()
     bad = zds.hparams(beta1=1.0)
     assert lib.zds_adam_step(ctypes.byref(bad), None, 0, None, None, None, None, 0, 10, None, None, None) == zds.ZDS_EINVAL
     # zero length is a no-op

@@ -15,24 +15,29 @@
 // 32 B make two instructions each touch every line half, which measured far
 // slower.) The kernels are wave-specialised: each wave of a block moves one
 // array piece of the block's tile (master, m, v, grads in / 16-bit params
-// out), and the pieces meet in LDS where every thread updates one element.
+// out), and the pieces meet in LDS where every thread updates its elements.
 // Against a kernel in which each lane moves all arrays of its own 4 elements,
 // this lowers the memory footprint per wave from 4 loads + 4 stores to 1 + 1
-// and raised the pass from about 5.8 to 6.0 TB/s on the 7B shard. A block
-// takes 2 consecutive tiles (6.0 -> 6.3 TB/s: half the block launches, same
-// footprint per wave) and the grid has one block per tile pair, so the
-// dispatcher keeps every CU full as blocks finish. Issuing the second tile's
-// loads before the first tile's update (software pipelining) measured
-// slower: on this memory system more bytes in flight per wave lose to more
-// waves with one access each.
+// and raised the pass from about 5.8 to 6.0 TB/s on the 7B shard.
 //
-// The default is adam_wide_kernel: 8 waves and 512 elements per tile, so that
-// the 16-bit grads and params also move as one 1 KiB access per wave (16
-// bytes per lane), like the fp32 halves; in A/B runs interleaved with the
-// order rotated each round it was 1.0 and 2.7 % faster (two boxes) than
-// adam_tile_kernel, the 4-wave form with 256-element tiles and 512-byte
-// 16-bit accesses, which remains the path for 16-bit buffers that are 8- but
-// not 16-byte aligned.
+// The default is adam_wide_kernel: 8 waves and one 1024-element tile per
+// block, the grid one block per tile, so the dispatcher keeps every CU full
+// with short-lived blocks that each stream one contiguous piece of every
+// array. Each wave moves 2 KiB of its array as two 1 KiB accesses (16 bytes
+// per lane) and issues the second only after the first has completed, for its
+// loads and for its stores: this memory system rewards many waves with one
+// access each in flight. Measured on the 7B shard against the kernel it
+// replaced (2 consecutive 512-element tiles per block, one 1 KiB access per
+// wave per tile: 6.3 TB/s), library builds swapped between bench runs, three
+// rounds on one box: 3.687-3.694 ms against 3.745-3.750 (+1.5 %); with the
+// two accesses of a wave back to back, or with only the loads or only the
+// stores one at a time, it is slower than that kernel (probe, bit-exact: -0.7,
+// -2.0, -2.9 %), and so are 2048-element tiles (4 accesses per wave, -1.6 %).
+// adam_tile_kernel, a 4-wave form with 256-element tiles and 512-byte 16-bit
+// accesses (2 tiles per block), remains the path for 16-bit buffers that are
+// 8- but not 16-byte aligned. In both kernels the wave's role index is made
+// wave-uniform (readfirstlane), so role branches, array bases and tile
+// counters are scalar.
 //
 // The update's instruction count shows in the pass's bandwidth: the VALU is
 // about half busy at full rate, and a block's update phase is time in which it
@@ -54,11 +59,11 @@
 #include "zds_internal.h"
 
 namespace {
-// Consecutive tiles per block in the tile kernels (1 and 3 measured slower).
+// Consecutive tiles per block in the 4-wave kernel (1 and 3 measured slower).
 constexpr int kTilesPerBlock = 2;
 // Threads per block of the element-wise kernel.
 constexpr int kScalarBlock = 256;
-// Upper bound on the tile kernels' grid (blocks loop over the tiles beyond it).
+// Upper bound on the tile kernels' grids (blocks loop over the tiles beyond it).
 constexpr int64_t kTileGridCap = int64_t(1) << 23;
 }  // namespace
 
@@ -150,7 +155,7 @@ __global__ void __launch_bounds__(256) adam_tile_kernel(const zds_step_scalars *
   if (sc->overflow) return;
   const ElemConsts c = load_consts(sc);
   const int lane = threadIdx.x & 63;
-  const int w = threadIdx.x >> 6;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: scalar role branches
   const int64_t quads = a.n >> 2;
   // Wave w reads and writes LDS buffer w in the load and store phases and
   // all threads touch every buffer in the update phase, which sits between
@@ -224,79 +229,96 @@ __global__ void __launch_bounds__(256) adam_tile_kernel(const zds_step_scalars *
   }
 }
 
-// Wide wave-specialised variant. A block of 8 waves owns a tile of 512
-// elements: waves 0-1 move the two 1 KiB halves of the master tile, 2-3 m,
-// 4-5 v; 16-bit grads come in through wave 6 (8 elements per lane, one 1 KiB
-// access) and the 16-bit params go out through wave 7; fp32 grads come in
-// through waves 6 and 7 (a half each). Each of the 512 threads updates one
-// element. The tiles cover the first n & ~7 elements; block 0 takes the rest
-// element-wise. As in the 4-wave kernel, outside the update phase each wave
-// writes and reads only its own part of the LDS tiles, so two barriers per
-// tile suffice. Whole tiles take a path without per-lane bounds checks (the
-// test is uniform per block); only the last, partial tile checks each lane.
-// LDS of one block: the three fp32 tiles, the grad tile (16-bit or fp32)
-// and the 16-bit param tile, each starting at a multiple of 1 KiB.
+// Wide wave-specialised variant: one tile of 1024 elements per 8-wave block.
+// Waves 0-1 move the two 2 KiB halves of the master tile, 2-3 m, 4-5 v;
+// 16-bit grads come in through wave 6 (2 KiB) and the 16-bit params go out
+// through wave 7 (2 KiB); fp32 grads come in through waves 6 and 7 (2 KiB
+// each). Every wave moves its 2 KiB as two 1 KiB wave accesses and issues the
+// second only after the first has completed, loads and stores alike, so each
+// wave has one access in flight; each thread updates elements t and t + 512.
+// The tiles cover the first n & ~7 elements; block 0 takes the rest
+// element-wise. Outside the update phase each wave writes and reads only its
+// own part of the LDS tiles. Whole tiles take a path without per-lane bounds
+// checks (the test is uniform per block); only the last, partial tile checks
+// each lane.
 template <int GD>
 struct WideTile {
-  f32x4 sf[3][128];
-  u32x4 sg16[64];
-  u32x4 so16[64];
+  f32x4 sf[3][256];
+  u32x4 sg16[128];
+  u32x4 so16[128];
   __device__ f32x4 *sgf() { return sf[0]; }  // unused for 16-bit grads
 };
 template <>
 struct WideTile<ZDS_FP32> {
-  f32x4 sf[3][128];
-  f32x4 sgf_[128];
-  u32x4 so16[64];
+  f32x4 sf[3][256];
+  f32x4 sgf_[256];
+  u32x4 so16[128];
   u32x4 sg16[1];
   __device__ f32x4 *sgf() { return sgf_; }
 };
 
+// Elements per tile of the wide kernel.
+constexpr int kWideTile = 1024;
+
 template <int GD, int PD, bool WRITE_OUT, bool FULL>
-__device__ __forceinline__ void wide_tile(const AdamArgs &a, const ElemConsts &c, WideTile<GD> &sh, float *arr,
-                                          int64_t tile, int64_t nv) {
+__device__ __forceinline__ void wide_tile(const AdamArgs &a, const ElemConsts &c, WideTile<GD> &sh, float *arr, int w,
+                                          uint32_t tile, int64_t nv) {
   const int lane = threadIdx.x & 63;
-  const int w = threadIdx.x >> 6;
-  const int half = (w & 1) * 64 + lane;  // this wave's half of a 128-quad tile
-  const int64_t q = tile * 128 + half;
-  const int64_t o = tile * 64 + lane;
+  const uint32_t i0 = (w & 1) * 128 + lane;  // this wave's quads of a 256-quad tile: i0 and i0 + 64
+  const int64_t q0 = static_cast<int64_t>(tile) * 256 + i0;  // the same as quads of the array
+  const int64_t o0 = static_cast<int64_t>(tile) * 128 + lane;  // 8-element groups of a 16-bit array
   const int64_t quads = nv >> 2;
   const int64_t octs = nv >> 3;
+  float *tp = arr + static_cast<size_t>(tile) * kWideTile;  // this tile of this wave's fp32 array
   memory_phase();
   if (w < 6) {
-    if (FULL || q < quads) sh.sf[w >> 1][half] = ld_stream(reinterpret_cast<const f32x4 *>(arr) + q);
+    if (FULL || q0 < quads) sh.sf[w >> 1][i0] = ld_stream_at_once<f32x4>(tp, i0 * 16);
+    if (FULL || q0 + 64 < quads) sh.sf[w >> 1][i0 + 64] = ld_stream_at_once<f32x4>(tp, (i0 + 64) * 16);
   } else if (GD == ZDS_FP32) {
-    if (FULL || q < quads) sh.sgf()[half] = ld_stream(static_cast<const f32x4 *>(a.g) + q);
+    const float *tg = static_cast<const float *>(a.g) + static_cast<size_t>(tile) * kWideTile;
+    if (FULL || q0 < quads) sh.sgf()[i0] = ld_stream_at_once<f32x4>(tg, i0 * 16);
+    if (FULL || q0 + 64 < quads) sh.sgf()[i0 + 64] = ld_stream_at_once<f32x4>(tg, (i0 + 64) * 16);
   } else if (w == 6) {
-    if (FULL || o < octs) sh.sg16[lane] = ld_stream(static_cast<const u32x4 *>(a.g) + o);
+    const uint16_t *tg = static_cast<const uint16_t *>(a.g) + static_cast<size_t>(tile) * kWideTile;
+    if (FULL || o0 < octs) sh.sg16[lane] = ld_stream_at_once<u32x4>(tg, lane * 16);
+    if (FULL || o0 + 64 < octs) sh.sg16[lane + 64] = ld_stream_at_once<u32x4>(tg, (lane + 64) * 16);
   }
   update_phase();
   __syncthreads();
-  const int t = threadIdx.x;
-  if (FULL || tile * 512 + t < nv) {
-    float *fp = reinterpret_cast<float *>(sh.sf[0]);
-    float *fm = reinterpret_cast<float *>(sh.sf[1]);
-    float *fv = reinterpret_cast<float *>(sh.sf[2]);
-    float x;
-    if (GD == ZDS_FP32) {
-      x = reinterpret_cast<const float *>(sh.sgf())[t];
-    } else {
-      const uint32_t b = reinterpret_cast<const uint16_t *>(sh.sg16)[t];
-      x = GD == ZDS_BF16 ? __uint_as_float(b << 16) : __half2float(__ushort_as_half(static_cast<unsigned short>(b)));
+  float *fp = reinterpret_cast<float *>(sh.sf[0]);
+  float *fm = reinterpret_cast<float *>(sh.sf[1]);
+  float *fv = reinterpret_cast<float *>(sh.sf[2]);
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int t = threadIdx.x + 512 * k;
+    if (FULL || static_cast<int64_t>(tile) * kWideTile + t < nv) {
+      float x;
+      if (GD == ZDS_FP32) {
+        x = reinterpret_cast<const float *>(sh.sgf())[t];
+      } else {
+        const uint32_t b = reinterpret_cast<const uint16_t *>(sh.sg16)[t];
+        x = GD == ZDS_BF16 ? __uint_as_float(b << 16)
+                           : __half2float(__ushort_as_half(static_cast<unsigned short>(b)));
+      }
+      float p = fp[t], m = fm[t], v = fv[t];
+      adam_elem(x, c, p, m, v);
+      fp[t] = p;
+      fm[t] = m;
+      fv[t] = v;
+      if (WRITE_OUT) reinterpret_cast<uint16_t *>(sh.so16)[t] = narrow1<PD>(p);
     }
-    float p = fp[t], m = fm[t], v = fv[t];
-    adam_elem(x, c, p, m, v);
-    fp[t] = p;
-    fm[t] = m;
-    fv[t] = v;
-    if (WRITE_OUT) reinterpret_cast<uint16_t *>(sh.so16)[t] = narrow1<PD>(p);
   }
   __syncthreads();
   memory_phase();
   if (w < 6) {
-    if (FULL || q < quads) st_stream(reinterpret_cast<f32x4 *>(arr) + q, sh.sf[w >> 1][half]);
+    if (FULL || q0 < quads) st_stream_at(tp, i0 * 16, sh.sf[w >> 1][i0]);
+    wait_vmem();
+    if (FULL || q0 + 64 < quads) st_stream_at(tp, (i0 + 64) * 16, sh.sf[w >> 1][i0 + 64]);
   } else if (WRITE_OUT && w == 7) {
-    if (FULL || o < octs) st_stream(static_cast<u32x4 *>(a.out) + o, sh.so16[lane]);
+    uint16_t *to = static_cast<uint16_t *>(a.out) + static_cast<size_t>(tile) * kWideTile;
+    if (FULL || o0 < octs) st_stream_at(to, lane * 16, sh.so16[lane]);
+    wait_vmem();
+    if (FULL || o0 + 64 < octs) st_stream_at(to, (lane + 64) * 16, sh.so16[lane + 64]);
   }
   update_phase();
 }
@@ -308,20 +330,22 @@ __global__ void __launch_bounds__(512) adam_wide_kernel(const zds_step_scalars *
                                                         void *__restrict__ out, int64_t n) {
   __shared__ WideTile<GD> sh;
   const AdamArgs a{sc, g, p, m, v, out, n};
-  const int w = threadIdx.x >> 6;
+  // The role index is the same on every lane of a wave; read through
+  // readfirstlane the compiler knows it, so role branches, array bases and
+  // tile counters are scalar.
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t nv = n & ~int64_t(7);
-  const int64_t full = nv >> 9;                // whole 512-element tiles
-  const int64_t ntiles = (nv + 511) >> 9;
+  const uint32_t full = static_cast<uint32_t>(nv / kWideTile);  // whole tiles
+  const uint32_t ntiles = static_cast<uint32_t>((nv + kWideTile - 1) / kWideTile);
   float *arr = w < 2 ? p : (w < 4 ? m : v);
   if (sc->overflow) return;  // the step is skipped: uniform, nothing is touched
   const ElemConsts c = load_consts(sc);
-  for (int64_t it = static_cast<int64_t>(blockIdx.x) * kTilesPerBlock; it < ntiles;
-       it += static_cast<int64_t>(gridDim.x) * kTilesPerBlock)
-  for (int64_t tile = it; tile < it + kTilesPerBlock && tile < ntiles; ++tile) {  // uniform per block
+  // One tile per block; a grid capped below the tile count loops.
+  for (uint32_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {  // uniform per block
     if (tile < full)
-      wide_tile<GD, PD, WRITE_OUT, true>(a, c, sh, arr, tile, nv);
+      wide_tile<GD, PD, WRITE_OUT, true>(a, c, sh, arr, w, tile, nv);
     else
-      wide_tile<GD, PD, WRITE_OUT, false>(a, c, sh, arr, tile, nv);
+      wide_tile<GD, PD, WRITE_OUT, false>(a, c, sh, arr, w, tile, nv);
   }
   // Ragged tail: the last n % 8 elements, one per lane of block 0.
   if (blockIdx.x == 0 && nv + threadIdx.x < n) {
@@ -396,11 +420,20 @@ static uint32_t tile_grid(int64_t elems, int64_t tile, int threads) {
   return static_cast<uint32_t>(g);
 }
 
+// One block per kWideTile elements, capped like tile_grid.
+static uint32_t wide_grid(int64_t elems) {
+  int64_t g = (elems + kWideTile - 1) / kWideTile;
+  if (g < 1) g = 1;
+  if (g > max_blocks(512)) g = max_blocks(512);
+  if (g > kTileGridCap) g = kTileGridCap;
+  return static_cast<uint32_t>(g);
+}
+
 template <int GD, int PD, bool WO>
 static void launch_one(bool vec, bool vec16, hipStream_t s, const AdamArgs &a) {
   if (vec16) {
-    hipLaunchKernelGGL((adam_wide_kernel<GD, PD, WO>), dim3(tile_grid(a.n & ~int64_t(7), 512, 512)), dim3(512), 0,
-                       s, a.sc, a.g, a.p, a.m, a.v, a.out, a.n);
+    hipLaunchKernelGGL((adam_wide_kernel<GD, PD, WO>), dim3(wide_grid(a.n & ~int64_t(7))), dim3(512), 0, s, a.sc,
+                       a.g, a.p, a.m, a.v, a.out, a.n);
   } else if (vec) {
     hipLaunchKernelGGL((adam_tile_kernel<GD, PD, WO>), dim3(tile_grid(a.n & ~int64_t(3), 256, 256)), dim3(256), 0,
                        s, a.sc, a.g, a.p, a.m, a.v, a.out, a.n);

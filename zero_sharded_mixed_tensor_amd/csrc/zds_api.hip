@@ -508,6 +508,7 @@ extern "C" zds_status zds_adam_step(const zds_adamw_hparams *hp, const void *gra
   if (params_out && param_dtype != ZDS_FP16 && param_dtype != ZDS_BF16)
     return fail(ZDS_EINVAL, "zds_adam_step: param dtype must be fp16 or bf16");
   if (n < 0) return fail(ZDS_EINVAL, "zds_adam_step: n < 0");
+  if (n >= (int64_t(1) << 40)) return fail(ZDS_EINVAL, "zds_adam_step: n must be below 2^40");
   if (!(hp->beta1 >= 0.5f && hp->beta1 < 1.0f && hp->beta2 >= 0.5f && hp->beta2 < 1.0f))
     return fail(ZDS_EINVAL, "zds_adam_step: betas must lie in [0.5, 1)");
   if (!(hp->eps > 0.0f) || !(hp->lr >= 0.0f) || !(hp->weight_decay >= 0.0f))

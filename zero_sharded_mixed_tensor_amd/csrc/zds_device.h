@@ -94,6 +94,26 @@ __device__ __forceinline__ void st_stream(T *p, T v) {
     __builtin_nontemporal_store(v, p);
   }
 }
+// The same 16-byte streaming store at a wave-uniform base plus a 32-bit
+// per-lane byte offset (the scalar-base address form: the base stays in
+// scalar registers and a loop over tiles advances it with scalar adds).
+template <typename T>
+__device__ __forceinline__ void st_stream_at(void *base, uint32_t byte_off, T v) {
+  static_assert(sizeof(T) == 16, "16-byte stores only");
+  asm volatile("global_store_dwordx4 %0, %1, %2 sc0 sc1 nt\n\ts_nop 1" : : "v"(byte_off), "v"(v), "s"(base) : "memory");
+}
+// A 16-byte streaming load in the same address form that returns only once
+// the data has arrived (the wait is part of the same instruction sequence), so
+// that a wave issuing several of them has one load in flight at a time.
+template <typename T>
+__device__ __forceinline__ T ld_stream_at_once(const void *base, uint32_t byte_off) {
+  static_assert(sizeof(T) == 16, "16-byte loads only");
+  T r;
+  asm volatile("global_load_dwordx4 %0, %1, %2 nt\n\ts_waitcnt vmcnt(0)" : "=v"(r) : "v"(byte_off), "s"(base) : "memory");
+  return r;
+}
+// Waits until every vector memory access of the wave has completed.
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0f70); }  // vmcnt(0)
 
 // 8 consecutive 16-bit elements (one 16-byte access) at group index `group`,
 // as fp32.
