@@ -23,32 +23,38 @@
 // The default is adam_wide_kernel: 8 waves and one 1024-element tile per
 // block, the grid one block per tile, so the dispatcher keeps every CU full
 // with short-lived blocks that each stream one contiguous piece of every
-// array. Each wave moves 2 KiB of its array as two 1 KiB accesses (16 bytes
-// per lane) and issues the second only after the first has completed, for its
-// loads and for its stores: this memory system rewards many waves with one
-// access each in flight. Measured on the 7B shard against the kernel it
-// replaced (2 consecutive 512-element tiles per block, one 1 KiB access per
-// wave per tile: 6.3 TB/s), library builds swapped between bench runs, three
-// rounds on one box: 3.687-3.694 ms against 3.745-3.750 (+1.5 %); with the
-// two accesses of a wave back to back, or with only the loads or only the
-// stores one at a time, it is slower than that kernel (probe, bit-exact: -0.7,
-// -2.0, -2.9 %), and so are 2048-element tiles (4 accesses per wave, -1.6 %).
+// array. Each wave moves its part of the tile as 1 KiB accesses (16 bytes per
+// lane) and issues the next only after the previous one has completed, for
+// its loads and for its stores: this memory system rewards many waves with
+// one access each in flight. The tile's two halves are pipelined: the second
+// half's loads are in flight while the first half is updated, and the first
+// half's stores while the second half is updated, so the arithmetic is hidden
+// behind the memory accesses. Measured on the 7B shard, library builds swapped
+// between bench runs, three rounds on one box: 3.609-3.616 ms (0.815-0.817 of
+// 8 TB/s) against 3.696-3.701 for the same tile without the pipelining and
+// 3.720-3.724 for the kernel before (2 consecutive 512-element tiles per
+// block, one 1 KiB access per wave per tile). In probes (bit-exact), the
+// pipelined kernel ran as fast as the unpipelined one with the arithmetic left
+// out; a wave's two accesses back to back, or only its loads or only its
+// stores one at a time, were slower than the 2-tile kernel (-0.7, -2.0,
+// -2.9 %), and so were 2048-element tiles (4 accesses per wave, -1.6 %).
 // adam_tile_kernel, a 4-wave form with 256-element tiles and 512-byte 16-bit
 // accesses (2 tiles per block), remains the path for 16-bit buffers that are
 // 8- but not 16-byte aligned. In both kernels the wave's role index is made
 // wave-uniform (readfirstlane), so role branches, array bases and tile
 // counters are scalar.
 //
-// The update's instruction count shows in the pass's bandwidth: the VALU is
-// about half busy at full rate, and a block's update phase is time in which it
-// has nothing in flight. Two measures follow from that. (1) The division by
-// the per-step constant sqrt(1 - beta2^t) is a float64 multiplication by its
+// The update's instruction count showed in the bandwidth of the earlier,
+// unpipelined kernels, where a block's update phase was time with nothing in
+// flight. Two measures came from that and are kept. (1) The division by the
+// per-step constant sqrt(1 - beta2^t) is a float64 multiplication by its
 // float64 reciprocal, rounded to fp32 (3 instructions instead of the 11 of a
-// correctly rounded fp32 divide), +2.2 % on the 7B shard; it gives the
+// correctly rounded fp32 divide), +2.2 % on the 7B shard then; it gives the
 // correctly rounded quotient for every input, see adam_elem. (2) The waves
 // raise their scheduling priority while they issue loads and stores and drop
 // it for the update, so that a block's memory accesses are not queued behind
-// other blocks' arithmetic on the same SIMD: +0.3 to 1 % in four A/B runs.
+// other blocks' arithmetic on the same SIMD: +0.3 to 1 % in four A/B runs
+// then, neutral to -0.3 % on the unpipelined 1024-element tile.
 //
 // The step constants (lr / (1 - beta1^t), sqrt(1 - beta2^t) and its float64
 // reciprocal, 1 - lr*wd, the 1 - beta values) are derived once per call by a
@@ -229,18 +235,24 @@ __global__ void __launch_bounds__(256) adam_tile_kernel(const zds_step_scalars *
   }
 }
 
-// Wide wave-specialised variant: one tile of 1024 elements per 8-wave block.
-// Waves 0-1 move the two 2 KiB halves of the master tile, 2-3 m, 4-5 v;
-// 16-bit grads come in through wave 6 (2 KiB) and the 16-bit params go out
-// through wave 7 (2 KiB); fp32 grads come in through waves 6 and 7 (2 KiB
-// each). Every wave moves its 2 KiB as two 1 KiB wave accesses and issues the
-// second only after the first has completed, loads and stores alike, so each
-// wave has one access in flight; each thread updates elements t and t + 512.
-// The tiles cover the first n & ~7 elements; block 0 takes the rest
-// element-wise. Outside the update phase each wave writes and reads only its
-// own part of the LDS tiles. Whole tiles take a path without per-lane bounds
-// checks (the test is uniform per block); only the last, partial tile checks
-// each lane.
+// Wide wave-specialised variant: one tile of 1024 elements per 8-wave block,
+// in two halves of 512. Waves 0-1 move the master tile, 2-3 m, 4-5 v: wave w
+// holds quarter (w & 1) of each half, one 1 KiB access per half. 16-bit
+// grads: wave 6 loads the first half's (1 KiB), wave 7 the second half's, and
+// the 16-bit params go out the same way; fp32 grads are moved by waves 6 and 7
+// like a fourth fp32 array, and the params by wave 6 (first half) and 7.
+// Each wave has one access in flight at a time, and the halves are pipelined
+// so that the arithmetic overlaps the memory accesses:
+//   load half 0 (and wait); issue the load of half 1      | barrier 1
+//   update half 0 (each thread one element); store half 1's data in LDS
+//                                                          | barrier 2
+//   store half 0; update half 1; wait for the store         | barrier 3
+//   store half 1
+// Outside the update phases each wave writes and reads only its own part of
+// the LDS tiles; the update of a half reads and writes only that half. The
+// tiles cover the first n & ~7 elements; block 0 takes the rest element-wise.
+// Whole tiles take a path without per-lane bounds checks (the test is uniform
+// per block); only the last, partial tile checks each lane.
 template <int GD>
 struct WideTile {
   f32x4 sf[3][256];
@@ -260,67 +272,106 @@ struct WideTile<ZDS_FP32> {
 // Elements per tile of the wide kernel.
 constexpr int kWideTile = 1024;
 
+// Update of element h * 512 + threadIdx.x of the tile in LDS.
 template <int GD, int PD, bool WRITE_OUT, bool FULL>
-__device__ __forceinline__ void wide_tile(const AdamArgs &a, const ElemConsts &c, WideTile<GD> &sh, float *arr, int w,
-                                          uint32_t tile, int64_t nv) {
-  const int lane = threadIdx.x & 63;
-  const uint32_t i0 = (w & 1) * 128 + lane;  // this wave's quads of a 256-quad tile: i0 and i0 + 64
-  const int64_t q0 = static_cast<int64_t>(tile) * 256 + i0;  // the same as quads of the array
-  const int64_t o0 = static_cast<int64_t>(tile) * 128 + lane;  // 8-element groups of a 16-bit array
-  const int64_t quads = nv >> 2;
-  const int64_t octs = nv >> 3;
-  float *tp = arr + static_cast<size_t>(tile) * kWideTile;  // this tile of this wave's fp32 array
-  memory_phase();
-  if (w < 6) {
-    if (FULL || q0 < quads) sh.sf[w >> 1][i0] = ld_stream_at_once<f32x4>(tp, i0 * 16);
-    if (FULL || q0 + 64 < quads) sh.sf[w >> 1][i0 + 64] = ld_stream_at_once<f32x4>(tp, (i0 + 64) * 16);
-  } else if (GD == ZDS_FP32) {
-    const float *tg = static_cast<const float *>(a.g) + static_cast<size_t>(tile) * kWideTile;
-    if (FULL || q0 < quads) sh.sgf()[i0] = ld_stream_at_once<f32x4>(tg, i0 * 16);
-    if (FULL || q0 + 64 < quads) sh.sgf()[i0 + 64] = ld_stream_at_once<f32x4>(tg, (i0 + 64) * 16);
-  } else if (w == 6) {
-    const uint16_t *tg = static_cast<const uint16_t *>(a.g) + static_cast<size_t>(tile) * kWideTile;
-    if (FULL || o0 < octs) sh.sg16[lane] = ld_stream_at_once<u32x4>(tg, lane * 16);
-    if (FULL || o0 + 64 < octs) sh.sg16[lane + 64] = ld_stream_at_once<u32x4>(tg, (lane + 64) * 16);
-  }
-  update_phase();
-  __syncthreads();
+__device__ __forceinline__ void wide_update(const ElemConsts &c, WideTile<GD> &sh, int h, int64_t first, int64_t nv) {
+  const int t = threadIdx.x + 512 * h;
+  if (!FULL && first + t >= nv) return;
   float *fp = reinterpret_cast<float *>(sh.sf[0]);
   float *fm = reinterpret_cast<float *>(sh.sf[1]);
   float *fv = reinterpret_cast<float *>(sh.sf[2]);
-#pragma unroll
-  for (int k = 0; k < 2; ++k) {
-    const int t = threadIdx.x + 512 * k;
-    if (FULL || static_cast<int64_t>(tile) * kWideTile + t < nv) {
-      float x;
-      if (GD == ZDS_FP32) {
-        x = reinterpret_cast<const float *>(sh.sgf())[t];
-      } else {
-        const uint32_t b = reinterpret_cast<const uint16_t *>(sh.sg16)[t];
-        x = GD == ZDS_BF16 ? __uint_as_float(b << 16)
-                           : __half2float(__ushort_as_half(static_cast<unsigned short>(b)));
-      }
-      float p = fp[t], m = fm[t], v = fv[t];
-      adam_elem(x, c, p, m, v);
-      fp[t] = p;
-      fm[t] = m;
-      fv[t] = v;
-      if (WRITE_OUT) reinterpret_cast<uint16_t *>(sh.so16)[t] = narrow1<PD>(p);
+  float x;
+  if (GD == ZDS_FP32) {
+    x = reinterpret_cast<const float *>(sh.sgf())[t];
+  } else {
+    const uint32_t b = reinterpret_cast<const uint16_t *>(sh.sg16)[t];
+    x = GD == ZDS_BF16 ? __uint_as_float(b << 16) : __half2float(__ushort_as_half(static_cast<unsigned short>(b)));
+  }
+  float p = fp[t], m = fm[t], v = fv[t];
+  adam_elem(x, c, p, m, v);
+  fp[t] = p;
+  fm[t] = m;
+  fv[t] = v;
+  if (WRITE_OUT) reinterpret_cast<uint16_t *>(sh.so16)[t] = narrow1<PD>(p);
+}
+
+// One tile. fp32 role (waves 0-5, and 6-7 for fp32 grads): `base` is this
+// wave's array, `lt` its LDS tile. The quads of half h this wave moves are
+// qa + 128 h (qa = 64 (w & 1) + lane).
+template <int GD, int PD, bool WRITE_OUT, bool FULL>
+__device__ __forceinline__ void wide_tile(const AdamArgs &a, const ElemConsts &c, WideTile<GD> &sh, float *base, int w,
+                                          uint32_t tile, int64_t nv) {
+  const int lane = threadIdx.x & 63;
+  const uint32_t qa = 64 * (w & 1) + lane;
+  const int64_t first = static_cast<int64_t>(tile) * kWideTile;  // first element of the tile
+  const int64_t quads = nv >> 2;
+  const int64_t octs = nv >> 3;
+  const bool fp32_role = w < 6 || GD == ZDS_FP32;
+  if (fp32_role) {
+    f32x4 *lt = w < 6 ? sh.sf[w >> 1] : sh.sgf();
+    float *tp = wave_uniform(base + first);
+    const bool in0 = FULL || first / 4 + qa < quads;
+    const bool in1 = FULL || first / 4 + qa + 128 < quads;
+    memory_phase();
+    if (in0) lt[qa] = ld_stream_at_once<f32x4>(tp, qa * 16);
+    f32x4 b4;
+    if (in1) b4 = ld_stream_global(reinterpret_cast<const f32x4 *>(tp) + qa + 128);
+    update_phase();
+    __syncthreads();
+    wide_update<GD, PD, WRITE_OUT, FULL>(c, sh, 0, first, nv);
+    if (in1) lt[qa + 128] = b4;
+    __syncthreads();
+    if (w < 6) {
+      memory_phase();
+      if (in0) st_stream_at(tp, qa * 16, lt[qa]);
+      update_phase();
+      wide_update<GD, PD, WRITE_OUT, FULL>(c, sh, 1, first, nv);
+      wait_vmem();
+      __syncthreads();
+      memory_phase();
+      if (in1) st_stream_at(tp, (qa + 128) * 16, lt[qa + 128]);
+      update_phase();
+      return;
     }
+  } else if (w == 6) {  // 16-bit grads of half 0
+    const uint16_t *tg = wave_uniform(static_cast<const uint16_t *>(a.g) + first);
+    memory_phase();
+    if (FULL || first / 8 + lane < octs) sh.sg16[lane] = ld_stream_at_once<u32x4>(tg, lane * 16);
+    update_phase();
+    __syncthreads();
+    wide_update<GD, PD, WRITE_OUT, FULL>(c, sh, 0, first, nv);
+    __syncthreads();
+  } else {  // w == 7: 16-bit grads of half 1
+    const uint16_t *tg = wave_uniform(static_cast<const uint16_t *>(a.g) + first);
+    const bool in1 = FULL || first / 8 + 64 + lane < octs;
+    memory_phase();
+    u32x4 gb;
+    if (in1) gb = ld_stream_global(reinterpret_cast<const u32x4 *>(tg) + 64 + lane);
+    update_phase();
+    __syncthreads();
+    wide_update<GD, PD, WRITE_OUT, FULL>(c, sh, 0, first, nv);
+    if (in1) sh.sg16[64 + lane] = gb;
+    __syncthreads();
   }
-  __syncthreads();
-  memory_phase();
-  if (w < 6) {
-    if (FULL || q0 < quads) st_stream_at(tp, i0 * 16, sh.sf[w >> 1][i0]);
+  // waves 6 and 7 from barrier 2 on: 16-bit params of half 0 (wave 6) and
+  // half 1 (wave 7)
+  uint16_t *to = wave_uniform(static_cast<uint16_t *>(a.out) + first);
+  const uint32_t o = 64 * (w & 1) + lane;
+  const bool ino = FULL || first / 8 + o < octs;
+  if (w == 6) {
+    memory_phase();
+    if (WRITE_OUT && ino) st_stream_at(to, o * 16, sh.so16[o]);
+    update_phase();
+    wide_update<GD, PD, WRITE_OUT, FULL>(c, sh, 1, first, nv);
     wait_vmem();
-    if (FULL || q0 + 64 < quads) st_stream_at(tp, (i0 + 64) * 16, sh.sf[w >> 1][i0 + 64]);
-  } else if (WRITE_OUT && w == 7) {
-    uint16_t *to = static_cast<uint16_t *>(a.out) + static_cast<size_t>(tile) * kWideTile;
-    if (FULL || o0 < octs) st_stream_at(to, lane * 16, sh.so16[lane]);
-    wait_vmem();
-    if (FULL || o0 + 64 < octs) st_stream_at(to, (lane + 64) * 16, sh.so16[lane + 64]);
+    __syncthreads();
+  } else {
+    wide_update<GD, PD, WRITE_OUT, FULL>(c, sh, 1, first, nv);
+    __syncthreads();
+    memory_phase();
+    if (WRITE_OUT && ino) st_stream_at(to, o * 16, sh.so16[o]);
+    update_phase();
   }
-  update_phase();
 }
 
 template <int GD, int PD, bool WRITE_OUT>
@@ -337,15 +388,19 @@ __global__ void __launch_bounds__(512) adam_wide_kernel(const zds_step_scalars *
   const int64_t nv = n & ~int64_t(7);
   const uint32_t full = static_cast<uint32_t>(nv / kWideTile);  // whole tiles
   const uint32_t ntiles = static_cast<uint32_t>((nv + kWideTile - 1) / kWideTile);
-  float *arr = w < 2 ? p : (w < 4 ? m : v);
+  // the fp32 array this wave moves (waves 6-7: the fp32 grads, if any)
+  float *base = w < 2 ? p : (w < 4 ? m : (w < 6 ? v : static_cast<float *>(const_cast<void *>(g))));
   if (sc->overflow) return;  // the step is skipped: uniform, nothing is touched
   const ElemConsts c = load_consts(sc);
-  // One tile per block; a grid capped below the tile count loops.
+  // One tile per block; a grid capped below the tile count loops. Every
+  // tile ends with the last wave stores after barrier 3; the next tile's
+  // loads write only the issuing wave's own LDS part, which no other wave
+  // reads before that tile's barrier 1.
   for (uint32_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {  // uniform per block
     if (tile < full)
-      wide_tile<GD, PD, WRITE_OUT, true>(a, c, sh, arr, w, tile, nv);
+      wide_tile<GD, PD, WRITE_OUT, true>(a, c, sh, base, w, tile, nv);
     else
-      wide_tile<GD, PD, WRITE_OUT, false>(a, c, sh, arr, w, tile, nv);
+      wide_tile<GD, PD, WRITE_OUT, false>(a, c, sh, base, w, tile, nv);
   }
   // Ragged tail: the last n % 8 elements, one per lane of block 0.
   if (blockIdx.x == 0 && nv + threadIdx.x < n) {

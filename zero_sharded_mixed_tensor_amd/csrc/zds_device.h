@@ -94,6 +94,15 @@ __device__ __forceinline__ void st_stream(T *p, T v) {
     __builtin_nontemporal_store(v, p);
   }
 }
+// A pointer that is the same on every lane of the wave, moved to scalar
+// registers (the address form below needs its base there).
+template <typename T>
+__device__ __forceinline__ T *wave_uniform(T *p) {
+  const uint64_t u = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(u));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(u >> 32));
+  return reinterpret_cast<T *>((static_cast<uint64_t>(hi) << 32) | lo);
+}
 // The same 16-byte streaming store at a wave-uniform base plus a 32-bit
 // per-lane byte offset (the scalar-base address form: the base stays in
 // scalar registers and a loop over tiles advances it with scalar adds).
@@ -111,6 +120,14 @@ __device__ __forceinline__ T ld_stream_at_once(const void *base, uint32_t byte_o
   T r;
   asm volatile("global_load_dwordx4 %0, %1, %2 nt\n\ts_waitcnt vmcnt(0)" : "=v"(r) : "v"(byte_off), "s"(base) : "memory");
   return r;
+}
+// A 16-byte streaming load through a global-address-space pointer, so that it
+// is a global (not a flat) load: a flat load also counts against the LDS
+// counter, and the wait for LDS before a barrier would then wait for it too.
+template <typename T>
+__device__ __forceinline__ T ld_stream_global(const T *p) {
+  typedef __attribute__((address_space(1))) const T gT;
+  return __builtin_nontemporal_load((gT *)p);
 }
 // Waits until every vector memory access of the wave has completed.
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0f70); }  // vmcnt(0)
