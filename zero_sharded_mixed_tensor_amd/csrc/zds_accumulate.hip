@@ -14,9 +14,9 @@
 // range so each wave-level access is contiguous. Unaligned entries fall back
 // to element-wise moves. Bytes per element: copy 2+2, overwrite 2+4,
 // accumulate 2+4+4. A block takes a whole chunk in copy mode (2 accesses per
-// lane), half a chunk in overwrite mode (2 quads per lane) and a quarter
-// chunk in accumulate mode (1 quad per lane), and issues all of its vector
-// loads before its first store. Measured on the 7B shard
+// lane), half a chunk in overwrite mode and a quarter chunk in accumulate
+// mode (1 quad per lane), and issues all of its vector loads before its
+// first store (overwrite: see parts_per_chunk). Measured on the 7B shard
 // against 8192-element chunks (whole / half): copy with the fused norm
 // 0.535 vs 0.543-0.564 ms, 16 accumulated micro-batches 20.5 vs 21.1-22.2 ms,
 // the whole 7B model's flatten 4.08-4.15 vs 4.36-4.45 ms. Small units pay
@@ -42,9 +42,14 @@ struct AccArgs {
 
 // Work units per chunk. Copy mode takes a whole chunk per block (2 accesses
 // of 8 elements per lane); accumulate a quarter chunk (one quad per lane: a
-// 16-bit load, an fp32 load and an fp32 store); overwrite half a chunk (two
-// quads per lane: its block moves only 6 B per element, and with a quarter
-// chunk the two rounds of table lookups at each block's start cost 15 %).
+// 16-bit load, an fp32 load and an fp32 store); overwrite half a chunk (its
+// block moves only 6 B per element, and with a quarter chunk the two rounds
+// of table lookups at each block's start cost 15 %). With 16-bit sources
+// that are 16-byte aligned, overwrite loads 8 elements per lane (1 KiB wave
+// accesses), re-lays them out through LDS and stores two 1 KiB fp32 wave
+// accesses one at a time: 776-778 against 789-790 us on the 7B shard (fp16
+// sources, rocprofv3 traces, builds swapped, two rounds); otherwise two
+// quads per lane (8-byte 16-bit loads).
 // Measured on the 7B shard, fp16 sources, library builds swapped, two
 // rounds: overwrite 0.90 ms (5,610 GB/s) with a quarter chunk, 0.80 ms
 // (6,330 GB/s) with half a chunk, 0.84 with a whole chunk (4 quads per
@@ -139,6 +144,46 @@ __global__ void __launch_bounds__(kAccBlock) accumulate_kernel(AccArgs a) {
       for (int64_t j = (groups << 3) + threadIdx.x; j < pc.cnt; j += BLK) {
         d16[j] = s16[j];
         if (NORM) ss = sq_add(widen1<SD>(s16, j), ss);
+      }
+    } else if (MODE == ZDS_OVERWRITE && SD != ZDS_FP32 && aligned(pc.src, 16) && pc.vec) {
+      // 16-bit sources 16-byte aligned: wave w converts elements
+      // [512 w, 512 w + 512) of the unit; lane l loads 8 of them (one 1 KiB
+      // wave access), the wave re-lays them out through LDS, and stores the
+      // 2 KiB of fp32 as two 1 KiB wave accesses, the second issued after the
+      // first has completed.
+      __shared__ f32x4 xch[BLK / 64][128];
+      const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+      const int lane = threadIdx.x & 63;
+      const int64_t groups = pc.cnt >> 3;  // whole 8-element groups of the unit
+      const int64_t gi = 64 * w + lane;
+      float *d32 = static_cast<float *>(a.dst) + pc.d0 + 512 * w;
+      if (gi < groups) {
+        float x[8];
+        load8<SD == ZDS_FP32 ? ZDS_FP16 : SD>(pc.src, gi, x);  // (never reached for fp32)
+        xch[w][2 * lane] = f32x4{x[0], x[1], x[2], x[3]};
+        xch[w][2 * lane + 1] = f32x4{x[4], x[5], x[6], x[7]};
+      }
+      __builtin_amdgcn_wave_barrier();  // the wave's LDS writes before its reads
+#pragma unroll
+      for (int r = 0; r < 2; ++r) {
+        const int qi = lane + 64 * r;  // quad of the wave's 512 elements
+        if (128 * w + qi < 2 * groups) {
+          const f32x4 o = xch[w][qi];
+          st_stream(reinterpret_cast<f32x4 *>(d32) + qi, o);
+          if (NORM) {
+            ss = sq_add(o.x, ss); ss = sq_add(o.y, ss); ss = sq_add(o.z, ss); ss = sq_add(o.w, ss);
+          }
+        }
+        if (r == 0) wait_vmem();
+      }
+      __builtin_amdgcn_wave_barrier();  // reads done before the next unit's writes
+      // the ragged tail of the unit
+      const uint16_t *s16 = reinterpret_cast<const uint16_t *>(pc.src);
+      float *t32 = static_cast<float *>(a.dst) + pc.d0;
+      for (int64_t j = (groups << 3) + threadIdx.x; j < pc.cnt; j += BLK) {
+        const float v = widen1<SD == ZDS_FP32 ? ZDS_FP16 : SD>(s16, j);
+        t32[j] = v;
+        if (NORM) ss = sq_add(v, ss);
       }
     } else {
       const int64_t quads = pc.vec ? pc.cnt >> 2 : 0;
