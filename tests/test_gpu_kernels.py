@@ -242,6 +242,9 @@ def test_scaler_device_trajectories():
 
 
 def _make_table(rng, T, dtype, misalign=False):
+    """misalign: every third source starts 1 element (True) or `misalign`
+    elements (an int: 4 gives 8-byte but not 16-byte aligned 16-bit
+    sources) past an aligned address."""
     numels = [int(x) for x in rng.integers(1, 40000, T)]
     numels[0] = 5  # a tiny tensor
     if T > 2:
@@ -251,7 +254,8 @@ def _make_table(rng, T, dtype, misalign=False):
         a = draw_grads(n, dtype, 1e-3, 2.0 ** 12, 9, 92, i)
         srcs_np.append(a)
         if misalign and i % 3 == 1:
-            d = to_dev(np.concatenate([a[:1], a]), dtype)[1:]
+            k = 1 if misalign is True else int(misalign)
+            d = to_dev(np.concatenate([a[:k], a]), dtype)[k:]
         else:
             d = to_dev(a, dtype)
         srcs_dev.append(d)
@@ -259,7 +263,7 @@ def _make_table(rng, T, dtype, misalign=False):
 
 
 @pytest.mark.parametrize("T,align,world,misalign", [(1, 64, 1, False), (7, 64, 3, False), (33, 8, 4, True),
-                                                    (100, 64, 8, False), (300, 1, 5, True)])
+                                                    (100, 64, 8, False), (300, 1, 5, True), (40, 64, 4, 4)])
 @pytest.mark.parametrize("dtype", ["fp16", "bf16"])
 def test_accumulate_parity(T, align, world, misalign, dtype):
     say("accumulate T=%d align=%d world=%d misalign=%s dtype=%s" % (T, align, world, misalign, dtype))
