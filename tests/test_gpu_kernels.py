@@ -30,7 +30,12 @@ def say(*a):
     sys.stdout.flush()
 
 
-SIZES = [1, 7, 8, 9, 255, 4099, 3 * 2048 + 5, 65536 * 3 + 13, (1 << 20) + 3]
+# The AdamW kernel works in 1024-element tiles of two 512-element halves,
+# the first n & ~7 elements, then n % 8 element-wise: sizes below cover a
+# lone partial tile, whole tiles, and partial last tiles that end inside the
+# first half, exactly at the halves' edge, and inside the second half.
+SIZES = [1, 7, 8, 9, 255, 4099, 3 * 2048 + 5, 65536 * 3 + 13, (1 << 20) + 3,
+         1024 + 523, 3 * 1024 + 512, 5 * 1024 + 709]
 
 
 def _inputs(n, gdt, seed, scale=2.0 ** 12, sigma=1e-3, prior=True):
