@@ -602,12 +602,14 @@ def test_adam_step_beyond_the_grid_cap(offset16):
     """n = 2^33 + 1003 elements, past the AdamW kernels' grid caps, so blocks
     loop over a second round of tiles, with a ragged n % 8 tail: bf16 grads
     N(0, 2e-3), static scale 1, clip 1.0, prior moments. offset16 = 0: the
-    8-wave kernel (cap 8,388,600 blocks of two 512-element tiles); 4: the
-    16-bit buffers start 8 bytes into their allocations, which takes the 4-wave
-    kernel (cap 16,777,208 blocks of two 256-element tiles). Sampled elements
-    (random, both ends, and around the first tiles of each kernel's second
-    round) against the oracle; the sum of squares against a float64 sum on the
-    device."""
+    8-wave kernel (a grid of at most min(2^23, (2^32 - 1) / 512) = 8,388,607
+    blocks of one 1024-element tile, so its second round starts at element
+    8,589,933,568 and holds one whole and one partial tile); 4: the 16-bit
+    buffers start 8 bytes into their allocations, which takes the 4-wave
+    kernel (at most 2^23 blocks of two 256-element tiles: second round from
+    element 2^32). Sampled elements (random, both ends, and around the first
+    tiles of each kernel's second round) against the oracle; the sum of
+    squares against the oracle's."""
     from workloads.device import fill_normal_
     n = (1 << 33) + 1003
     say("AdamW beyond the grid cap: n =", n, "16-bit offset", offset16)
@@ -621,7 +623,8 @@ def test_adam_step_beyond_the_grid_cap(offset16):
     out = oraw[offset16:]
     rng = np.random.default_rng(134)
     idx = [rng.integers(0, n, 65536), np.arange(0, 64), np.arange(n - 1100, n)]
-    for wrap in (8_388_600 * 2 * 512, 16_777_208 * 2 * 256):
+    cap = lambda threads: min(1 << 23, ((1 << 32) - 1) // threads)  # noqa: E731  (blocks per launch)
+    for wrap in (cap(512) * 1024, cap(256) * 2 * 256):
         idx.append(np.arange(wrap - 600, min(n, wrap + 600)))
     idx = np.concatenate(idx)
     idx = torch.from_numpy(np.unique(idx).astype(np.int64)).cuda()
