@@ -599,17 +599,16 @@ def test_beyond_the_grid_cap_intake_and_codec():
 
 @pytest.mark.parametrize("offset16", [0, 4])
 def test_adam_step_beyond_the_grid_cap(offset16):
-    """n = 2^33 + 1003 elements, past the AdamW kernels' grid caps, so blocks
+    """n = 2^33 + 1003 elements, past the AdamW kernel's grid cap, so blocks
     loop over a second round of tiles, with a ragged n % 8 tail: bf16 grads
-    N(0, 2e-3), static scale 1, clip 1.0, prior moments. offset16 = 0: the
-    8-wave kernel (a grid of at most min(2^23, (2^32 - 1) / 512) = 8,388,607
-    blocks of one 1024-element tile, so its second round starts at element
-    8,589,933,568 and holds one whole and one partial tile); 4: the 16-bit
-    buffers start 8 bytes into their allocations, which takes the 4-wave
-    kernel (at most 2^23 blocks of two 256-element tiles: second round from
-    element 2^32). Sampled elements (random, both ends, and around the first
-    tiles of each kernel's second round) against the oracle; the sum of
-    squares against the oracle's."""
+    N(0, 2e-3), static scale 1, clip 1.0, prior moments. The grid holds at
+    most min(2^23, (2^32 - 1) / 512) = 8,388,607 blocks of one 1024-element
+    tile, so the second round starts at element 8,589,933,568 and holds one
+    whole and one partial tile. offset16 = 0: 16-bit buffers 16-byte aligned
+    (16-byte 16-bit accesses); 4: they start 8 bytes into their allocations
+    (the 8-byte form). Sampled elements (random, both ends, and around the
+    first tiles of the second round) against the oracle; the sum of squares
+    against the oracle's."""
     from workloads.device import fill_normal_
     n = (1 << 33) + 1003
     say("AdamW beyond the grid cap: n =", n, "16-bit offset", offset16)
@@ -623,9 +622,8 @@ def test_adam_step_beyond_the_grid_cap(offset16):
     out = oraw[offset16:]
     rng = np.random.default_rng(134)
     idx = [rng.integers(0, n, 65536), np.arange(0, 64), np.arange(n - 1100, n)]
-    cap = lambda threads: min(1 << 23, ((1 << 32) - 1) // threads)  # noqa: E731  (blocks per launch)
-    for wrap in (cap(512) * 1024, cap(256) * 2 * 256):
-        idx.append(np.arange(wrap - 600, min(n, wrap + 600)))
+    wrap = min(1 << 23, ((1 << 32) - 1) // 512) * 1024  # blocks per launch x elements per block
+    idx.append(np.arange(wrap - 600, min(n, wrap + 600)))
     idx = np.concatenate(idx)
     idx = torch.from_numpy(np.unique(idx).astype(np.int64)).cuda()
     P0, M0, V0 = master[idx].cpu().numpy(), m[idx].cpu().numpy(), v[idx].cpu().numpy()

@@ -123,7 +123,7 @@ def test_adam_step_misaligned_buffers(n, gdt):
 @pytest.mark.parametrize("gdt,pdt", [("fp16", "fp16"), ("bf16", "bf16"), ("fp32", "bf16")])
 def test_adam_step_8_byte_aligned_16bit_buffers(n, gdt, pdt):
     """16-bit buffers 8- but not 16-byte aligned (fp32 arrays 16-byte aligned):
-    the 4-wave tile path instead of the 8-wave one."""
+    the AdamW kernel's 8-byte form of its 16-bit accesses."""
     say("adam 16-bit buffers at 8-byte alignment n=%d grads=%s params=%s" % (n, gdt, pdt))
     hp = O.AdamW()
     g, p, m, v = _inputs(n, gdt, 57 + n)

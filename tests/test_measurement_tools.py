@@ -15,7 +15,7 @@ sys.path.insert(0, ROOT)
 
 from zero_sharded_mixed_tensor_amd import profiling as P  # noqa: E402
 
-ADAM = "void zds::adam_tile_kernel<1, 1, true>(zds::AdamArgs)"
+ADAM = "void zds::adam_wide_kernel<1, 1, true, 16>(zds::AdamArgs)"
 COPY = "__amd_rocclr_copyBuffer"
 
 
@@ -41,7 +41,7 @@ def test_trace_summary_skips_warm_up_launches(tmp_path):
     _write(os.path.join(d, "x", "bench_kernel_trace.csv"), ["Kernel_Name", "Start_Timestamp", "End_Timestamp"],
            rows)
     out = P.trace_summary(d, "cmd --flag", skip=2)
-    line = [ln for ln in out.splitlines() if ln.startswith("| adam_tile_kernel<1, 1, true>")][0]
+    line = [ln for ln in out.splitlines() if ln.startswith("| adam_wide_kernel<1, 1, true, 16>")][0]
     cells = [c.strip() for c in line.strip("|").split("|")]
     assert cells[1] == "5" and cells[2] == "3.00" and cells[3] == "2.00" and cells[4] == "15.0"
     assert "    cmd --flag" in out
@@ -58,18 +58,18 @@ def test_counters_scale_by_the_calibration_copy(tmp_path, monkeypatch):
     _write(os.path.join(wd, "bench_counter_collection.csv"), hdr,
            [[COPY, "WRITE_SIZE", gib_kib], [ADAM, "WRITE_SIZE", 14.0], [ADAM, "WRITE_SIZE", 14.0]])
     out = P.counters_summary(fd, wd, ["c1", "c2"], "wl", params)
-    line = [ln for ln in out.splitlines() if ln.startswith("| adam_tile_kernel")][0]
+    line = [ln for ln in out.splitlines() if ln.startswith("| adam_wide_kernel")][0]
     cells = [c.strip() for c in line.strip("|").split("|")]
     # read 7 KiB x 2 = 14336 B, written 14 KiB = 14336 B per launch
     assert cells[1] == "2" and cells[4] == "14.336" and cells[5] == "14.336" and cells[6] == "28672"
     assert "scaled by 2.0000" in out and "by 1.0000" in out
     path = tmp_path / "summary.md"
     path.write_text(out)
-    assert P.traffic_from_summary(str(path), "adam_tile_kernel") == 28672
+    assert P.traffic_from_summary(str(path), "adam_wide_kernel") == 28672
     # a changed source invalidates the figure
     monkeypatch.setattr(P, "kernel_source_hash", lambda k: "0" * 16)
-    assert P.traffic_from_summary(str(path), "adam_tile_kernel") is None
-    assert P.traffic_from_summary(str(tmp_path / "missing.md"), "adam_tile_kernel") is None
+    assert P.traffic_from_summary(str(path), "adam_wide_kernel") is None
+    assert P.traffic_from_summary(str(tmp_path / "missing.md"), "adam_wide_kernel") is None
 
 
 def test_counters_need_the_calibration_copy(tmp_path):

@@ -38,11 +38,12 @@
 // out; a wave's two accesses back to back, or only its loads or only its
 // stores one at a time, were slower than the 2-tile kernel (-0.7, -2.0,
 // -2.9 %), and so were 2048-element tiles (4 accesses per wave, -1.6 %).
-// adam_tile_kernel, a 4-wave form with 256-element tiles and 512-byte 16-bit
-// accesses (2 tiles per block), remains the path for 16-bit buffers that are
-// 8- but not 16-byte aligned. In both kernels the wave's role index is made
-// wave-uniform (readfirstlane), so role branches, array bases and tile
-// counters are scalar.
+// 16-bit buffers that are 8- but not 16-byte aligned take the same kernel
+// with 8-byte 16-bit accesses (two 512-byte wave accesses per half tile;
+// wave 7's two loads of the second half are in flight together); that form
+// replaced a 4-wave kernel with 256-element tiles. The
+// wave's role index is made wave-uniform (readfirstlane), so role branches,
+// array bases and tile counters are scalar.
 //
 // The update's instruction count showed in the bandwidth of the earlier,
 // unpipelined kernels, where a block's update phase was time with nothing in
@@ -65,11 +66,9 @@
 #include "zds_internal.h"
 
 namespace {
-// Consecutive tiles per block in the 4-wave kernel (1 and 3 measured slower).
-constexpr int kTilesPerBlock = 2;
 // Threads per block of the element-wise kernel.
 constexpr int kScalarBlock = 256;
-// Upper bound on the tile kernels' grids (blocks loop over the tiles beyond it).
+// Upper bound on the tile kernel's grid (blocks loop over the tiles beyond it).
 constexpr int64_t kTileGridCap = int64_t(1) << 23;
 }  // namespace
 
@@ -143,98 +142,6 @@ __device__ __forceinline__ void adam_elem(float x, const ElemConsts &c, float &p
 __device__ __forceinline__ void memory_phase() { __builtin_amdgcn_s_setprio(3); }
 __device__ __forceinline__ void update_phase() { __builtin_amdgcn_s_setprio(0); }
 
-// Wave-specialised variant. A block of 4 waves owns a tile of 64 quads (256
-// elements). Wave 0 moves the master tile, wave 1 m, wave 2 v and wave 3 the
-// grad tile in and the 16-bit param tile out, each with one contiguous
-// wave-wide access per direction; the tiles meet in LDS, where each of the
-// 256 threads updates one element. Every wave thus issues one load and one
-// store instead of four of each.
-template <int GD, int PD, bool WRITE_OUT>
-__global__ void __launch_bounds__(256) adam_tile_kernel(const zds_step_scalars *__restrict__ sc,
-                                                        const void *__restrict__ g, float *__restrict__ p,
-                                                        float *__restrict__ m, float *__restrict__ v,
-                                                        void *__restrict__ out, int64_t n) {
-  __shared__ f32x4 sp[64], sm[64], sv[64];
-  __shared__ f32x4 sgf[GD == ZDS_FP32 ? 64 : 1];
-  __shared__ u32x2 s16[64];  // 16-bit grads in, then the 16-bit params out
-  const AdamArgs a{sc, g, p, m, v, out, n};
-  if (sc->overflow) return;
-  const ElemConsts c = load_consts(sc);
-  const int lane = threadIdx.x & 63;
-  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: scalar role branches
-  const int64_t quads = a.n >> 2;
-  // Wave w reads and writes LDS buffer w in the load and store phases and
-  // all threads touch every buffer in the update phase, which sits between
-  // the two barriers; so a wave may start the next tile's load right after
-  // its own store without a third barrier.
-  const int64_t ntiles = (quads + 63) >> 6;
-  for (int64_t it = static_cast<int64_t>(blockIdx.x) * kTilesPerBlock; it < ntiles;
-       it += static_cast<int64_t>(gridDim.x) * kTilesPerBlock)
-  for (int64_t tile = it; tile < it + kTilesPerBlock && tile < ntiles; ++tile) {  // uniform per block
-    const int64_t q0 = tile * 64;
-    const int64_t q = q0 + lane;
-    const bool ok = q < quads;
-    memory_phase();
-    if (w == 0) {
-      if (ok) sp[lane] = ld_stream(reinterpret_cast<const f32x4 *>(a.p) + q);
-    } else if (w == 1) {
-      if (ok) sm[lane] = ld_stream(reinterpret_cast<const f32x4 *>(a.m) + q);
-    } else if (w == 2) {
-      if (ok) sv[lane] = ld_stream(reinterpret_cast<const f32x4 *>(a.v) + q);
-    } else if (ok) {
-      if (GD == ZDS_FP32)
-        sgf[lane] = ld_stream(static_cast<const f32x4 *>(a.g) + q);
-      else
-        s16[lane] = ld_stream(static_cast<const u32x2 *>(a.g) + q);
-    }
-    update_phase();
-    __syncthreads();
-    const int t = threadIdx.x;
-    if (q0 + (t >> 2) < quads) {
-      float *fp = reinterpret_cast<float *>(sp);
-      float *fm = reinterpret_cast<float *>(sm);
-      float *fv = reinterpret_cast<float *>(sv);
-      uint16_t *h = reinterpret_cast<uint16_t *>(s16);
-      float x;
-      if (GD == ZDS_FP32) {
-        x = reinterpret_cast<const float *>(sgf)[t];
-      } else {
-        const uint32_t b = h[t];
-        x = GD == ZDS_BF16 ? __uint_as_float(b << 16) : __half2float(__ushort_as_half(static_cast<unsigned short>(b)));
-      }
-      float p = fp[t], m = fm[t], v = fv[t];
-      adam_elem(x, c, p, m, v);
-      fp[t] = p;
-      fm[t] = m;
-      fv[t] = v;
-      if (WRITE_OUT) h[t] = narrow1<PD>(p);
-    }
-    __syncthreads();
-    memory_phase();
-    if (w == 0) {
-      if (ok) st_stream(reinterpret_cast<f32x4 *>(a.p) + q, sp[lane]);
-    } else if (w == 1) {
-      if (ok) st_stream(reinterpret_cast<f32x4 *>(a.m) + q, sm[lane]);
-    } else if (w == 2) {
-      if (ok) st_stream(reinterpret_cast<f32x4 *>(a.v) + q, sv[lane]);
-    } else if (WRITE_OUT && ok) {
-      st_stream(static_cast<u32x2 *>(a.out) + q, s16[lane]);
-    }
-    update_phase();
-  }
-  // Ragged tail: the last n % 4 elements, one per lane of block 0.
-  const int64_t tail0 = quads << 2;
-  if (blockIdx.x == 0 && tail0 + threadIdx.x < a.n) {
-    const int64_t e = tail0 + threadIdx.x;
-    float p = a.p[e], m = a.m[e], v = a.v[e];
-    adam_elem(widen1<GD>(a.g, e), c, p, m, v);
-    a.p[e] = p;
-    a.m[e] = m;
-    a.v[e] = v;
-    if (WRITE_OUT) static_cast<uint16_t *>(a.out)[e] = narrow1<PD>(p);
-  }
-}
-
 // Wide wave-specialised variant: one tile of 1024 elements per 8-wave block,
 // in two halves of 512. Waves 0-1 move the master tile, 2-3 m, 4-5 v: wave w
 // holds quarter (w & 1) of each half, one 1 KiB access per half. 16-bit
@@ -295,17 +202,38 @@ __device__ __forceinline__ void wide_update(const ElemConsts &c, WideTile<GD> &s
   if (WRITE_OUT) reinterpret_cast<uint16_t *>(sh.so16)[t] = narrow1<PD>(p);
 }
 
+// The 16-bit accesses of the wide kernel: V16 = 16 bytes per lane (8
+// elements; one 1 KiB wave access per half tile) when the 16-bit buffers are
+// 16-byte aligned, else 8 bytes per lane (4 elements; two 512-byte wave
+// accesses per half tile).
+template <int V16>
+struct Vec16 {
+  typedef u32x4 T;
+};
+template <>
+struct Vec16<8> {
+  typedef u32x2 T;
+};
+
 // One tile. fp32 role (waves 0-5, and 6-7 for fp32 grads): `base` is this
 // wave's array, `lt` its LDS tile. The quads of half h this wave moves are
-// qa + 128 h (qa = 64 (w & 1) + lane).
-template <int GD, int PD, bool WRITE_OUT, bool FULL>
+// qa + 128 h (qa = 64 (w & 1) + lane). 16-bit role (waves 6 and 7): half
+// (w & 1)'s grads and params, as V16-byte pieces j of the tile, j counted
+// in units of V16 / 2 elements.
+template <int GD, int PD, bool WRITE_OUT, bool FULL, int V16>
 __device__ __forceinline__ void wide_tile(const AdamArgs &a, const ElemConsts &c, WideTile<GD> &sh, float *base, int w,
                                           uint32_t tile, int64_t nv) {
+  typedef typename Vec16<V16>::T V;
+  constexpr int E16 = V16 / 2;                 // 16-bit elements per piece
+  constexpr int PH = 512 / E16;                // pieces per half tile: 64 (16 B) or 128 (8 B)
   const int lane = threadIdx.x & 63;
   const uint32_t qa = 64 * (w & 1) + lane;
   const int64_t first = static_cast<int64_t>(tile) * kWideTile;  // first element of the tile
   const int64_t quads = nv >> 2;
-  const int64_t octs = nv >> 3;
+  const int64_t pieces = nv / E16;             // whole V16 pieces of the 16-bit arrays
+  const int64_t p0 = first / E16;              // the tile's first piece
+  V *sg = reinterpret_cast<V *>(sh.sg16);
+  V *so = reinterpret_cast<V *>(sh.so16);
   const bool fp32_role = w < 6 || GD == ZDS_FP32;
   if (fp32_role) {
     f32x4 *lt = w < 6 ? sh.sf[w >> 1] : sh.sgf();
@@ -333,34 +261,49 @@ __device__ __forceinline__ void wide_tile(const AdamArgs &a, const ElemConsts &c
       update_phase();
       return;
     }
-  } else if (w == 6) {  // 16-bit grads of half 0
+  } else if (w == 6) {  // 16-bit grads of half 0, one piece access at a time
     const uint16_t *tg = wave_uniform(static_cast<const uint16_t *>(a.g) + first);
     memory_phase();
-    if (FULL || first / 8 + lane < octs) sh.sg16[lane] = ld_stream_at_once<u32x4>(tg, lane * 16);
+#pragma unroll
+    for (int k = 0; k < PH / 64; ++k) {
+      const int j = 64 * k + lane;
+      if (FULL || p0 + j < pieces) sg[j] = ld_stream_at_once<V>(tg, j * V16);
+    }
     update_phase();
     __syncthreads();
     wide_update<GD, PD, WRITE_OUT, FULL>(c, sh, 0, first, nv);
     __syncthreads();
-  } else {  // w == 7: 16-bit grads of half 1
+  } else {  // w == 7: 16-bit grads of half 1, in flight during the update of half 0
     const uint16_t *tg = wave_uniform(static_cast<const uint16_t *>(a.g) + first);
-    const bool in1 = FULL || first / 8 + 64 + lane < octs;
     memory_phase();
-    u32x4 gb;
-    if (in1) gb = ld_stream_global(reinterpret_cast<const u32x4 *>(tg) + 64 + lane);
+    V gb[PH / 64];
+#pragma unroll
+    for (int k = 0; k < PH / 64; ++k) {
+      const int j = PH + 64 * k + lane;
+      if (FULL || p0 + j < pieces) gb[k] = ld_stream_global(reinterpret_cast<const V *>(tg) + j);
+    }
     update_phase();
     __syncthreads();
     wide_update<GD, PD, WRITE_OUT, FULL>(c, sh, 0, first, nv);
-    if (in1) sh.sg16[64 + lane] = gb;
+#pragma unroll
+    for (int k = 0; k < PH / 64; ++k) {
+      const int j = PH + 64 * k + lane;
+      if (FULL || p0 + j < pieces) sg[j] = gb[k];
+    }
     __syncthreads();
   }
   // waves 6 and 7 from barrier 2 on: 16-bit params of half 0 (wave 6) and
-  // half 1 (wave 7)
+  // half 1 (wave 7), one piece access at a time
   uint16_t *to = wave_uniform(static_cast<uint16_t *>(a.out) + first);
-  const uint32_t o = 64 * (w & 1) + lane;
-  const bool ino = FULL || first / 8 + o < octs;
+  const int j0 = PH * (w & 1) + lane;
   if (w == 6) {
     memory_phase();
-    if (WRITE_OUT && ino) st_stream_at(to, o * 16, sh.so16[o]);
+#pragma unroll
+    for (int k = 0; k < PH / 64; ++k) {
+      if (k > 0) wait_vmem();
+      const int j = j0 + 64 * k;
+      if (WRITE_OUT && (FULL || p0 + j < pieces)) st_stream_at(to, j * V16, so[j]);
+    }
     update_phase();
     wide_update<GD, PD, WRITE_OUT, FULL>(c, sh, 1, first, nv);
     wait_vmem();
@@ -369,12 +312,17 @@ __device__ __forceinline__ void wide_tile(const AdamArgs &a, const ElemConsts &c
     wide_update<GD, PD, WRITE_OUT, FULL>(c, sh, 1, first, nv);
     __syncthreads();
     memory_phase();
-    if (WRITE_OUT && ino) st_stream_at(to, o * 16, sh.so16[o]);
+#pragma unroll
+    for (int k = 0; k < PH / 64; ++k) {
+      if (k > 0) wait_vmem();
+      const int j = j0 + 64 * k;
+      if (WRITE_OUT && (FULL || p0 + j < pieces)) st_stream_at(to, j * V16, so[j]);
+    }
     update_phase();
   }
 }
 
-template <int GD, int PD, bool WRITE_OUT>
+template <int GD, int PD, bool WRITE_OUT, int V16>
 __global__ void __launch_bounds__(512) adam_wide_kernel(const zds_step_scalars *__restrict__ sc,
                                                         const void *__restrict__ g, float *__restrict__ p,
                                                         float *__restrict__ m, float *__restrict__ v,
@@ -398,9 +346,9 @@ __global__ void __launch_bounds__(512) adam_wide_kernel(const zds_step_scalars *
   // reads before that tile's barrier 1.
   for (uint32_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {  // uniform per block
     if (tile < full)
-      wide_tile<GD, PD, WRITE_OUT, true>(a, c, sh, base, w, tile, nv);
+      wide_tile<GD, PD, WRITE_OUT, true, V16>(a, c, sh, base, w, tile, nv);
     else
-      wide_tile<GD, PD, WRITE_OUT, false>(a, c, sh, base, w, tile, nv);
+      wide_tile<GD, PD, WRITE_OUT, false, V16>(a, c, sh, base, w, tile, nv);
   }
   // Ragged tail: the last n % 8 elements, one per lane of block 0.
   if (blockIdx.x == 0 && nv + threadIdx.x < n) {
@@ -464,18 +412,9 @@ static int resident_blocks_per_cu(K kernel) {
   return cached;
 }
 
-// One block per kTilesPerBlock tiles of `tile` elements, at most
-// max_blocks(threads) (a dispatch holds fewer than 2^32 work-items) and
-// kTileGridCap; larger arrays loop over the tiles.
-static uint32_t tile_grid(int64_t elems, int64_t tile, int threads) {
-  int64_t g = ((elems + tile - 1) / tile + kTilesPerBlock - 1) / kTilesPerBlock;
-  if (g < 1) g = 1;
-  if (g > max_blocks(threads)) g = max_blocks(threads);
-  if (g > kTileGridCap) g = kTileGridCap;
-  return static_cast<uint32_t>(g);
-}
-
-// One block per kWideTile elements, capped like tile_grid.
+// One block per kWideTile elements, at most max_blocks(512) (a dispatch
+// holds fewer than 2^32 work-items) and kTileGridCap; larger arrays loop
+// over the tiles.
 static uint32_t wide_grid(int64_t elems) {
   int64_t g = (elems + kWideTile - 1) / kWideTile;
   if (g < 1) g = 1;
@@ -487,11 +426,11 @@ static uint32_t wide_grid(int64_t elems) {
 template <int GD, int PD, bool WO>
 static void launch_one(bool vec, bool vec16, hipStream_t s, const AdamArgs &a) {
   if (vec16) {
-    hipLaunchKernelGGL((adam_wide_kernel<GD, PD, WO>), dim3(wide_grid(a.n & ~int64_t(7))), dim3(512), 0, s, a.sc,
-                       a.g, a.p, a.m, a.v, a.out, a.n);
+    hipLaunchKernelGGL((adam_wide_kernel<GD, PD, WO, 16>), dim3(wide_grid(a.n & ~int64_t(7))), dim3(512), 0, s,
+                       a.sc, a.g, a.p, a.m, a.v, a.out, a.n);
   } else if (vec) {
-    hipLaunchKernelGGL((adam_tile_kernel<GD, PD, WO>), dim3(tile_grid(a.n & ~int64_t(3), 256, 256)), dim3(256), 0,
-                       s, a.sc, a.g, a.p, a.m, a.v, a.out, a.n);
+    hipLaunchKernelGGL((adam_wide_kernel<GD, PD, WO, 8>), dim3(wide_grid(a.n & ~int64_t(7))), dim3(512), 0, s,
+                       a.sc, a.g, a.p, a.m, a.v, a.out, a.n);
   } else {
     int64_t g = (a.n + kScalarBlock - 1) / kScalarBlock;
     const int64_t cap = static_cast<int64_t>(device_cu_count()) *

@@ -103,26 +103,33 @@ __device__ __forceinline__ T *wave_uniform(T *p) {
   const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(u >> 32));
   return reinterpret_cast<T *>((static_cast<uint64_t>(hi) << 32) | lo);
 }
-// The same 16-byte streaming store at a wave-uniform base plus a 32-bit
-// per-lane byte offset (the scalar-base address form: the base stays in
-// scalar registers and a loop over tiles advances it with scalar adds).
+// The same 16- or 8-byte streaming store at a wave-uniform base plus a
+// 32-bit per-lane byte offset (the scalar-base address form: the base stays
+// in scalar registers and a loop over tiles advances it with scalar adds).
 template <typename T>
 __device__ __forceinline__ void st_stream_at(void *base, uint32_t byte_off, T v) {
-  static_assert(sizeof(T) == 16, "16-byte stores only");
-  asm volatile("global_store_dwordx4 %0, %1, %2 sc0 sc1 nt\n\ts_nop 1" : : "v"(byte_off), "v"(v), "s"(base) : "memory");
+  static_assert(sizeof(T) == 16 || sizeof(T) == 8, "16- or 8-byte stores only");
+  if constexpr (sizeof(T) == 16)
+    asm volatile("global_store_dwordx4 %0, %1, %2 sc0 sc1 nt\n\ts_nop 1" : : "v"(byte_off), "v"(v), "s"(base) : "memory");
+  else
+    asm volatile("global_store_dwordx2 %0, %1, %2 sc0 sc1 nt" : : "v"(byte_off), "v"(v), "s"(base) : "memory");
 }
-// A 16-byte streaming load in the same address form that returns only once
-// the data has arrived (the wait is part of the same instruction sequence), so
-// that a wave issuing several of them has one load in flight at a time.
+// A 16- or 8-byte streaming load in the same address form that returns only
+// once the data has arrived (the wait is part of the same instruction
+// sequence), so that a wave issuing several of them has one load in flight at
+// a time.
 template <typename T>
 __device__ __forceinline__ T ld_stream_at_once(const void *base, uint32_t byte_off) {
-  static_assert(sizeof(T) == 16, "16-byte loads only");
+  static_assert(sizeof(T) == 16 || sizeof(T) == 8, "16- or 8-byte loads only");
   T r;
-  asm volatile("global_load_dwordx4 %0, %1, %2 nt\n\ts_waitcnt vmcnt(0)" : "=v"(r) : "v"(byte_off), "s"(base) : "memory");
+  if constexpr (sizeof(T) == 16)
+    asm volatile("global_load_dwordx4 %0, %1, %2 nt\n\ts_waitcnt vmcnt(0)" : "=v"(r) : "v"(byte_off), "s"(base) : "memory");
+  else
+    asm volatile("global_load_dwordx2 %0, %1, %2 nt\n\ts_waitcnt vmcnt(0)" : "=v"(r) : "v"(byte_off), "s"(base) : "memory");
   return r;
 }
-// A 16-byte streaming load through a global-address-space pointer, so that it
-// is a global (not a flat) load: a flat load also counts against the LDS
+// A streaming load through a global-address-space pointer, so that it is a
+// global (not a flat) load: a flat load also counts against the LDS
 // counter, and the wait for LDS before a barrier would then wait for it too.
 template <typename T>
 __device__ __forceinline__ T ld_stream_global(const T *p) {

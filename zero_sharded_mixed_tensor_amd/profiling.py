@@ -28,7 +28,6 @@ ROOT = os.path.dirname(PKG)
 
 # kernel name prefix -> sources that define it
 KERNEL_SOURCES = {
-    "adam_tile_kernel": ["csrc/zds_adam.hip", "csrc/zds_device.h", "csrc/zds_internal.h", "build.py"],
     "adam_wide_kernel": ["csrc/zds_adam.hip", "csrc/zds_device.h", "csrc/zds_internal.h", "build.py"],
     "norm_stage1": ["csrc/zds_norm.hip", "csrc/zds_device.h", "csrc/zds_internal.h", "build.py"],
     "accumulate_kernel": ["csrc/zds_accumulate.hip", "csrc/zds_device.h", "csrc/zds_internal.h", "build.py"],
