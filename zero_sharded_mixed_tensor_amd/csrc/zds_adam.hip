@@ -55,7 +55,9 @@
 // raise their scheduling priority while they issue loads and stores and drop
 // it for the update, so that a block's memory accesses are not queued behind
 // other blocks' arithmetic on the same SIMD: +0.3 to 1 % in four A/B runs
-// then, neutral to -0.3 % on the unpipelined 1024-element tile.
+// then, neutral to -0.3 % on the unpipelined 1024-element tile and neutral on
+// the pipelined one (3.623-3.626 ms against 3.623-3.628 without it, four
+// rounds on one box).
 //
 // The step constants (lr / (1 - beta1^t), sqrt(1 - beta2^t) and its float64
 // reciprocal, 1 - lr*wd, the 1 - beta values) are derived once per call by a
