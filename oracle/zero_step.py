@@ -183,7 +183,9 @@ def flatten_accumulate(srcs, src_dtype, entries, acc, overwrite):
 # the scale is lowered; §4.4 a NaN loss points at the fp16 setup. Clipping by
 # the global norm is not on the pages: it is the conventional
 # coef = max_norm / (norm + 1e-6), applied only when norm > max_norm (reading;
-# the 1e-6 is unpinned). Accumulated grads are averaged over the K
+# pinned to a library's global-norm clip, which agrees except within 1e-6
+# below max_norm, where it scales by slightly less than 1 and this leaves
+# the grads alone). Accumulated grads are averaged over the K
 # micro-batches ([csdn] §2.3: the accumulated grad stands for the big batch).
 # ---------------------------------------------------------------------------
 

@@ -48,6 +48,16 @@ MUTANTS = {
  "onebit_err_sign": ("np.where(pos[a:b], c[a:b] - s, c[a:b] + s)", "np.where(pos[a:b], c[a:b] + s, c[a:b] - s)"),
  "onebit_neg_zero": ("    pos = c >= np.float32(0.0)\n", "    pos = ~np.signbit(c)\n"),
  "onebit_dec_sign": ("return np.where(bit == 1, np.float32(1.0), np.float32(-1.0))", "return np.where(bit == 1, np.float32(-1.0), np.float32(1.0))"),
+ "clip_no_eps": ("coef = float(max_norm) / (norm + 1e-6)", "coef = float(max_norm) / norm"),
+ "clip_at_or_below_max": ("if max_norm > 0.0 and norm > max_norm:", "if max_norm > 0.0 and norm >= max_norm * 0.999:"),
+ "norm_sqrt_of_quotient": ("norm = math.sqrt(sumsq) / sk", "norm = math.sqrt(sumsq / sk)"),
+ "grad_scale_no_K": ("grad_scale = np.float32(coef / sk)", "grad_scale = np.float32(coef / float(scale))"),
+ "bc2_no_sqrt": ("c[\"bc2_sqrt\"] = np.float32(math.sqrt(1.0 - p2))", "c[\"bc2_sqrt\"] = np.float32(1.0 - p2)"),
+ "m_unscaled_grad": ("m = c[\"b1\"] * m + c[\"omb1\"] * g", "m = c[\"b1\"] * m + c[\"omb1\"] * widen(x, dtype)"),
+ "decay_after_update": ("    p = master * c[\"decay\"]\n    p = p - c[\"step_size\"] * (m / denom)",
+                        "    p = master - c[\"step_size\"] * (m / denom)\n    p = p * c[\"decay\"]"),
+ "fp16_truncate": ("return p.astype(np.float16).view(np.uint16)", "return (p.view(np.uint32) >> np.uint32(13)).astype(np.uint16)"),
+ "bf16_nan_rounded": ("r = np.where(nan, (u >> np.uint64(16)) | np.uint64(0x40), r)", "r = r"),
  "beta_pow_skip": ("st = replace(st, t=st.t + 1, beta1_pow=st.beta1_pow * b1, beta2_pow=st.beta2_pow * b2,", "st = replace(st, t=st.t + 1, beta1_pow=st.beta1_pow * b2, beta2_pow=st.beta2_pow * b1,"),
 }
 

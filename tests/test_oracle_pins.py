@@ -214,6 +214,9 @@ def test_narrow_bf16_exact_rounding():
     pats = [(int(h) << 16) | int(l) for h in his for l in los]
     pats += [int(x) for x in rng.integers(0, 2 ** 32, 4000, dtype=np.uint64)]
     pats += [0x7F7F7FFF, 0x7F7F8000, 0x7F7F8001, 0xFF7F8000, 0x00008000, 0x00018000]
+    # NaNs whose payload lies only in the dropped half, or fills it: a
+    # conversion of a NaN is a NaN (rounding them like numbers gives inf or -0)
+    pats += [0x7F800001, 0xFF800001, 0x7F807FFF, 0x7F80FFFF, 0x7FBFFFFF, 0x7FFFFFFF, 0xFFFFFFFF]
     arr = np.array(pats, dtype=np.uint32)
     got = O.narrow(arr.view(np.float32), O.BF16)
     for p, g in zip(pats, got):
@@ -325,6 +328,33 @@ def test_clip_brings_norm_to_max():
     # below the threshold nothing is clipped
     _, coef2, gs2 = O.clip_scalars(s, S, K, 10 * norm)
     assert coef2 == 1.0 and gs2 == np.float32(1.0 / (S * K))
+
+
+def test_clip_matches_the_library_global_norm_clip():
+    """The conventional global-norm clip as PyTorch implements it
+    (torch.nn.utils.clip_grad_norm_ multiplies the grads by
+    min(1, max_norm / (norm + 1e-6))) against clip_scalars: the norm and the
+    coefficient agree, the 1e-6 included, away from the 1e-6-wide band just
+    below max_norm where the two readings differ (clip_scalars leaves grads
+    whose norm is at most max_norm unscaled)."""
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(11)
+    S, K = 2.0 ** 12, 4
+    for max_norm in (0.3, 1.0, 5.0):
+        for ratio in (0.25, 0.9, 0.9995, 1.01, 1.5, 2.0, 10.0, 1000.0):
+            base = rng.standard_normal(3000)
+            g = base / np.linalg.norm(base) * max_norm * ratio
+            x = (g * S * K).astype(np.float32)  # the raw grads the step sees
+            norm, coef, gs = O.clip_scalars(O.sum_of_squares(x, O.FP32), S, K, max_norm)
+            gt = torch.from_numpy(x.astype(np.float64) / (S * K))
+            p = torch.zeros_like(gt, requires_grad=True)
+            p.grad = gt.clone()
+            total = float(torch.nn.utils.clip_grad_norm_([p], max_norm))
+            nz = gt != 0
+            factor = float((p.grad[nz] / gt[nz]).mean())
+            assert abs(total - norm) <= 1e-12 * norm, (max_norm, ratio)
+            assert abs(coef - factor) <= 1e-12 * factor, (max_norm, ratio, coef, factor)
+            assert gs == np.float32(coef / (S * K))
 
 
 def test_overflow_and_norm_flags():
