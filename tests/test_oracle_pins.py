@@ -531,6 +531,29 @@ def test_scaler_brute_force_all_sequences():
                     assert st.t == len(seq) - sum(seq)
 
 
+def test_scaler_hysteresis1_matches_the_library_amp_scaler():
+    """With hysteresis 1 the dynamic scaler is the one PyTorch's AMP grad
+    scaler runs (torch._amp_update_scale_: halve on an overflow and reset the
+    clean-step count; double after `window` clean steps): scale and count
+    agree on random overflow sequences, the floor kept out of reach."""
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(12)
+    # (window, overflow probability) pairs whose random walks stay between
+    # the floor and the 2^127 cap
+    for W, p_ovf in ((1, 0.4), (1, 0.5), (1, 0.6), (2, 0.2), (2, 0.35), (5, 0.05), (5, 0.12), (13, 0.02),
+                     (13, 0.06)):
+        st = O.scaler_init(initial_scale_power=16, window=W, hysteresis=1, min_scale=2.0 ** -100)
+        scale = torch.tensor([2.0 ** 16])
+        tracker = torch.tensor([0], dtype=torch.int32)
+        found = torch.tensor([0.0])
+        for f in (rng.random(200) < p_ovf).astype(int):
+            st = O.scaler_update(st, int(f), 0.9, 0.999)
+            assert st.min_scale < st.scale < 2.0 ** 127  # neither bound binds here
+            found.fill_(float(f))
+            torch._amp_update_scale_(scale, tracker, found, 2.0, 0.5, W)
+            assert st.scale == float(scale) and st.good_steps == int(tracker), (W, p_ovf)
+
+
 def test_scaler_static_and_floor():
     st = O.scaler_init(dynamic=False, static_scale=1.0)
     for f in (1, 0, 1, 1, 0):
