@@ -13,6 +13,9 @@ that hold at any size.
   16-bit params within 1 ulp. The next rows at full size use sampled
   elements (65,536 seeded positions plus the first and last element of
   every table entry).
+* The 8-peer Stage-2 intake on the 7B shard: every element of the shard
+  gradient against the oracle's in-order sum (bit-exact), then the whole
+  update as above.
 * The norm: the oracle's overflow flag and sum of squares over the whole
   flat buffer, chunk by chunk on host threads; the GPU's sum must agree
   within 1e-12 relative, the oracle derives the clip scalars itself and the
@@ -20,8 +23,7 @@ that hold at any size.
 * Flags, skips and the loss-scale trajectory are compared exactly.
 The Stage-1 shards run the bench's step (the norm fused into the flatten or
 the last accumulate call); the whole-7B run uses the separate norm pass.
-The next rows at the 7B shard size: the 8-peer Stage-2 intake, the 1-bit
-codec on sampled chunks, one offloaded step (host optimizer state) on
+The other next rows at the 7B shard size: the 1-bit codec on sampled chunks, one offloaded step (host optimizer state) on
 sampled elements, and a 10.1 GB checkpoint round trip compared bit for bit.
 """
 
@@ -382,10 +384,20 @@ def test_llama65b_stage1_shard_bf16():
     plan.close()
 
 
+def _cmp_reduce_chunk(a, parts, got):
+    want = O.reduce_peer_slices(parts, "bf16", None, "fp32", accumulate=False)
+    bad = np.nonzero(got.view(np.uint32) != want.view(np.uint32))[0]
+    assert bad.size == 0, "intake differs from the oracle at %d (%d elements)" % (a + int(bad[0]), bad.size)
+
+
 def test_llama7b_stage2_intake_eight_peers():
     """Stage 2 at N = 8 on the 7B shard: the rank sums 8 peers' bf16 copies of
     its 842M-element slice into an fp32 shard gradient, then steps on it with
-    the mean over the peers (accum_steps = 8)."""
+    the mean over the peers (accum_steps = 8). Every element: the oracle's
+    in-order sum of the 8 peers (bit-exact), its flag, sum and clip scalars
+    over the whole shard gradient, and its update of the whole pre-step
+    state."""
+    from concurrent.futures import ThreadPoolExecutor
     say("full size: Llama-7B Stage-2 intake, 8 peers")
     numels, plan, ents, n, srcs, master, m, v = _setup_shard(llama_7b_tensors(), 8, 0, "bf16", 2e-3, True, 61)
     del srcs
@@ -395,21 +407,25 @@ def test_llama7b_stage2_intake_eight_peers():
     out = torch.empty(n, dtype=torch.bfloat16, device="cuda")
     st = ShardStep(n, zds.hparams(), zds.scaler_config(dynamic=False, static_scale=1.0), max_norm=1.0,
                    accum_steps=8, t0=1, beta1_pow0=B1, beta2_pow0=B2)
-    idx = _sample_index(n, ents)
-    P0, M0, V0 = master[idx].cpu().numpy(), m[idx].cpu().numpy(), v[idx].cpu().numpy()
+    pre = (master.clone(), m.clone(), v.clone())
     zds.zds_reduce_peer_slices(peers, acc, zds.ZDS_OVERWRITE)
     st.step(acc, master, m, v, out)
     torch.cuda.synchronize()
-    psamp = [_h16(pk[idx]) for pk in peers]
-    want_acc = O.reduce_peer_slices(psamp, "bf16", None, "fp32", accumulate=False)
-    assert (acc[idx].cpu().numpy().view(np.uint32) == want_acc.view(np.uint32)).all()
-    acc_h = acc.cpu().numpy()
-    osc = _oracle_scalars(O.sum_of_squares(acc_h, "fp32"), 1.0, 8, 1.0, O.overflow_flag(acc_h, "fp32"))
-    del acc_h
+    futs = []
+    with ThreadPoolExecutor(POOL) as ex:
+        for k, a in enumerate(range(0, n, CHUNK)):
+            b = min(n, a + CHUNK)
+            _bounded(ex, futs, _cmp_reduce_chunk, a, [_h16(pk[a:b]) for pk in peers], acc[a:b].cpu().numpy())
+            if k % 16 == 15:
+                say("  intake: %d of %d elements compared" % (b, n))
+        for f in futs:
+            f.result()
+    ovf, sumsq = _oracle_flag_and_sumsq(acc, "fp32")
+    osc = _oracle_scalars(sumsq, 1.0, 8, 1.0, ovf)
     _compare_scalars(st.read_scalars(), osc)
     ost = O.scaler_init(dynamic=False, static_scale=1.0, t=1, beta1_pow=B1, beta2_pow=B2)
-    want = _oracle_update(want_acc, "fp32", osc, ost, P0, M0, V0, "bf16")
-    _compare_samples("7B stage-2 intake", idx, master, m, v, out, want)
+    _compare_whole("7B stage-2 intake", acc, "fp32", osc, ost, pre, master, m, v, out, "bf16")
+    del pre
     # the intake with the norm fused in: the same shard gradient, and the
     # oracle's scalars of it (its ~822K block partials take two folding levels)
     say("full size: Llama-7B Stage-2 intake with the norm fused in")
