@@ -247,7 +247,8 @@ size_t zds_workspace_bytes(int64_t n);
  * overflow = 1 iff some element is inf or NaN ([csdn] §2.2: overflow under the
  * loss scale is detected). sumsq = sum of float64(x)^2 in a fixed order
  * (run-to-run identical for the same n). norm, clip_coef and grad_scale are
- * computed in float64 and rounded once to fp32. */
+ * computed in float64 and rounded once to fp32. On overflow the step is
+ * skipped: norm = inf, clip_coef = 1 and grad_scale = 0. */
 zds_status zds_overflow_and_norm(const void *grads, zds_dtype dtype, int64_t n,
                                  int32_t accum_steps, float max_norm,
                                  const zds_step_state *state_dev, zds_step_scalars *out_dev,

@@ -366,6 +366,11 @@ def test_overflow_and_norm_flags():
     assert O.overflow_and_norm(x.view(np.uint16), O.FP16, 1.0, 1, 1.0)["overflow"] == 1
     x[37] = 65504
     assert O.overflow_and_norm(x.view(np.uint16), O.FP16, 1.0, 1, 1.0)["overflow"] == 0
+    # an overflowing step is skipped: it reports an infinite norm, no
+    # clipping and a grad factor of 0 (nothing may be applied)
+    x[37] = -np.inf
+    r = O.overflow_and_norm(x.view(np.uint16), O.FP16, 1.0, 1, 1.0)
+    assert r["norm"] == np.inf and r["coef"] == 1.0 and r["grad_scale"] == 0.0
 
 
 # ---------------------------------------------------------------- accumulation
@@ -567,6 +572,15 @@ def test_scaler_static_and_floor():
     assert st.scale == 1.0 and st.t == 0
 
 
+def test_scaler_growth_saturates_at_2_127():
+    # the scale is an fp32 power of two, so growth stops at the largest one
+    st = O.scaler_init(initial_scale_power=126, window=1)
+    for k in range(3):
+        st = O.scaler_update(st, 0, 0.9, 0.999)
+        assert st.scale == 2.0 ** 127 and st.good_steps == 0
+    assert st.t == 3
+
+
 def test_beta_powers():
     st = O.scaler_init()
     for _ in range(50):
@@ -723,6 +737,31 @@ def test_stage1_concat_invariant():
             assert (cat.view(np.uint32) == full[k].view(np.uint32)).all()
         # padding stays exactly zero
         assert (np.concatenate([o[0] for o in outs])[total:] == 0).all()
+
+
+def test_step_params_are_the_cast_of_the_new_master():
+    # the 16-bit params written by a step are the round-to-nearest cast of the
+    # master values it returns, element for element (checked on enough
+    # elements that some lie within an fp32 ulp of a 16-bit rounding tie)
+    rng = np.random.default_rng(16)
+    n = 400000
+    for gdt, pdt in ((O.FP16, O.FP16), (O.BF16, O.BF16), (O.FP32, O.BF16)):
+        g = (rng.standard_normal(n) * 1e-3).astype(np.float32)
+        x = g if gdt == O.FP32 else O.narrow(g, gdt)
+        master = (rng.standard_normal(n) * 0.05).astype(np.float32)
+        m = (rng.standard_normal(n) * 1e-4).astype(np.float32)
+        v = (rng.standard_normal(n) ** 2 * 1e-7).astype(np.float32)
+        st = O.scaler_init(dynamic=False, t=3, beta1_pow=0.9 ** 3, beta2_pow=0.999 ** 3)
+        r = O.optimizer_step(x, gdt, master, m, v, st, O.AdamW(), 1.0, 1, pdt)
+        p = r[0].view(np.uint32).astype(np.uint64)
+        if pdt == O.FP16:
+            want = r[0].astype(np.float16).view(np.uint16)
+        else:  # nearest bf16, ties to even, from the exact fp32 bits (no NaN here)
+            lo = p & np.uint64(0xFFFF)
+            hi = p >> np.uint64(16)
+            up = (lo > np.uint64(0x8000)) | ((lo == np.uint64(0x8000)) & ((hi & np.uint64(1)) == np.uint64(1)))
+            want = (hi + up.astype(np.uint64)).astype(np.uint16)
+        assert (r[3] == want).all(), (gdt, pdt)
 
 
 def test_overflow_step_leaves_state():
@@ -940,6 +979,35 @@ def test_onebit_error_feedback_telescopes():
         e = e_new
     assert (np.abs(sent + e - T * x.astype(np.float64)) <= bound).all()
     assert np.abs(sent / T - x).max() < np.abs(e).max() / T + 1e-5
+
+
+def test_onebit_decompress_adds_peers_in_order():
+    # 1 + 2^-24 is a tie that rounds to 1 (even), so adding the two small
+    # scales one at a time after the large one leaves 1, while adding the
+    # small ones first gives 1 + 2^-23
+    n = chunk = 4
+    words = np.zeros(64, np.uint32)
+    words[0] = 0xF  # elements 0..3: bits 0..3 of word 0, all positive
+    small = np.float32(2.0 ** -24)
+    pay = [(words, np.array([1.0], np.float32)), (words, np.array([small])), (words, np.array([small]))]
+    assert (O.onebit_decompress(pay, n, chunk, None, False) == np.float32(1.0)).all()
+    assert (O.onebit_decompress(pay[::-1], n, chunk, None, False) == np.float32(1.0 + 2.0 ** -23)).all()
+
+
+def test_onebit_scale_is_the_correctly_rounded_rms():
+    # the scale is sqrt(S / len) for the exact sum of squares S; summing
+    # rounded fp32 squares in fp32 gives another scale on some of these
+    # chunks, which the last assertion makes sure of
+    rng = np.random.default_rng(90)
+    chunk, differ = 1024, 0
+    for _ in range(48):
+        c = (rng.standard_normal(chunk) * 10.0 ** rng.uniform(-3, 3)).astype(np.float32)
+        _, scales, _ = O.onebit_compress(c, np.zeros(chunk, np.float32), chunk)
+        S = sum(Fraction(float(v)) ** 2 for v in c)
+        want = _f32_sqrt_of_fraction(S / chunk)
+        assert scales[0] == want
+        differ += np.float32(math.sqrt(float(np.sum(c * c)) / chunk)) != want
+    assert differ >= 2, differ
 
 
 def test_onebit_decompress_sums_peers_exactly():
