@@ -104,6 +104,47 @@ def test_adam_step_parity(n, gdt, pdt):
     assert st.t == ost.t and st.beta1_pow == ost.beta1_pow and st.last_skip == 0
 
 
+@pytest.mark.parametrize("n", [9, 4099, 3 * 1024 + 512, 65536 * 3 + 13])
+@pytest.mark.parametrize("gdt,pdt", [("fp16", "fp16"), ("fp16", "bf16"), ("bf16", "fp16"), ("bf16", "bf16"),
+                                     ("fp32", "fp16"), ("fp32", "bf16")])
+def test_adam_step_bit_exact(n, gdt, pdt):
+    """Every dtype pair: the kernel performs the oracle's fp32 operations in
+    its order with correctly rounded divide and sqrt, so master/m/v and the
+    16-bit params agree bit for bit (the stated bound elsewhere is 2 ulp /
+    1 ulp; this is the stronger property the kernel has)."""
+    say("adam bit-exact n=%d grads=%s params=%s" % (n, gdt, pdt))
+    hp = O.AdamW()
+    g, p, m, v = _inputs(n, gdt, 3 * n + len(gdt) + 7 * len(pdt))
+    P, M, V, OUT, sc, st, pows = _run_step(g, p, m, v, gdt, pdt, 12, 2, 1.0, hp)
+    oP, oM, oV, oOUT, ost, osc = _oracle_step(g, p, m, v, gdt, pdt, 2.0 ** 12, 2, pows, 1.0, hp)
+    assert sc.grad_scale == osc["grad_scale"]
+    for name, a, b in (("master", P, oP), ("exp_avg", M, oM), ("exp_avg_sq", V, oV)):
+        assert (a.view(np.uint32) == b.view(np.uint32)).all(), (name, assert_state_close(name, a, b, 2))
+    assert (OUT == oOUT).all(), assert_p16_close("params_out", OUT, oOUT, 1)
+
+
+@pytest.mark.parametrize("n", [1, 9, 4099, 3 * 1024 + 512, 65536 * 3 + 13])
+@pytest.mark.parametrize("gdt", ["fp16", "bf16", "fp32"])
+def test_adam_step_without_params_out(n, gdt):
+    """params_out NULL skips the cast (the kernel's no-output form):
+    master/m/v bit for bit against the oracle's update."""
+    say("adam without params_out n=%d grads=%s" % (n, gdt))
+    hp = O.AdamW()
+    g, p, m, v = _inputs(n, gdt, 11 * n + len(gdt))
+    dg, dp, dm, dv = to_dev(g, gdt), to_dev(p, "fp32"), to_dev(m, "fp32"), to_dev(v, "fp32")
+    b1p, b2p = float(np.float32(hp.beta1)), float(np.float32(hp.beta2))
+    cfg = zds.scaler_config(dynamic=True, initial_scale_power=12, window=1000, hysteresis=1, static_scale=1.0)
+    st = ShardStep(n, zds.hparams(hp.lr, hp.beta1, hp.beta2, hp.eps, hp.weight_decay), cfg,
+                   max_norm=1.0, accum_steps=1, t0=1, beta1_pow0=b1p, beta2_pow0=b2p)
+    st.step(dg, dp, dm, dv, None)
+    torch.cuda.synchronize()
+    oP, oM, oV, _, _, osc = _oracle_step(g, p, m, v, gdt, "bf16", 2.0 ** 12, 1, (b1p, b2p), 1.0, hp)
+    assert st.read_scalars().grad_scale == osc["grad_scale"]
+    for name, a, b in (("master", to_host(dp), oP), ("exp_avg", to_host(dm), oM), ("exp_avg_sq", to_host(dv), oV)):
+        assert (a.view(np.uint32) == b.view(np.uint32)).all(), name
+    assert st.read_state().t == 2
+
+
 @pytest.mark.parametrize("n", [1, 9, 4099, 65536 + 3])
 @pytest.mark.parametrize("gdt", ["fp16", "bf16", "fp32"])
 def test_adam_step_misaligned_buffers(n, gdt):
