@@ -145,6 +145,29 @@ def test_adam_step_without_params_out(n, gdt):
     assert st.read_state().t == 2
 
 
+def test_empty_shard_step():
+    """n = 0: the step launches and returns, the scalars are those of an
+    empty sum (no overflow, norm 0, no clipping) and the scaler commits the
+    step like the oracle's."""
+    say("empty shard step")
+    hp = O.AdamW()
+    e32 = torch.empty(0, dtype=torch.float32, device="cuda")
+    g = torch.empty(0, dtype=torch.bfloat16, device="cuda")
+    out = torch.empty(0, dtype=torch.bfloat16, device="cuda")
+    cfg = zds.scaler_config(dynamic=True, initial_scale_power=12, window=2, hysteresis=1, static_scale=1.0)
+    st = ShardStep(0, zds.hparams(), cfg, max_norm=1.0, accum_steps=1, t0=0)
+    ost = O.scaler_init(dynamic=True, initial_scale_power=12, window=2, hysteresis=1)
+    for _ in range(3):
+        st.step(g, e32, e32.clone(), e32.clone(), out)
+        ost = O.optimizer_step(np.zeros(0, np.uint16), O.BF16, np.zeros(0, np.float32), np.zeros(0, np.float32),
+                               np.zeros(0, np.float32), ost, hp, 1.0, 1, O.BF16)[4]
+    torch.cuda.synchronize()
+    sc, dst = st.read_scalars(), st.read_state()
+    assert sc.overflow == 0 and sc.sumsq == 0.0 and float(sc.norm) == 0.0 and float(sc.clip_coef) == 1.0
+    assert dst.t == ost.t == 3 and float(dst.scale) == ost.scale == 2.0 ** 13 and dst.good_steps == ost.good_steps
+    assert dst.beta1_pow == ost.beta1_pow and dst.beta2_pow == ost.beta2_pow
+
+
 @pytest.mark.parametrize("n", [1, 9, 4099, 65536 + 3])
 @pytest.mark.parametrize("gdt", ["fp16", "bf16", "fp32"])
 def test_adam_step_misaligned_buffers(n, gdt):
