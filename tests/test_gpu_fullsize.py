@@ -23,7 +23,10 @@ that hold at any size.
 * Flags, skips and the loss-scale trajectory are compared exactly.
 The Stage-1 shards run the bench's step (the norm fused into the flatten or
 the last accumulate call); the whole-7B run uses the separate norm pass.
-The other next rows at the 7B shard size: the 1-bit codec on sampled chunks, one offloaded step (host optimizer state) on
+The other next rows at the 7B shard size: the 1-bit codec against the
+oracle on sampled chunks and over the whole shard by properties (sign bits,
+one-peer decodes, the new error, the scales against a float64 RMS, the
+8-peer decode as the in-order fp32 sum of one-peer decodes), one offloaded step (host optimizer state) on
 sampled elements, and a 10.1 GB checkpoint round trip compared bit for bit.
 """
 
@@ -484,6 +487,85 @@ def test_llama7b_onebit_codec_shard():
                for pw, ps in peers]
         want = O.onebit_decompress(pay, b - a, chunk, None, False)
         assert (out[a:b].cpu().numpy().view(np.uint32) == want.view(np.uint32)).all(), j
+
+
+def _onebit_bits(words, a, b):
+    """Sign bits of elements [a, b) of a packed 1-bit stream (the library's
+    word layout: bit 4r + i of word 64u + l is element 2048u + 256r + 4l + i),
+    restated with torch index arithmetic."""
+    i = torch.arange(a, b, dtype=torch.int64, device="cuda")
+    wi = 64 * (i // 2048) + (i % 256) // 4
+    bi = (4 * ((i % 2048) // 256) + i % 4).to(torch.int32)
+    return (torch.bitwise_right_shift(words[wi], bi) & 1).bool()
+
+
+def _ulp32(a, b):
+    """|ordered(a) - ordered(b)| of fp32 tensors, in units in the last place."""
+    def ordered(t):
+        u = t.view(torch.int32).to(torch.int64)
+        return torch.where(u < 0, -(u & 0x7FFFFFFF), u)
+    return (ordered(a) - ordered(b)).abs()
+
+
+def test_llama7b_onebit_codec_whole_array_properties():
+    """Every element of the 7B shard (842,301,440 fp32, chunk 2048), by
+    properties that hold at any size. Encode with error feedback: each sign
+    bit is c >= 0 for c = x + e (fp32), the one-peer decode of the message is
+    +-(its chunk's scale) with that sign, the new error is c minus it (one
+    fp32 rounding), and each scale is within 1 ulp of the chunk's RMS from a
+    float64 sum (at most 1 chunk in 1000 differing, as the oracle tests
+    state). Decode of 8 random messages: each one-peer decode is +-scale with
+    the sign of its bit, and the 8-peer decode (and the accumulating form) is
+    their fp32 sum in peer order, bit for bit."""
+    from workloads.device import draw_payload_, fill_normal_
+    say("full size: 1-bit codec properties over the whole Llama-7B shard")
+    n, chunk, S = 842301440, 2048, 1 << 26
+    assert n % chunk == 0 and S % chunk == 0
+    x = fill_normal_(torch.empty(n, dtype=torch.float32, device="cuda"), 2e-3, 171)
+    e = fill_normal_(torch.empty(n, dtype=torch.float32, device="cuda"), 2e-5, 172)
+    c = x + e
+    words, scales = zds.onebit_payload(n, chunk)
+    zds.zds_onebit_compress(x, e, chunk, words, scales)
+    d1 = torch.empty(n, dtype=torch.float32, device="cuda")
+    zds.zds_onebit_decompress([(words, scales)], chunk, d1)
+    torch.cuda.synchronize()
+    del x
+    off = 0
+    for a in range(0, n, S):
+        b = min(n, a + S)
+        bits = _onebit_bits(words, a, b)
+        assert torch.equal(bits, c[a:b] >= 0), a
+        s_el = scales[a // chunk:b // chunk].repeat_interleave(chunk)
+        want = torch.where(bits, s_el, -s_el)
+        assert torch.equal(d1[a:b].view(torch.int32), want.view(torch.int32)), a
+        assert torch.equal(e[a:b].view(torch.int32), (c[a:b] - want).view(torch.int32)), a
+        rms = torch.sqrt(c[a:b].double().view(-1, chunk).square().sum(1) / chunk).float()
+        du = _ulp32(scales[a // chunk:b // chunk], rms)
+        assert int(du.max()) <= 1, a
+        off += int((du > 0).sum())
+    assert off <= (n // chunk) // 1000, off
+    del c, e, d1, words, scales
+    torch.cuda.empty_cache()
+
+    peers = [draw_payload_(*zds.onebit_payload(n, chunk), 1e-3, 180 + k) for k in range(8)]
+    dec = torch.empty(n, dtype=torch.float32, device="cuda")
+    zds.zds_onebit_decompress(peers, chunk, dec)
+    base = fill_normal_(torch.empty(n, dtype=torch.float32, device="cuda"), 1e-2, 190)
+    dacc = base.clone()
+    zds.zds_onebit_decompress(peers, chunk, dacc, zds.ZDS_ACCUMULATE)
+    one = torch.empty(n, dtype=torch.float32, device="cuda")
+    acc = None
+    for k, (w, sc) in enumerate(peers):
+        zds.zds_onebit_decompress([(w, sc)], chunk, one)
+        torch.cuda.synchronize()
+        for a in range(0, n, S):
+            b = min(n, a + S)
+            bits = _onebit_bits(w, a, b)
+            s_el = sc[a // chunk:b // chunk].repeat_interleave(chunk)
+            assert torch.equal(one[a:b].view(torch.int32), torch.where(bits, s_el, -s_el).view(torch.int32)), (k, a)
+        acc = one.clone() if acc is None else acc + one
+    assert torch.equal(dec.view(torch.int32), acc.view(torch.int32))
+    assert torch.equal(dacc.view(torch.int32), (base + acc).view(torch.int32))
 
 
 def test_llama7b_offloaded_shard_one_step():
