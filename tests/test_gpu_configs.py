@@ -101,6 +101,56 @@ def test_tiny_shard_five_steps(inf_at):
     plan.close()
 
 
+def test_tiny_shard_from_ds_config():
+    """The tiny shard stepped with the settings of a DeepSpeed-style JSON
+    block (the tutorial's fp16 block: dynamic scale from 2^16, window 1000,
+    hysteresis 2; AdamW lr 2e-5; clip 1.0) through ShardStep.from_config,
+    against the oracle with the same settings: overflows at steps 2 and 3
+    skip both, and only the second halves the scale."""
+    from zero_sharded_mixed_tensor_amd.config import from_ds_config
+    say("tiny shard from a JSON config")
+    cfg = from_ds_config({"fp16": {"enabled": True, "loss_scale": 0, "loss_scale_window": 1000,
+                                   "initial_scale_power": 16, "hysteresis": 2, "min_loss_scale": 1},
+                          "optimizer": {"type": "AdamW", "params": {"lr": 2e-5, "betas": [0.9, 0.999],
+                                                                   "eps": 1e-8, "weight_decay": 0.01}},
+                          "gradient_clipping": 1.0})
+    numels = [n for _, n in tiny_shard_sizes()]
+    offs, total, master = _flat_master(numels, 64, 0, 1)
+    hp = O.AdamW(lr=cfg.lr, beta1=cfg.beta1, beta2=cfg.beta2, eps=cfg.eps, weight_decay=cfg.weight_decay)
+    plan = zds.zds_plan_create(numels, 64, 0, total)
+    ent = O.shard_entries(numels, 64, 0, total)
+    st = ShardStep.from_config(total, cfg)
+    dP = to_dev(master, "fp32")
+    dM = torch.zeros(total, dtype=torch.float32, device="cuda")
+    dV = torch.zeros(total, dtype=torch.float32, device="cuda")
+    dOUT = to_dev(O.narrow(master, "fp16"), "fp16")
+    bucket = torch.zeros(total, dtype=torch.float16, device="cuda")
+    oP, oM, oV = master.copy(), np.zeros(total, np.float32), np.zeros(total, np.float32)
+    oOUT = O.narrow(master, "fp16")
+    ost = O.scaler_init(initial_scale_power=16, window=1000, hysteresis=2, min_scale=1.0)
+    scales, applied = [], []
+    for k in range(1, 6):
+        S = ost.scale
+        scales.append(S)
+        srcs = [draw_grads(n, "fp16", 1e-3, S, 0, 1, k, offset=o) for o, n in zip(offs, numels)]
+        if k in (2, 3):
+            srcs[7 * k][k] = 0xFC00  # -inf
+        zds.zds_grad_accumulate(plan, [to_dev(s, "fp16") for s in srcs], bucket, zds.ZDS_COPY)
+        st.step(bucket, dP, dM, dV, dOUT)
+        torch.cuda.synchronize()
+        flat = O.flatten_copy(srcs, ent, np.zeros(total, np.uint16))
+        oP, oM, oV, out16, ost, osc = O.optimizer_step(flat, "fp16", oP, oM, oV, ost, hp, cfg.max_norm,
+                                                       cfg.accum_steps, "fp16")
+        if out16 is not None:
+            oOUT = out16
+        applied.append(None if ost.last_skip else ost.t)
+        _compare("config step %d" % k, (to_host(dP), to_host(dM), to_host(dV), to_host(dOUT)),
+                 (oP, oM, oV, oOUT), st.read_scalars(), osc, ost, st.read_state())
+    assert scales == [2.0 ** 16] * 3 + [2.0 ** 15] * 2
+    assert applied == [1, None, None, 2, 3]
+    plan.close()
+
+
 def test_gradient_accumulation_sixteen_microbatches():
     """16 micro-batches of fp16 grads N(0, 1e-3) x 2^14 accumulated in fp32,
     then overflow check, clip at 1.0 and AdamW (t = 2, prior moments), on a

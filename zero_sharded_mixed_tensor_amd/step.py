@@ -26,6 +26,13 @@ class ShardStep:
         self.ws = zds.new_workspace(n, device)
         zds.zds_step_state_init(self.state, self.cfg, t0, beta1_pow0, beta2_pow0, stream)
 
+    @classmethod
+    def from_config(cls, n, cfg, t0=0, beta1_pow0=1.0, beta2_pow0=1.0, device="cuda", stream=None):
+        """A step with the settings of a config.StepConfig (hyperparameters,
+        loss scaler, clip threshold, micro-batches per step)."""
+        return cls(n, cfg.hparams(), cfg.scaler_config(), cfg.max_norm, cfg.accum_steps, t0, beta1_pow0,
+                   beta2_pow0, device, stream)
+
     def accumulate_norm(self, plan, srcs, dst, mode, ws, stream=None):
         """The step's last micro-batch with the overflow/norm pass fused in."""
         zds.zds_grad_accumulate_norm(plan, srcs, dst, mode, self.accum_steps, self.max_norm, self.state,
